@@ -1,0 +1,136 @@
+"""ctypes front end of the fp64 HCA oracle in ``hca_oracle.c``.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark are the only users.  Nothing in the HIP library imports,
+links or calls this package, and this package imports nothing from the HIP
+library.  Arrays of bfloat16 values travel as ``numpy.uint16`` bit patterns.
+
+What each function computes is documented at its C definition, with the page
+and section it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "hca_oracle.c")
+LIB = os.path.join(HERE, "libhca_oracle.so")
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (plain IEEE double, no FMA contraction)."""
+    tmp = LIB + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+         "-fno-fast-math", "-Wall", "-Wextra", SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        build()
+    _lib = bind(ctypes.CDLL(LIB))
+    return _lib
+
+
+def bind(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.hca_oracle_compress.argtypes = [P, I64, I64, I, I, P]
+    lib.hca_oracle_attn.argtypes = [P, P, P, I64, P, P, I64, I64, P, P, I64, I, I, I, I, D, P, I]
+    lib.hca_oracle_decode.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, D, P, I]
+    lib.hca_oracle_round_bf16.argtypes = [D]
+    lib.hca_oracle_round_bf16.restype = ctypes.c_uint16
+    lib.hca_oracle_widen_bf16.argtypes = [ctypes.c_uint16]
+    lib.hca_oracle_widen_bf16.restype = D
+    lib.hca_oracle_threads.restype = I
+    return lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bfloat16 data travels as uint16 bit patterns")
+    return a
+
+
+def threads() -> int:
+    return _load().hca_oracle_threads()
+
+
+def round_bf16(x: float) -> int:
+    return int(_load().hca_oracle_round_bf16(float(x)))
+
+
+def widen_bf16(bits: int) -> float:
+    return float(_load().hca_oracle_widen_bf16(int(bits)))
+
+
+def compress(x, block: int = 128) -> np.ndarray:
+    """Mean of each complete ``block`` of rows of ``x`` [T, D], rounded to bf16."""
+    x = _u16(x)
+    T, D = x.shape
+    out = np.zeros((T // block, D), dtype=np.uint16)
+    rc = _load().hca_oracle_compress(_ptr(x), T, D, D, block, _ptr(out))
+    if rc:
+        raise OracleError(f"hca_oracle_compress: {rc}")
+    return out
+
+
+def attn(q, g, tpos, k, v, kv_start, ck, cv, *, block=128, window=128, scale=None,
+         nthreads=0) -> np.ndarray:
+    """HCA attention rows.  q, g: [n, H, D]; tpos: [n] positions; k, v: raw rows
+    from ``kv_start``; ck, cv: [Nc, D] entries.  Returns float64 [n, H, D]."""
+    q, g, k, v = _u16(q), _u16(g), _u16(k), _u16(v)
+    ck = _u16(ck) if ck is not None else np.zeros((0, q.shape[2]), np.uint16)
+    cv = _u16(cv) if cv is not None else np.zeros((0, q.shape[2]), np.uint16)
+    n, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    tpos = np.ascontiguousarray(tpos, dtype=np.int64)
+    assert tpos.shape == (n,) and g.shape == q.shape
+    out = np.empty((n, H, D), dtype=np.float64)
+    rc = _load().hca_oracle_attn(_ptr(q), _ptr(g), _ptr(tpos), n, _ptr(k), _ptr(v), k.shape[0],
+                                 int(kv_start), _ptr(ck), _ptr(cv), ck.shape[0], H, D, block,
+                                 window, float(scale), _ptr(out), int(nthreads))
+    if rc:
+        raise OracleError(f"hca_oracle_attn: {rc}")
+    return out
+
+
+def decode(q, g, ck, cv, wk, wv, pos, *, block=128, window=128, scale=None,
+           nthreads=0) -> np.ndarray:
+    """Decode rows.  q, g: [B, H, D]; ck, cv: [B, nc_cap, D]; wk, wv: [B, window, D]
+    rings (position p in slot p % window); pos: [B].  Returns float64 [B, H, D]."""
+    q, g, wk, wv = _u16(q), _u16(g), _u16(wk), _u16(wv)
+    ck, cv = _u16(ck), _u16(cv)
+    B, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    assert pos.shape == (B,) and wk.shape == (B, window, D)
+    out = np.empty((B, H, D), dtype=np.float64)
+    rc = _load().hca_oracle_decode(_ptr(q), _ptr(g), _ptr(ck), _ptr(cv), ck.shape[1], _ptr(wk),
+                                   _ptr(wv), _ptr(pos), B, H, D, block, window, float(scale),
+                                   _ptr(out), int(nthreads))
+    if rc:
+        raise OracleError(f"hca_oracle_decode: {rc}")
+    return out
