@@ -1,0 +1,137 @@
+/*
+ * hca.h - C ABI of the HCA (Heavily Compressed Attention) library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed.  In 37 of the 43 layers of the model these pages describe,
+ * attention reads two kinds of keys (aitest123.com, "ERNIE-5.5-Flash-Base开源：
+ * 280B总参数，激活仅14B", section 模型结构; yilup.net, section 架構設計：稀疏 MoE
+ * 與混合注意力機制; blog.derekhsu.net, section 潛在閘控稀疏注意力):
+ *   (a) one cached entry per completed block of 128 tokens, and
+ *   (b) the most recent 128 raw tokens (lininn.cn, "2800 亿参数的模型，每次只叫醒
+ *       140 亿", section 43 层里，37 层只读摘要).
+ * Heads are 512 wide and there are 64 query heads (blog.derekhsu.net,
+ * section 潛在閘控稀疏注意力, the head-width paragraph; knowflowhub.com, table
+ * 关键信息).  The attention output is multiplied elementwise by a learned
+ * sigmoid gate (blog.derekhsu.net, section 低秩閘控注意力).
+ *
+ * Choices this library makes where the pages are silent:
+ *   - entry b = arithmetic mean of the block's 128 K rows (and of its 128 V
+ *     rows), rounded to bfloat16;
+ *   - one K/V head shared by every query head;
+ *   - entry b is visible to the query at position t iff 128*b + 127 <= t;
+ *   - the window is positions max(0, t-127) .. t, inclusive;
+ *   - one softmax over entries and window together, scores scale*<q,k>;
+ *   - out[t,h,:] = attn[t,h,:] * sigmoid(G[t,h,:]) with G supplied.
+ *
+ * Conventions.
+ *   - bf16 = IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
+ *   - All tensors are dense, row major, with the innermost dimension listed
+ *     last; device pointers must be 16-byte aligned.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronizes; all work is enqueued on `stream` (a hipStream_t; NULL =
+ *     the default stream) and returns before it completes.
+ *   - Inputs are read only; outputs are fully overwritten.
+ *   - Argument checking happens on the host before any HIP call; a rejected
+ *     call returns a non-zero status and enqueues nothing.  A launch failure
+ *     returns HCA_ERR_HIP.  Faults during execution surface at the caller's
+ *     next synchronization, as usual in HIP.
+ *   - hca_last_error() gives a human-readable reason for the last non-OK
+ *     status returned on the calling thread.
+ *   - Supported shapes: D = 512, block = 128, window = 128, 1 <= H <= 64 for
+ *     prefill and H a multiple of 16 up to 64 for decode.
+ */
+#ifndef HCA_H
+#define HCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HCA_OK = 0,
+  HCA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, inconsistent ranges */
+  HCA_ERR_UNSUPPORTED = 2, /* a shape this build has no kernel for (D, block, window, H) */
+  HCA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  HCA_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} hca_status_t;
+
+typedef enum { HCA_BF16 = 0, HCA_F32 = 1 } hca_dtype_t;
+
+/* Static description of a status code. */
+const char* hca_status_string(hca_status_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* hca_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int hca_version(void);
+
+/*
+ * Block compression (the cache entry of each completed block).
+ *   k, v     device, bf16 [T, ld]: rows 0..T-1, the first D columns are used (ld >= D)
+ *   ck, cv   device, bf16 [floor(T/block), D]: ck[b][d] = bf16(mean_{i<block} k[b*block+i][d]),
+ *            likewise cv from v.  The sum is formed exactly (in binary64, in row
+ *            order) and rounded once to nearest-even bfloat16.  A trailing partial
+ *            block produces no entry.
+ *   T >= 0.  Either of (k, ck) or (v, cv) may be NULL to compress only the other.
+ *   T < block is a no-op (no pointer is checked).
+ * For decode the caller compresses its 128-slot ring (T = 128) whenever a block
+ * completes and appends the entry before the next decode call.
+ */
+hca_status_t hca_compress(const void* k, const void* v, int64_t T, int64_t ld, int D, int block,
+                          void* ck, void* cv, void* stream);
+
+/*
+ * Prefill attention for Tq consecutive queries at positions q_start .. q_start+Tq-1.
+ *   q, g     device, bf16 [Tq, H, D]     queries and pre-sigmoid gate logits
+ *   k, v     device, bf16 [Tkv, D]       raw rows of positions kv_start .. kv_start+Tkv-1
+ *   ck, cv   device, bf16 [Nc, D]        entries of blocks 0 .. Nc-1 (may be NULL if Nc = 0)
+ *   out      device, [Tq, H, D]          bf16 (rounded to nearest-even) or f32
+ *   scale    score scale (1/sqrt(512) for the model's layer)
+ * Query at position t attends to entries b < Nc with 128*b+127 <= t and to the raw
+ * rows of positions max(0, t-127) .. t.
+ * Requirements when Tq > 0 (else HCA_ERR_INVALID_ARG):
+ *   Tq, Tkv, Nc, q_start, kv_start >= 0 and scale finite and > 0;
+ *   kv_start <= max(0, q_start-127)       (the first query's window is present);
+ *   kv_start + Tkv >= q_start + Tq        (the last query's own row is present);
+ *   Nc >= floor((q_start+Tq)/128)         (every entry a query can see is present;
+ *                                          entries past that are never read).
+ * Positions, Tq*H and Nc must stay below 2^31 (else HCA_ERR_UNSUPPORTED).
+ * K and V must be finite: a key hidden from one row but visible to another row
+ * of the same tile is multiplied by a zero weight.  Tq = 0 is a no-op.
+ */
+hca_status_t hca_attn_prefill(const void* q, const void* g, const void* k, const void* v,
+                              const void* ck, const void* cv, int64_t Tq, int64_t q_start,
+                              int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D, int block,
+                              int window, float scale, void* out, hca_dtype_t out_dtype,
+                              void* stream);
+
+/*
+ * Decode attention: one new query per sequence, for B sequences at once.
+ *   q, g     device, bf16 [B, H, D]          the new token's queries and gate logits
+ *   ck, cv   device, bf16 [B, nc_cap, D]     per-sequence entries (only the first
+ *                                            floor((pos+1)/128) are read)
+ *   wk, wv   device, bf16 [B, window, D]     per-sequence ring of raw rows; position p
+ *                                            lives in slot p % window, and slots of
+ *                                            positions max(0,pos-127)..pos must be valid
+ *   pos      device, int64 [B]               position of the new token (already written
+ *                                            into its ring slot)
+ *   out      device, [B, H, D]               bf16 or f32
+ * Entry counts come from device memory, so the host cannot check them: a pos with
+ * floor((pos+1)/128) > nc_cap or pos < 0 is clamped on the device (never read out
+ * of bounds) and its output is then unspecified.
+ * B = 0 is a no-op.
+ */
+hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const void* cv,
+                             int64_t nc_cap, const void* wk, const void* wv, const int64_t* pos,
+                             int B, int H, int D, int block, int window, float scale, void* out,
+                             hca_dtype_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCA_H */

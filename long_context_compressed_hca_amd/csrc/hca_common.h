@@ -1,0 +1,49 @@
+// hca_common.h - device-side building blocks shared by the HCA kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "hca_kernels.h"
+
+namespace hca {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two floats -> packed bfloat16 pair (lo in bits 0..15), nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- LDS DMA
+// global -> LDS copy of 16 bytes per lane: lane i's 16 bytes land at
+// lds_row + 16*i, whatever global address lane i supplies.  lds_row must be
+// the same for every lane of the wave.
+__device__ __forceinline__ void dma16(const void* gsrc, lds_void* lds_row) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_row, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): wait for this wave's outstanding vector-memory loads,
+// including LDS DMA (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; expcnt and lgkmcnt left at their "no wait" maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+}  // namespace hca

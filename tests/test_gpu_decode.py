@@ -1,0 +1,93 @@
+"""GPU decode attention against the fp64 oracle (every output compared)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_compressed_hca_amd as hca
+import oracle
+import synth
+from tests.gpu_util import D, Prefill, compare, dev, gen, host, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+class Decode:
+    def __init__(self, seed, positions, H=64, nc_cap=None, out_dtype="bf16"):
+        positions = np.asarray(positions, dtype=np.int64)
+        B = len(positions)
+        self.nc_cap = int(max((positions + 1) // 128)) if nc_cap is None else nc_cap
+        self.q = gen(seed, synth.Q, (B, H, D))
+        self.g = gen(seed, synth.G, (B, H, D))
+        self.ck = gen(seed, synth.CK, (B, self.nc_cap, D))
+        self.cv = gen(seed, synth.CV, (B, self.nc_cap, D))
+        self.wk = gen(seed, synth.WK, (B, 128, D))
+        self.wv = gen(seed, synth.WV, (B, 128, D))
+        self.pos_np = positions
+        self.pos = torch.as_tensor(positions, device=dev())
+        self.out = torch.empty((B, H, D), device=dev(),
+                               dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
+
+    def run(self):
+        hca.hca_attn_decode(self.q, self.g, self.ck, self.cv, self.wk, self.wv, self.pos,
+                            self.out)
+        torch.cuda.synchronize()
+        return self.out
+
+    def oracle(self):
+        return oracle.decode(host(self.q), host(self.g), host(self.ck), host(self.cv),
+                             host(self.wk), host(self.wv), self.pos_np)
+
+
+def test_64_sequences_32k_history():
+    # the batched decode workload: 64 sequences, new token at 32768,
+    # 256 entries + 128 window rows each, 64 heads
+    d = Decode(seed=4, positions=[32768] * 64, nc_cap=256)
+    print(compare(host_f64(d.run()), d.oracle(), "decode B=64"))
+
+
+@pytest.mark.parametrize("H", [16, 32, 48, 64])
+def test_mixed_positions(H):
+    positions = [0, 1, 5, 126, 127, 128, 129, 255, 256, 383, 1000, 4095, 4096, 32767]
+    d = Decode(seed=10 + H, positions=positions, H=H, out_dtype="f32")
+    compare(host_f64(d.run()), d.oracle(), f"decode H={H}")
+
+
+def test_cache_larger_than_needed():
+    d = Decode(seed=12, positions=[200, 700, 50], H=32, nc_cap=40)
+    compare(host_f64(d.run()), d.oracle(), "nc_cap 40")
+
+
+def test_gate_limits():
+    d = Decode(seed=13, positions=[10, 300, 5000], H=16, out_dtype="f32")
+    d.g = torch.full_like(d.g, float("-inf"))
+    assert torch.all(d.run() == 0)
+    d.g = torch.zeros_like(d.g)
+    half = d.run().clone()
+    d.g = torch.full_like(d.g, float("inf"))
+    assert torch.equal(2 * half, d.run())
+
+
+def test_decode_matches_prefill_row():
+    # decode at position t reads the same keys as row t of a prefill over [0, t]
+    T, H = 1000, 64
+    p = Prefill(seed=14, Tq=T, H=H, out_dtype="f32")
+    p.run()
+    positions = np.array([0, 127, 128, 640, 999])
+    d = Decode(seed=14, positions=positions, H=H, nc_cap=T // 128, out_dtype="f32")
+    for b, t in enumerate(positions):
+        d.q[b], d.g[b] = p.q[t], p.g[t]
+        n = (t + 1) // 128
+        d.ck[b, :n], d.cv[b, :n] = p.ck[:n], p.cv[:n]
+        for s in range(max(0, t - 127), t + 1):
+            d.wk[b, s % 128], d.wv[b, s % 128] = p.k_all[s], p.v_all[s]
+    got = d.run()
+    torch.cuda.synchronize()
+    torch.testing.assert_close(got, p.out[torch.as_tensor(positions, device=dev())],
+                               rtol=2e-2, atol=2e-3)
+    compare(host_f64(got), d.oracle(), "decode rows")
+
+
+def test_batch_zero_is_noop():
+    d = Decode(seed=15, positions=[5], H=16)
+    hca.hca_attn_decode(d.q[:0], d.g[:0], d.ck[:0], d.cv[:0], d.wk[:0], d.wv[:0], d.pos[:0],
+                        d.out[:0])
