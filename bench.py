@@ -1,0 +1,230 @@
+"""Benchmark of the HCA hot path on one MI355X.
+
+One step = the whole prefill path over one 128K-token sequence with 64 query
+heads: block compression of K and V (1024 entries each), then HCA prefill
+attention (entries + 128-token window, 512-wide heads, sigmoid gate), bf16 in
+and out.  Inputs are seeded synthetic N(0,1) bf16 tensors already resident in
+HBM.  The reported value is algorithmic TFLOP/s of the step:
+    FLOPs = 4 * 512 * H * sum_t (floor((t+1)/128) + min(t+1, 128))
+(visible keys only; masked work, exp and the gate are not counted).
+
+Also reported:
+  roofline      the prefill kernel's own rate (HIP events on its stream) against
+                the 2.5 PFLOP/s dense bf16 MFMA peak, plus HBM bytes from
+                rocprofv3 counters when they were taken on the current source;
+  decode        batched decode (64 sequences, 256 entries + 128 window rows, 64
+                heads) in GB/s of compulsory HBM traffic, against 8 TB/s;
+  cpu_baseline  the fp64 oracle timed on a bounded sample of the same workload.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+D, BLOCK, WINDOW = 512, 128, 128
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+METRIC = "HCA attn TFLOP/s (128K prefill, % bf16 MFMA peak); decode HBM GB/s"
+COUNTERS = os.path.join(ROOT, "profiles", "prefill_128k_counters.json")
+PREFILL_SRC = os.path.join(ROOT, "long_context_compressed_hca_amd", "csrc", "prefill.hip")
+
+
+def visible_keys(t0: int, t1: int, Nc_cap: int | None = None) -> int:
+    """sum over query positions t0..t1-1 of floor((t+1)/128) + min(t+1, 128)."""
+    t = np.arange(t0, t1, dtype=np.int64)
+    nc = (t + 1) // BLOCK
+    if Nc_cap is not None:
+        nc = np.minimum(nc, Nc_cap)
+    return int(nc.sum() + np.minimum(t + 1, WINDOW).sum())
+
+
+def prefill_flops(T: int, H: int, q_start: int = 0) -> float:
+    return 4.0 * D * H * visible_keys(q_start, q_start + T)
+
+
+def sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per prefill launch from committed rocprofv3 counter runs, or None
+    if the counters were taken on a different prefill source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != sha256(PREFILL_SRC):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def bench_prefill(args, torch, hca, synth):
+    dev = torch.device("cuda:0")
+    T, H = args.T, 64
+    gen = lambda tid, shape: synth.normal_bf16_device(3, tid, shape, dev)
+    q, g = gen(synth.Q, (T, H, D)), gen(synth.G, (T, H, D))
+    k, v = gen(synth.K, (T, D)), gen(synth.V, (T, D))
+    Nc = T // BLOCK
+    ck = torch.empty((Nc, D), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        hca.hca_compress(k, v, ck, cv)
+        if i is not None:
+            ev[i][0].record(stream)
+        hca.hca_attn_prefill(q, g, k, v, ck, cv, out)
+        if i is not None:
+            ev[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = prefill_flops(T, H)
+    return dict(T=T, H=H, flops=flops, ms_per_step=elapsed * 1e3 / args.steps,
+                prefill_ms=kernel_ms, tensors=(q, g, k, v, ck, cv, out))
+
+
+def bench_decode(args, torch, hca, synth):
+    """64 sequences, new token at position 32768: 256 entries + 128 window rows each."""
+    dev = torch.device("cuda:0")
+    B, H, nc_cap, pos = 64, 64, 256, 32768
+    reps = 6
+    sets = []
+    for r in range(reps):
+        gen = lambda tid, shape: synth.normal_bf16_device(40 + r, tid, shape, dev)
+        sets.append(dict(q=gen(synth.Q, (B, H, D)), g=gen(synth.G, (B, H, D)),
+                         ck=gen(synth.CK, (B, nc_cap, D)), cv=gen(synth.CV, (B, nc_cap, D)),
+                         wk=gen(synth.WK, (B, WINDOW, D)), wv=gen(synth.WV, (B, WINDOW, D)),
+                         out=torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)))
+    posd = torch.full((B,), pos, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    n = 240
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+
+    def call(s):
+        hca.hca_attn_decode(s["q"], s["g"], s["ck"], s["cv"], s["wk"], s["wv"], posd, s["out"])
+
+    for i in range(24):
+        call(sets[i % reps])
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record(stream)
+        call(sets[i % reps])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    n_keys = (pos + 1) // BLOCK + WINDOW
+    kv_bytes = B * n_keys * D * 2 * 2
+    qgo_bytes = 3 * B * H * D * 2
+    total = kv_bytes + qgo_bytes
+    gbs = total / (us * 1e-6) / 1e9
+    return dict(metric="decode HBM GB/s", value=round(gbs, 1), unit="GB/s",
+                us_per_call=round(us, 2), bytes_per_call=total,
+                config={"workload": "HCA batched decode: 64 sequences x (256 entries + 128 "
+                        "window rows), 64 heads, dim 512, bf16", "input_replicas": reps},
+                roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "traffic": None})
+
+
+def cpu_baseline(args, torch, synth, tensors):
+    """The oracle, as it stands, on a bounded sample of query positions of the same
+    128K workload (every head), timed on this host's cores."""
+    import oracle
+    q, g, k, v = tensors[:4]
+    T, H = q.shape[0], q.shape[1]
+    rng = np.random.default_rng(2024)
+    pos = np.sort(rng.choice(T, size=args.cpu_positions, replace=False)).astype(np.int64)
+    host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    idx = torch.as_tensor(pos, device=q.device)
+    qh, gh = host(q.index_select(0, idx)), host(g.index_select(0, idx))
+    kh, vh = host(k), host(v)
+    threads = oracle.threads()
+    t0 = time.perf_counter()
+    ck, cv = oracle.compress(kh), oracle.compress(vh)
+    oracle.attn(qh, gh, pos, kh, vh, 0, ck, cv, nthreads=threads)
+    dt = time.perf_counter() - t0
+    t = pos
+    keys = int(((t + 1) // BLOCK).sum() + np.minimum(t + 1, WINDOW).sum())
+    flops = 4.0 * D * H * keys
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(pos)} seeded query positions (all {H} heads) of the 128K-token "
+                      f"workload, plus compressing its full K and V; fp64 C oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--T", type=int, default=131072, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-positions", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_compressed_hca_amd as hca
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    hca.lib()  # fail loudly if the HIP library is missing
+
+    pf = bench_prefill(args, torch, hca, synth)
+    value = pf["flops"] / (pf["ms_per_step"] * 1e-3) / 1e12
+    achieved = pf["flops"] / (pf["prefill_ms"] * 1e-3) / 1e12
+    traffic = load_traffic()
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(pf["ms_per_step"], 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "HCA prefill at 128K context: batch 1, T=131072, 64 query "
+                   "heads, 1 KV head, dim 512, block 128, window 128; compress + prefill "
+                   "per step; bf16 in/out", "seq_len": pf["T"], "heads": pf["H"],
+                   "global_batch": 1, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "hca prefill_kernel", "flops_per_launch": pf["flops"],
+                     "launch_ms": round(pf["prefill_ms"], 4)},
+    }
+    if not args.no_decode:
+        rec["decode"] = bench_decode(args, torch, hca, synth)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args, torch, synth, pf["tensors"])
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

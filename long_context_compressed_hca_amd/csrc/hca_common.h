@@ -41,6 +41,19 @@ __device__ __forceinline__ void dma16(const void* gsrc, lds_void* lds_row) {
   __builtin_amdgcn_global_load_lds(gsrc, lds_row, 16, 0, 0);
 }
 
+// Buffer descriptor of `bytes` bytes at `base` (raw, stride 0, 32-bit data
+// format, the gfx9 default for untyped buffer access).  Loads at offsets
+// >= bytes are range checked by the hardware and return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// buffer -> LDS copy of 16 bytes per lane through a descriptor: lane i's 16
+// bytes (from byte offset voff of the buffer) land at lds_row + 16*i.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, lds_void* lds_row) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row, 16, voff, 0, 0, 0);
+}
+
 // s_waitcnt vmcnt(0): wait for this wave's outstanding vector-memory loads,
 // including LDS DMA (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8; expcnt and lgkmcnt left at their "no wait" maxima).

@@ -8,41 +8,50 @@
 //   out   = softmax_j(scale * <q, key_j>) . value_j  *  sigmoid(G[t,h,:])
 // with one 512-wide K/V head shared by every query head.
 //
-// Work decomposition.  The query tensor is viewed as a flat list of Tq*H rows
-// (row = query*H + head); a workgroup owns 128 consecutive rows, 4 waves of 32.
-// All rows of a workgroup share one K/V head, so every 32-key tile of K and V
-// is staged once in LDS and read by the four waves (for H = 64 that is 2
-// queries x 64 heads).  The workgroup walks the compressed entries it can see
-// (one set for all its rows except at block ends) and then the raw window,
-// in one online softmax.
-//
-// Per wave and 32-key tile:
+// Work decomposition.  The query tensor is a flat list of Tq*H rows (row =
+// query*H + head).  A work item is 128 consecutive rows (for H = 64: two
+// queries, all heads).  It walks, in one softmax, the 32-key tiles of the
+// compressed entries its rows can see and then of their raw window.  Each K/V
+// tile is copied once into LDS and read by the 4 waves; wave w owns rows
+// 32w .. 32w+31 of the item with all 512 dims:
 //   S^T[key][row] = K . Q^T      32 MFMA 32x32x16 (A = K from LDS, B = Q in VGPRs)
-//   mask, online softmax         each lane owns one row and 16 of the 32 keys
+//   mask, softmax                each lane owns one row and 16 of the 32 keys
 //   O^T[dv][row] += V^T . P^T    32 MFMA 32x32x16 (A = V^T via LDS transpose reads)
-// Computing the transposes keeps a row in one lane (a 2-lane max/sum per tile)
-// and makes P^T the B operand straight from the S^T accumulator layout.
+// Q (128 VGPRs) and O (256 accumulator registers) stay in registers for the
+// whole item.  Computing the transposes keeps a row in one lane and makes P^T
+// the B operand straight from the S^T accumulator layout.
+//
+// Persistent schedule.  The kernel runs one workgroup per CU; each workgroup
+// loops over items, heaviest (latest positions, most entries) first.  Items
+// are dealt so that the workgroups of one XCD take runs of adjacent items,
+// whose raw windows overlap in that XCD's L2.
+//
+// Q, G and out move between HBM and registers through LDS (each wave stages
+// its 32 rows in a 32 KiB region that aliases the idle tile stages between
+// items): global traffic is whole 1 KiB rows, while the MFMA layouts spread
+// a wave's registers over 32 rows.
 //
 // LDS: two stages x (K tile + V tile) x 32 rows x 1 KiB = 128 KiB.  Tiles are
-// copied global -> LDS by DMA (global_load_lds_dwordx4, no VGPRs), one 1 KiB
-// row per wave instruction, with an XOR swizzle of the 16-byte chunks chosen
-// so the two read patterns are bank-conflict free:
+// copied global -> LDS by DMA (buffer_load_dwordx4 ... lds, no VGPRs), one
+// 1 KiB row per wave instruction, with an XOR swizzle of the 16-byte chunks
+// chosen so the two read patterns are bank-conflict free:
 //   K: chunk c of key r stored at c ^ (r & 15)   (b128 reads, 16 keys x 1 chunk)
 //   V: chunk c of key r stored at c ^ 4(r & 3)   (b64 transpose reads, 4 keys x 4 chunks)
-// The tile i+1 copy is in flight while tile i is computed.
+// The copy of tile i+1 is issued spread over tile i's MFMAs and is in flight
+// while tile i is computed.  LDS fragments are read a few MFMAs ahead of use.
 //
 // Softmax: scores are kept in the exp2 domain (x = s * scale * log2 e).  Each
 // row fixes its reference m at its first tile with a visible key and weighs
 // every key by p = 2^(x - m); O is never rescaled in the loop (a rescale of
-// 256 accumulator registers per lane would cost more than the tile's MFMAs).
-// If any score rises more than 2^64 above its reference, the workgroup runs
-// its tiles again with the exact row maximum as reference.  P is rounded to
-// bf16 for the MFMA and the row sum l adds the rounded values, so O/l is an
-// exact weighted mean of V rows up to fp32 accumulation.
+// 256 accumulator registers per lane would cost more than a tile's MFMAs).
+// If any score rises more than 2^64 above its reference, the item's tiles are
+// run again with the exact row maximum as reference.  P is rounded to bf16
+// for the MFMA and the row sum l adds the rounded values, so O/l is a
+// weighted mean of V rows up to fp32 accumulation.
 //
 // Epilogue: out = O / l * sigmoid(G), sigmoid(x) = 1/(1 + 2^(-x log2 e)),
-// which gives exactly 0 at G = -inf and 1 at G = +inf.  bf16 (nearest even)
-// or f32 output.
+// which is exactly 0 at G = -inf and 1 at G = +inf.  bf16 (nearest even) or
+// f32 output.
 //
 // Roofline: 4*512 flop per (row, visible key); at 128K context the kernel is
 // MFMA bound (about 420 flop per HBM byte).
@@ -52,10 +61,13 @@
 namespace hca {
 namespace {
 
-constexpr int kRowsPerWG = 128;
+constexpr int kRowsPerItem = 128;
 constexpr int kTile = 32;
-constexpr int kRun = 16;  // consecutive workgroups kept on one XCD
 constexpr float kHeadroom = 64.0f;  // p = 2^(x - m) stays below 2^64 in a pass
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
 
 struct Args {
   const uint16_t* q;
@@ -65,9 +77,10 @@ struct Args {
   const uint16_t* ck;
   const uint16_t* cv;
   void* out;
-  int rows;  // Tq * H
+  int rows;                   // Tq * H
   int q_start, kv_start, Nc;  // positions and counts fit in 31 bits (checked on the host)
-  int n_wg;
+  int n_items;
+  int per_xcd;                // workgroups per XCD (grid = 8 * per_xcd)
   int H;
   float c;  // scale * log2(e)
   int out_f32;
@@ -78,50 +91,126 @@ __device__ __forceinline__ int n_entries(int t, int Nc) {
   return n < Nc ? n : Nc;
 }
 
-// Describes the tile sequence of one workgroup.
-struct Tiles {
-  int nc_wg;  // entries visible to the last row of the workgroup
-  int w_lo;   // first raw position of the window union
-  int t_max;  // last position of the workgroup
-  int n_ct;       // compressed tiles
+// One work item as seen by one lane.
+struct Item {
+  int row0, last;      // rows of the item (last clamped to the final row)
+  int my_row_raw;      // this lane's row (may be past `last` in the final item)
+  int my_row;          // clamped to `last`
+  int t;               // this lane's query position
+  int tw_min, tw_max;  // positions of this wave's first and last row
+  int t_max;           // last position of the item
+  int nc_wg;           // entries visible to the last row of the item
+  int w_lo;            // first raw position of the item's window union
+  int n_ct;            // compressed tiles
   int n_tiles;
 };
 
-// Copy tile `it` into (sK, sV).  Each wave copies 8 of the 32 key rows of K and
-// of V; the row pointers are wave-uniform (SGPRs), the lane offset is 32-bit.
-__device__ __forceinline__ void issue_tile(const Args& a, const Tiles& ts, int it, uint8_t* sK,
-                                           uint8_t* sV, int wave, int lane) {
+__device__ __forceinline__ Item make_item(const Args& a, int idx, int wave, int l32) {
+  Item it;
+  it.row0 = idx * kRowsPerItem;
+  it.last = (it.row0 + kRowsPerItem < a.rows ? it.row0 + kRowsPerItem : a.rows) - 1;
+  const int wr0 = it.row0 + wave * 32 < it.last ? it.row0 + wave * 32 : it.last;
+  const int wr1 = it.row0 + wave * 32 + 31 < it.last ? it.row0 + wave * 32 + 31 : it.last;
+  it.my_row_raw = it.row0 + wave * 32 + l32;
+  it.my_row = it.my_row_raw < it.last ? it.my_row_raw : it.last;
+  it.t = a.q_start + it.my_row / a.H;
+  it.tw_min = a.q_start + wr0 / a.H;
+  it.tw_max = a.q_start + wr1 / a.H;
+  const int t_min = a.q_start + it.row0 / a.H;
+  it.t_max = a.q_start + it.last / a.H;
+  it.nc_wg = n_entries(it.t_max, a.Nc);
+  it.w_lo = t_min - (kWindow - 1) > 0 ? t_min - (kWindow - 1) : 0;
+  it.n_ct = (it.nc_wg + kTile - 1) / kTile;
+  it.n_tiles = it.n_ct + (it.t_max - it.w_lo + 1 + kTile - 1) / kTile;
+  return it;
+}
+
+// First key (entry index or raw position) of tile `i`; kind 0 = entries, 1 = window.
+__device__ __forceinline__ int tile_first(const Item& it, int i, int& kind) {
+  if (i < it.n_ct) {
+    kind = 0;
+    return i * kTile;
+  }
+  kind = 1;
+  return it.w_lo + (i - it.n_ct) * kTile;
+}
+
+// The copy of one 32-key tile into (sK, sV): buffer descriptors that cover
+// exactly the tile's valid rows.  Each wave copies 8 of the 32 key rows of K and
+// of V (dma_row); rows past the end repeat the last valid row (finite data;
+// those keys are masked), so every LDS row of the tile is written.
+struct TileCopy {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int nrows;
+  uint8_t* sK;
+  uint8_t* sV;
+};
+
+__device__ __forceinline__ TileCopy tile_copy(const Args& a, const Item& it, int i, uint8_t* sK,
+                                              uint8_t* sV) {
   const uint8_t* kb;
   const uint8_t* vb;
   int first, last;
-  if (it < ts.n_ct) {
+  if (i < it.n_ct) {
     kb = reinterpret_cast<const uint8_t*>(a.ck);
     vb = reinterpret_cast<const uint8_t*>(a.cv);
-    first = it * kTile;
-    last = ts.nc_wg - 1;
+    first = i * kTile;
+    last = it.nc_wg - 1;
   } else {
     kb = reinterpret_cast<const uint8_t*>(a.k);
     vb = reinterpret_cast<const uint8_t*>(a.v);
-    first = ts.w_lo + (it - ts.n_ct) * kTile - a.kv_start;
-    last = ts.t_max - a.kv_start;
+    first = it.w_lo + (i - it.n_ct) * kTile - a.kv_start;
+    last = it.t_max - a.kv_start;
   }
+  TileCopy c;
+  c.nrows = last - first + 1 < kTile ? last - first + 1 : kTile;
+  c.rk = make_rsrc(kb + (size_t)first * (kD * 2), c.nrows * kD * 2);
+  c.rv = make_rsrc(vb + (size_t)first * (kD * 2), c.nrows * kD * 2);
+  c.sK = sK;
+  c.sV = sV;
+  return c;
+}
+
+// Copy key row u (0..7) of this wave's share of a tile (two DMA instructions).
+__device__ __forceinline__ void dma_row(const TileCopy& c, int u, int wave, int lane) {
+  const int r = wave * (kTile / 4) + u;  // key row within the tile
+  const int src = (r < c.nrows ? r : c.nrows - 1) * 1024;
+  dma16_buf(c.rk, src + ((lane ^ (r & 15)) << 4), (lds_void*)(c.sK + r * 1024));
+  dma16_buf(c.rv, src + ((lane ^ ((r & 3) << 2)) << 4), (lds_void*)(c.sV + r * 1024));
+}
+
+__device__ __forceinline__ void issue_tile(const Args& a, const Item& it, int i, uint8_t* sK,
+                                           uint8_t* sV, int wave, int lane) {
+  const TileCopy c = tile_copy(a, it, i, sK, sV);
 #pragma unroll
-  for (int u = 0; u < kTile / 4; ++u) {
-    const int r = wave * (kTile / 4) + u;  // key row within the tile
-    int src = first + r;
-    src = src < last ? src : last;  // rows past the end repeat a valid row; they are masked
-    const uint8_t* krow = kb + (size_t)src * (kD * 2);
-    const uint8_t* vrow = vb + (size_t)src * (kD * 2);
-    dma16(krow + ((lane ^ (r & 15)) << 4), (lds_void*)(sK + r * 1024));
-    dma16(vrow + ((lane ^ ((r & 3) << 2)) << 4), (lds_void*)(sV + r * 1024));
+  for (int u = 0; u < kTile / 4; ++u) dma_row(c, u, wave, lane);
+}
+
+// Copy this wave's 32 rows of a [rows, 512] bf16 tensor (rows row0w .. row0w+31)
+// into the wave's 32 KiB LDS region, one 1 KiB row per instruction (coalesced),
+// chunk c of row r stored at c ^ (r & 15).  Rows past `last` repeat `last`.
+__device__ __forceinline__ void dma_rows(const uint16_t* base, int row0w, int last,
+                                         uint8_t* region, int lane) {
+  const int first = row0w < last ? row0w : last;
+  const int nrows = last - first + 1 < 32 ? last - first + 1 : 32;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(reinterpret_cast<const uint8_t*>(base) + (size_t)first * (kD * 2), nrows * kD * 2);
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const int src = (r < nrows ? r : nrows - 1) * 1024;
+    dma16_buf(rs, src + ((lane ^ (r & 15)) << 4), (lds_void*)(region + r * 1024));
   }
 }
 
-__device__ __forceinline__ float max16(const f32x16& s) {
-  float m = s[0];
+// Q fragments (B operand of S^T) from the wave's region: lane holds row l%32,
+// dims 16ss + 8g .. +8, i.e. chunk 2ss+g of its row (same swizzle as K).
+__device__ __forceinline__ void read_q(const uint8_t* region, int lane, bf16x8 (&qf)[32]) {
+  const int l32 = lane & 31, g = lane >> 5;
+  const uint8_t* row = region + l32 * 1024;
 #pragma unroll
-  for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
-  return m;
+  for (int ss = 0; ss < 32; ++ss)
+    qf[ss] = *reinterpret_cast<const bf16x8*>(
+        row + 256 * (ss >> 3) + (((2 * (ss & 7) + g) ^ (l32 & 15)) << 4));
 }
 
 struct WaveState {
@@ -132,202 +221,159 @@ struct WaveState {
   bool over;     // a score exceeded m + kHeadroom in this pass
 };
 
-// Process one 32-key tile for this wave.
-//   kind 0: compressed entries e0 .. e0+31;  kind 1: raw positions p0 .. p0+31.
+// Process one 32-key tile.  kind 0: entries first .. first+31; kind 1: raw positions.
+// If `copy_next`, the copy of the next tile (`nc`) is issued spread over this
+// tile's MFMAs (one K and one V row every 4 MFMAs), so the vector memory path
+// works in the background instead of stalling the wave's instruction issue.
 __device__ __forceinline__ void compute_tile(const Args& a, WaveState& st, const bf16x8 (&qf)[32],
                                              const uint8_t* sK, const uint8_t* sV, int kind,
-                                             int first, int t, int tw_min, int tw_max,
-                                             int lane) {
+                                             int first, const Item& it, int lane, int wave,
+                                             bool copy_next, const TileCopy& nc) {
   const int l32 = lane & 31, g = lane >> 5;
   bool need, full;
   if (kind == 0) {
-    need = first < n_entries(tw_max, a.Nc);
-    full = first + kTile <= n_entries(tw_min, a.Nc);
+    need = first < n_entries(it.tw_max, a.Nc);
+    full = first + kTile <= n_entries(it.tw_min, a.Nc);
   } else {
-    need = first <= tw_max && first + kTile - 1 >= tw_min - (kWindow - 1);
-    full = first >= tw_max - (kWindow - 1) && first + kTile - 1 <= tw_min;
+    need = first <= it.tw_max && first + kTile - 1 >= it.tw_min - (kWindow - 1);
+    full = first >= it.tw_max - (kWindow - 1) && first + kTile - 1 <= it.tw_min;
   }
-  if (!need) return;
+  if (!need) {
+    if (copy_next)
+#pragma unroll
+      for (int u = 0; u < kTile / 4; ++u) dma_row(nc, u, wave, lane);
+    return;
+  }
 
-  // ---- S^T = K . Q^T
-  // Step ss reads logical chunk 2ss+g of key row l32, stored at (2ss+g) ^ (l32&15).
-  // With ss = 8j + i that is 16j + ((2i + g) ^ (l32&15)): 8 lane offsets, and j
-  // becomes an immediate offset of 256 bytes.
+  // ---- S^T = K . Q^T.  Step ss reads chunk 2ss+g of key row l32, stored at
+  // (2ss+g) ^ (l32&15); with ss = 8j + i that is 16j + ((2i + g) ^ (l32&15)),
+  // so 8 lane offsets serve all steps (j becomes an immediate offset).
   f32x16 s = {};
   const uint8_t* krow = sK + l32 * 1024;
   int koff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) koff[i] = ((2 * i + g) ^ (l32 & 15)) << 4;
+  constexpr int kAhead = 4;  // K fragments read this many MFMAs ahead
+  bf16x8 kf[kAhead];
+#pragma unroll
+  for (int ss = 0; ss < kAhead; ++ss)
+    kf[ss] = *reinterpret_cast<const bf16x8*>(krow + koff[ss & 7] + 256 * (ss >> 3));
 #pragma unroll
   for (int ss = 0; ss < 32; ++ss) {
-    const bf16x8 kf =
-        *reinterpret_cast<const bf16x8*>(krow + koff[ss & 7] + 256 * (ss >> 3));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ss], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ss % kAhead], qf[ss], s, 0, 0, 0);
+    if (ss + kAhead < 32) {
+      const int n = ss + kAhead;
+      kf[ss % kAhead] = *reinterpret_cast<const bf16x8*>(krow + koff[n & 7] + 256 * (n >> 3));
+    }
+    if ((ss & 7) == 7 && copy_next) dma_row(nc, ss >> 3, wave, lane);
+  }
+#pragma unroll
+  for (int ss = 0; ss < kAhead; ++ss) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int ss = 0; ss < 32; ++ss) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (ss + kAhead < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if ((ss & 7) == 7) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
   }
 
-  // ---- mask (only on tiles where some row of this wave sees part of the tile)
+  // ---- mask, on tiles that some row of this wave sees only in part.  The
+  // lane's visible keys form one interval [lo, hi] of this tile's key space.
   if (!full) {
-    const int nc = n_entries(t, a.Nc);
+    const int lo = kind == 0 ? 0 : it.t - (kWindow - 1);
+    const int hi = kind == 0 ? n_entries(it.t, a.Nc) - 1 : it.t;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = first + 8 * (r >> 2) + 4 * g + (r & 3);
-      const bool vis = kind == 0 ? key < nc : (key <= t && key >= t - (kWindow - 1));
-      s[r] = vis ? s[r] : -INFINITY;
+      s[r] = (key >= lo && key <= hi) ? s[r] : -INFINITY;
     }
   }
 
   // ---- softmax weights against the row's reference max (exp2 domain)
-  float mt = max16(s) * a.c;
+  float mt = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+  mt *= a.c;
   mt = fmaxf(mt, __shfl_xor(mt, 32));
   st.mseen = fmaxf(st.mseen, mt);
   st.m = st.m == -INFINITY ? mt : st.m;  // fixed at the row's first visible key
   st.over |= mt > st.m + kHeadroom;
   const float msub = st.m == -INFINITY ? 0.0f : st.m;
-  uint32_t pk[8];
-  float lsum = 0.0f;
+  bf16x2 pk[8];
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -msub));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], a.c, -msub));
-    const uint32_t w = pack_bf16x2(p0, p1);
-    pk[r >> 1] = w;
-    lsum += bf16_bits_to_f32(w & 0xFFFFu) + bf16_bits_to_f32(w >> 16);
+    const f32x2 pr = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -msub)),
+                      __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], a.c, -msub))};
+    pk[r >> 1] = __builtin_convertvector(pr, bf16x2);
+    st.l = __builtin_amdgcn_fdot2_f32_bf16(pk[r >> 1], ones, st.l, false);
   }
-  st.l += lsum;
 
-  // ---- O^T += V^T . P^T
+  // ---- O^T += V^T . P^T.  Transpose reads: in each 16-lane group, source lane
+  // s16 addresses key row 4(lane/32) + s16/4 (+16 c2 + 8 r) and dims
+  // 32b + 16((lane/16)&1) + 4(s16&3); the result lane holds 4 keys of one dim.
   const int s16 = lane & 15, q4 = lane >> 4;
-  const int gq = q4 >> 1, h = q4 & 1;
-  const int krow_lo = 4 * gq + (s16 >> 2);                 // + 16*c2 + 8*r
-  const int sw = (s16 >> 2) & 3;                            // V swizzle (in 4-chunk units)
-  const int cbase = 2 * h + ((s16 & 3) >> 1);               // + 4*b
+  const int sw = (s16 >> 2) & 3;                      // V swizzle of those rows (4-chunk units)
+  const int cbase = 2 * (q4 & 1) + ((s16 & 3) >> 1);  // + 4b
   const int half = (s16 & 1) << 3;
-  // dv block b = 4j + i reads chunk (4b + cbase) ^ 4sw = 16j + 4(i ^ sw) + cbase:
-  // 4 lane offsets, j is an immediate offset of 256 bytes.
+  // dv block b = 4j + i reads chunk (4b + cbase) ^ 4sw = 16j + 4(i ^ sw) + cbase
   int voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = ((4 * (i ^ sw) + cbase) << 4) + half;
+  bf16x8 pf[2];  // P^T for keys 0..15 and 16..31 of the tile (lane's row, slot order)
 #pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2) {
-    bf16x8 pf;
-    {
-      const uint32_t w[4] = {pk[4 * c2], pk[4 * c2 + 1], pk[4 * c2 + 2], pk[4 * c2 + 3]};
-      pf = *reinterpret_cast<const bf16x8*>(w);
-    }
-    const uint8_t* v0 = sV + (16 * c2 + krow_lo) * 1024;
-    const uint8_t* v1 = v0 + 8 * 1024;
+  for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const int off = voff[b & 3] + 256 * (b >> 2);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + off));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + off));
-      const short w8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(w8);
-      st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, st.o[b], 0, 0, 0);
+    for (int e = 0; e < 4; ++e) {
+      pf[c2][2 * e] = pk[4 * c2 + e][0];
+      pf[c2][2 * e + 1] = pk[4 * c2 + e][1];
     }
+  const uint8_t* vbase = sV + (4 * (q4 >> 1) + (s16 >> 2)) * 1024;
+  auto vread = [&](int n) -> bf16x8 {  // step n = 16 c2 + b
+    const int c2 = n >> 4, b = n & 15;
+    const uint8_t* p = vbase + 16384 * c2 + voff[b & 3] + 256 * (b >> 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8192));
+    const i16x8 w8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w8);
+  };
+  constexpr int kV = 3;  // V fragments read this many MFMAs ahead
+  bf16x8 vf[kV];
+#pragma unroll
+  for (int n = 0; n < kV; ++n) vf[n] = vread(n);
+#pragma unroll
+  for (int n = 0; n < 32; ++n) {
+    const int b = n & 15;
+    st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n % kV], pf[n >> 4], st.o[b], 0, 0, 0);
+    if (n + kV < 32) vf[n % kV] = vread(n + kV);
+    if ((n & 7) == 7 && copy_next) dma_row(nc, 4 + (n >> 3), wave, lane);
+  }
+#pragma unroll
+  for (int n = 0; n < kV; ++n) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+  for (int n = 0; n < 32; ++n) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    if (n + kV < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    if ((n & 7) == 7) __builtin_amdgcn_sched_group_barrier(0x020, 2, 1);
   }
 }
 
-__global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTile * 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV0[kTile * 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTile * 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTile * 1024];
-
-  // Block -> workgroup: runs of kRun consecutive workgroups stay on one XCD
-  // (blocks are dealt to the 8 XCDs round robin), and the heaviest
-  // workgroups (latest positions, most entries) are dispatched first.
-  const int bid = blockIdx.x;
-  const int jx = bid >> 3, xcd = bid & 7;
-  const int logical = (jx / kRun) * (8 * kRun) + xcd * kRun + (jx % kRun);
-  if (logical >= a.n_wg) return;
-  const int wg = a.n_wg - 1 - logical;
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, l32 = lane & 31;
-  const int row0 = wg * kRowsPerWG;
-  const int last = (row0 + kRowsPerWG < a.rows ? row0 + kRowsPerWG : a.rows) - 1;
-  const int wr0 = row0 + wave * 32 < last ? row0 + wave * 32 : last;
-  const int wr1 = row0 + wave * 32 + 31 < last ? row0 + wave * 32 + 31 : last;
-  const int my_row_raw = row0 + wave * 32 + l32;
-  const int my_row = my_row_raw < last ? my_row_raw : last;
-  const int t = a.q_start + my_row / a.H;
-  const int tw_min = a.q_start + wr0 / a.H, tw_max = a.q_start + wr1 / a.H;
-
-  Tiles ts;
-  const int t_min = a.q_start + row0 / a.H;
-  ts.t_max = a.q_start + last / a.H;
-  ts.nc_wg = n_entries(ts.t_max, a.Nc);
-  ts.w_lo = t_min - (kWindow - 1) > 0 ? t_min - (kWindow - 1) : 0;
-  ts.n_ct = (ts.nc_wg + kTile - 1) / kTile;
-  ts.n_tiles = ts.n_ct + (ts.t_max - ts.w_lo + 1 + kTile - 1) / kTile;
-
-  // Q fragments (B operand of S^T): lane holds row l%32, dims 16ss + 8g .. +8.
-  bf16x8 qf[32];
-  {
-    const uint16_t* qrow = a.q + (size_t)my_row * kD + 8 * (lane >> 5);
-#pragma unroll
-    for (int ss = 0; ss < 32; ++ss) qf[ss] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ss);
-  }
-
-  auto tile_first = [&](int it, int& kind) -> int {
-    if (it < ts.n_ct) {
-      kind = 0;
-      return it * kTile;
-    }
-    kind = 1;
-    return ts.w_lo + (it - ts.n_ct) * kTile;
-  };
-
-  WaveState st;
-  st.m = -INFINITY;
-  st.mseen = -INFINITY;
-  for (int pass = 0;; ++pass) {
-#pragma unroll
-    for (int b = 0; b < 16; ++b) st.o[b] = f32x16{};
-    st.l = 0.0f;
-    st.over = false;
-
-    issue_tile(a, ts, 0, sK0, sV0, wave, lane);
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < ts.n_tiles; it += 2) {
-      int kind;
-      int first;
-      if (it + 1 < ts.n_tiles) issue_tile(a, ts, it + 1, sK1, sV1, wave, lane);
-      first = tile_first(it, kind);
-      compute_tile(a, st, qf, sK0, sV0, kind, first, t, tw_min, tw_max, lane);
-      wait_vmem();
-      __syncthreads();
-      if (it + 1 >= ts.n_tiles) break;
-      if (it + 2 < ts.n_tiles) issue_tile(a, ts, it + 2, sK0, sV0, wave, lane);
-      first = tile_first(it + 1, kind);
-      compute_tile(a, st, qf, sK1, sV1, kind, first, t, tw_min, tw_max, lane);
-      wait_vmem();
-      __syncthreads();
-    }
-    // Scores are weighted against a reference fixed at each row's first
-    // visible tile, so O is never rescaled inside the loop.  Only if some
-    // score rose more than 2^kHeadroom above its reference (possible only
-    // for extreme score ranges) is the workgroup's pass repeated, with the
-    // exact row maximum of the first pass as reference; that cannot overflow.
-    if (pass == 1 || !__syncthreads_or(st.over)) break;
-    st.m = st.mseen;
-  }
-
-  // ---- epilogue: out = O / l * sigmoid(G)
-  const float l_tot = st.l + __shfl_xor(st.l, 32);
-  const float inv = 1.0f / l_tot;
-  if (my_row_raw > last) return;
-  const int g = lane >> 5;
-  const uint16_t* grow = a.g + (size_t)my_row * kD;
+// Epilogue for this lane's row, with the row's gate logits in the wave's LDS
+// region: out = O / l * sigmoid(G).  Lane (row n, half g) owns dims
+// 32b + 8i + 4g .. +3, i.e. bytes 8g.. of chunk 4b+i of row n.  bf16 output is
+// written back over the logits it replaces (same size) and stored later as
+// whole rows; f32 output is stored from registers.
+template <bool kF32>
+__device__ __forceinline__ void gate_rows(const Args& a, const WaveState& st, const Item& it,
+                                          uint8_t* region, int lane, float inv) {
   constexpr float kLog2e = 1.4426950408889634f;
+  const int l32 = lane & 31, g = lane >> 5;
+  uint8_t* row = region + l32 * 1024 + 8 * g;
 #pragma unroll
   for (int b = 0; b < 16; ++b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int dv = 32 * b + 8 * i + 4 * g;
-      const uint2 gw = *reinterpret_cast<const uint2*>(grow + dv);
+      uint8_t* p = row + 256 * (b >> 2) + (((4 * (b & 3) + i) ^ (l32 & 15)) << 4);
+      const uint2 gw = *reinterpret_cast<const uint2*>(p);
       const float gv[4] = {bf16_bits_to_f32(gw.x & 0xFFFFu), bf16_bits_to_f32(gw.x >> 16),
                            bf16_bits_to_f32(gw.y & 0xFFFFu), bf16_bits_to_f32(gw.y >> 16)};
       float r[4];
@@ -336,16 +382,124 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
         const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[e] * kLog2e));
         r[e] = st.o[b][4 * i + e] * inv * sig;
       }
-      if (a.out_f32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (size_t)my_row * kD + dv) =
-            make_float4(r[0], r[1], r[2], r[3]);
+      if (kF32) {
+        if (it.my_row_raw <= it.last)
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (size_t)it.my_row * kD +
+                                     32 * b + 8 * i + 4 * g) = make_float4(r[0], r[1], r[2], r[3]);
       } else {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + (size_t)my_row * kD + dv) =
-            make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+        const bf16x2 lo = __builtin_convertvector((f32x2){r[0], r[1]}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2){r[2], r[3]}, bf16x2);
+        *reinterpret_cast<uint2*>(p) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
       }
     }
   }
 }
+
+// Store the wave's bf16 output rows from its LDS region, one 1 KiB row per
+// instruction (lane i writes chunk i of the row).
+__device__ __forceinline__ void store_rows(const Args& a, int row0w, int last,
+                                           const uint8_t* region, int lane) {
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if (row0w + r > last) break;  // wave-uniform
+    const uint4 v = *reinterpret_cast<const uint4*>(region + r * 1024 + ((lane ^ (r & 15)) << 4));
+    *reinterpret_cast<uint4*>(out + (size_t)(row0w + r) * kD + 8 * lane) = v;
+  }
+}
+
+template <bool kF32>
+__global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
+  // Separate arrays per stage: the compiler then knows a tile copy into one
+  // stage cannot alias reads of the other and inserts no wait between them.
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTile * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTile * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[kTile * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTile * 1024];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, l32 = lane & 31;
+
+  // Items in processing order p = 0, 1, ... are item n_items-1-p (heaviest
+  // first).  Round r covers p in [r*G, (r+1)*G); within a round, XCD x (the
+  // workgroups with blockIdx % 8 == x) takes the run of per_xcd adjacent items
+  // starting at x*per_xcd.
+  const int G = gridDim.x;
+  int p = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
+  if (p >= a.n_items) return;
+  Item it = make_item(a, a.n_items - 1 - p, wave, l32);
+
+  // The wave's 32 KiB staging region for its Q, gate and output rows (the
+  // tile stages are free between items).
+  uint8_t* const region = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
+
+  bf16x8 qf[32];
+  dma_rows(a.q, it.row0 + wave * 32, it.last, region, lane);
+  wait_vmem();
+  read_q(region, lane, qf);
+  __syncthreads();
+  issue_tile(a, it, 0, sK0, sV0, wave, lane);
+
+  for (;;) {
+    WaveState st;
+    st.m = -INFINITY;
+    st.mseen = -INFINITY;
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+      for (int b = 0; b < 16; ++b) st.o[b] = f32x16{};
+      st.l = 0.0f;
+      st.over = false;
+      if (pass > 0) issue_tile(a, it, 0, sK0, sV0, wave, lane);
+      wait_vmem();
+      __syncthreads();
+      for (int i = 0; i < it.n_tiles; i += 2) {
+        int kind, first;
+        first = tile_first(it, i, kind);
+        compute_tile(a, st, qf, sK0, sV0, kind, first, it, lane, wave, i + 1 < it.n_tiles,
+                     tile_copy(a, it, i + 1, sK1, sV1));
+        wait_vmem();
+        __syncthreads();
+        if (i + 1 >= it.n_tiles) break;
+        first = tile_first(it, i + 1, kind);
+        compute_tile(a, st, qf, sK1, sV1, kind, first, it, lane, wave, i + 2 < it.n_tiles,
+                     tile_copy(a, it, i + 2, sK0, sV0));
+        wait_vmem();
+        __syncthreads();
+      }
+      // Only if some score rose more than 2^kHeadroom above its row reference
+      // (possible only for extreme score ranges) is the pass repeated, with the
+      // exact row maximum of the first pass as reference; that cannot overflow.
+      if (pass == 1 || !__syncthreads_or(st.over)) break;
+      st.m = st.mseen;
+    }
+
+    // Epilogue: gate logits in through LDS, output out through LDS (bf16),
+    // then the next item's Q rows in through LDS; all transfers move whole
+    // 1 KiB rows.  The regions alias the tile stages, which are idle here.
+    const float l_tot = st.l + __shfl_xor(st.l, 32);
+    const float inv = 1.0f / l_tot;
+    dma_rows(a.g, it.row0 + wave * 32, it.last, region, lane);
+    wait_vmem();
+    gate_rows<kF32>(a, st, it, region, lane, inv);
+    if (!kF32) store_rows(a, it.row0 + wave * 32, it.last, region, lane);
+    p += G;
+    const bool more = p < a.n_items;
+    Item nx = it;
+    if (more) {
+      nx = make_item(a, a.n_items - 1 - p, wave, l32);
+      dma_rows(a.q, nx.row0 + wave * 32, nx.last, region, lane);
+      wait_vmem();
+      read_q(region, lane, qf);
+    }
+    __syncthreads();  // every wave is done with its region
+    if (more) issue_tile(a, nx, 0, sK0, sV0, wave, lane);
+    if (!more) break;
+    it = nx;
+  }
+}
+
+int g_cus[64];  // CUs per device, looked up once
 
 }  // namespace
 
@@ -365,11 +519,29 @@ hipError_t launch_prefill(const PrefillProblem& p, hipStream_t stream) {
   a.H = p.H;
   a.c = p.scale * 1.4426950408889634f;
   a.out_f32 = p.out_f32 ? 1 : 0;
-  a.n_wg = (a.rows + kRowsPerWG - 1) / kRowsPerWG;
-  if (a.n_wg == 0) return hipSuccess;
-  const int per = 8 * kRun;
-  const int grid = (a.n_wg + per - 1) / per * per;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  a.n_items = (a.rows + kRowsPerItem - 1) / kRowsPerItem;
+  if (a.n_items == 0) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (g_cus[dev] == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_cus[dev] = cus > 0 ? cus : 256;
+  }
+  // One workgroup per CU (LDS and registers allow no more), a multiple of the
+  // 8 XCDs, and no more workgroups than items.
+  int per_xcd = g_cus[dev] / 8;
+  if (per_xcd < 1) per_xcd = 1;
+  const int need = (a.n_items + 7) / 8;
+  if (per_xcd > need) per_xcd = need;
+  a.per_xcd = per_xcd;
+  if (a.out_f32)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(8 * per_xcd), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(8 * per_xcd), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
