@@ -54,6 +54,13 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_row, 16, voff, 0, 0, 0);
 }
 
+// buffer store of 16 bytes per lane at byte offset voff of the buffer; stores at
+// offsets >= the descriptor's size are dropped by the hardware range check.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+__device__ __forceinline__ void store16_buf(__amdgpu_buffer_rsrc_t r, int voff, u32x4 data) {
+  __builtin_amdgcn_raw_buffer_store_b128(data, r, voff, 0, 0);
+}
+
 // s_waitcnt vmcnt(0): wait for this wave's outstanding vector-memory loads,
 // including LDS DMA (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8; expcnt and lgkmcnt left at their "no wait" maxima).
