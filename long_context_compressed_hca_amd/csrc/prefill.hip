@@ -124,14 +124,13 @@ __device__ __forceinline__ Item make_item(const Args& a, int idx, int wave, int 
 }
 
 // Source of one 32-key tile of K or V: a buffer descriptor that covers exactly
-// the tile's valid rows.  Rows past the end repeat the last valid row (finite
-// data; those keys are masked), so every LDS row of the tile is written.  A
-// tile index past the item's last tile gets an empty descriptor: its copy
-// reads nothing (the hardware range check turns every access into zeros), so
-// the pipeline can issue copies without branches.
+// the tile's valid rows.  Reads past its end return zeros (hardware range
+// check), so rows past the tile's last key arrive as zeros: those keys are
+// masked (their weights are 0), and every LDS row of the tile is written.  A
+// tile index past the item's last tile gets an empty descriptor, so the
+// pipeline can issue copies without branches.
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rs;
-  int nrows;
 };
 
 __device__ __forceinline__ TileSrc tile_src(const Args& a, const Item& it, int i, bool v) {
@@ -147,8 +146,8 @@ __device__ __forceinline__ TileSrc tile_src(const Args& a, const Item& it, int i
     last = it.t_max - a.kv_start;
   }
   TileSrc s;
-  s.nrows = last - first + 1 < kTile ? last - first + 1 : kTile;
-  const int bytes = i < it.n_tiles ? s.nrows * kD * 2 : 0;
+  const int nrows = last - first + 1 < kTile ? last - first + 1 : kTile;
+  const int bytes = i < it.n_tiles ? nrows * kD * 2 : 0;
   s.rs = make_rsrc(i < it.n_tiles ? base + (size_t)first * kD : base, bytes);
   return s;
 }
@@ -157,31 +156,12 @@ __device__ __forceinline__ TileSrc tile_src(const Args& a, const Item& it, int i
 __device__ __forceinline__ void dma_k_row(const TileSrc& s, uint8_t* sK, int u, int wave,
                                           int lane) {
   const int r = wave * (kTile / 4) + u;
-  const int src = (r < s.nrows ? r : s.nrows - 1) * 1024;
-  dma16_buf(s.rs, src + ((lane ^ (r & 15)) << 4), (lds_void*)(sK + r * 1024));
+  dma16_buf(s.rs, r * 1024 + ((lane ^ (r & 15)) << 4), (lds_void*)(sK + r * 1024));
 }
 __device__ __forceinline__ void dma_v_row(const TileSrc& s, uint8_t* sV, int u, int wave,
                                           int lane) {
   const int r = wave * (kTile / 4) + u;
-  const int src = (r < s.nrows ? r : s.nrows - 1) * 1024;
-  dma16_buf(s.rs, src + ((lane ^ ((r & 3) << 2)) << 4), (lds_void*)(sV + r * 1024));
-}
-
-// Copy this wave's 32 rows of a [rows, 512] bf16 tensor (rows row0w .. row0w+31)
-// into the wave's 32 KiB LDS region, one 1 KiB row per instruction (coalesced),
-// chunk c of row r stored at c ^ (r & 15).  Rows past `last` repeat `last`.
-__device__ __forceinline__ void dma_rows(const uint16_t* base, int row0w, int last,
-                                         uint8_t* region, int lane) {
-  asm volatile("" : "+v"(lane));
-  const int first = row0w < last ? row0w : last;
-  const int nrows = last - first + 1 < 32 ? last - first + 1 : 32;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)first * kD, nrows * kD * 2);
-#pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    const int src = (r < nrows ? r : nrows - 1) * 1024;
-    dma16_buf(rs, src + ((lane ^ (r & 15)) << 4), (lds_void*)(region + r * 1024));
-    if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-  }
+  dma16_buf(s.rs, r * 1024 + ((lane ^ ((r & 3) << 2)) << 4), (lds_void*)(sV + r * 1024));
 }
 
 // Copy dims 128w .. 128w+127 (256 bytes) of the item's 128 rows of a
@@ -201,18 +181,19 @@ __device__ __forceinline__ void dma_quarter(const uint16_t* base, int row0, int 
   }
 }
 
-// Q fragments (B operand of S^T) from the wave's region: lane holds row l%32,
-// dims 16ss + 8g .. +8, i.e. chunk 2ss+g of its row (same swizzle as K).
-__device__ __forceinline__ void read_q(const uint8_t* region, int lane, bf16x8 (&qf)[32]) {
-  asm volatile("" : "+v"(lane));
-  const int l32 = lane & 31, g = lane >> 5;
-  const uint8_t* row = region + l32 * 1024;
+// Q fragments of the wave's score rows (B operand of S^T), loaded from global
+// memory straight into registers: lane (row l%32, half g) holds dims 16ss +
+// 8g .. +8 of its row for ss = 0..31, so one load instruction covers 32 B of
+// each of 32 rows.  Rows past the item's last repeat the last one.
+__device__ __forceinline__ const uint16_t* q_row(const Args& a, const Item& it, int wave,
+                                                 int lane) {
+  const int r = it.row0 + wave * 32 + (lane & 31);
+  return a.q + (size_t)(r < it.last ? r : it.last) * kD + 8 * (lane >> 5);
+}
+// Fragments ss0 .. ss0+n-1.
+__device__ __forceinline__ void load_q(const uint16_t* row, int ss0, int n, bf16x8 (&qf)[32]) {
 #pragma unroll
-  for (int ss = 0; ss < 32; ++ss) {
-    qf[ss] = *reinterpret_cast<const bf16x8*>(
-        row + 256 * (ss >> 3) + (((2 * (ss & 7) + g) ^ (l32 & 15)) << 4));
-    if ((ss & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int ss = ss0; ss < ss0 + n; ++ss) qf[ss] = *reinterpret_cast<const bf16x8*>(row + 16 * ss);
 }
 
 struct WaveState {
@@ -435,8 +416,8 @@ __device__ __forceinline__ bf16x8 p_frag(const uint8_t* sP, int rb, int c2, int 
 //   carry = scores of tile i+2              32 MFMAs (one VGPR chain)
 //   copies of K(i+3) into sKd, V(i+1) into sVd (empty past the last tile).
 // The three parts are independent; group k issues score MFMA k, PV MFMA k,
-// softmax slice k, the K read three MFMAs ahead and every second group a
-// copy row.  Scheduling barriers keep that
+// softmax slice k, the K read three MFMAs ahead, and groups 5..20 one copy
+// row each.  Scheduling barriers keep that
 // order, so the softmax arithmetic and the score chain's latency hide behind
 // the MFMAs.
 __device__ __forceinline__ void step(const Args& a, WaveState& st, const bf16x8 (&qf)[32],
@@ -444,6 +425,7 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, const bf16x8 
                                      const uint8_t* sP, const uint8_t* sK, uint8_t* sPn,
                                      uint8_t* sKd, uint8_t* sVd, int lane, int wave) {
   asm volatile("" : "+v"(lane));
+  asm volatile("" : "+s"(wave));  // per-row LDS addresses recomputed, not kept in registers
   const int l32 = lane & 31, g = lane >> 5;
   const TileSrc ks = tile_src(a, it, i + 3, false);
   const TileSrc vs = tile_src(a, it, i + 1, true);
@@ -458,13 +440,14 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, const bf16x8 
   auto kread = [&](int ss) {
     return *reinterpret_cast<const bf16x8*>(krow + (kx ^ (32 * (ss & 7))) + 256 * (ss >> 3));
   };
-  // All V^T fragments of the step are read before its first copy is issued:
-  // the compiler cannot tell transpose reads from the copies' LDS writes and
-  // would make every transpose read after a copy wait for all copies.
+  // The V^T fragments of key half 0 are read first, those of half 1 in
+  // groups 1..4, and the copies issued from group 5 on: the compiler cannot
+  // tell transpose reads from the copies' LDS writes and would make every
+  // transpose read after a copy wait for all copies.
   constexpr int kAhead = 3;
   bf16x8 kf[kAhead], vf[8], pf[4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) vf[n] = v_frag(sV, n, lane, wave);
+  for (int n = 0; n < 4; ++n) vf[n] = v_frag(sV, n, lane, wave);
 #pragma unroll
   for (int ss = 0; ss < kAhead; ++ss) kf[ss] = kread(ss);
 #pragma unroll
@@ -484,13 +467,10 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, const bf16x8 
     st.o[4 * (n & 3) + rb] =
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n], pf[rb], st.o[4 * (n & 3) + rb], 0, 0, 0);
     if (k + kAhead < 32) kf[k % kAhead] = kread(k + kAhead);
+    if (k >= 1 && k < 5) vf[k + 3] = v_frag(sV, k + 3, lane, wave);
     if (k >= 12 && k < 16) pf[rb] = p_frag(sP, rb, 1, lane);  // last use of half 0 was MFMA k
-    if (k & 1) {
-      if (k < 16)
-        dma_k_row(ks, sKd, k >> 1, wave, lane);
-      else
-        dma_v_row(vs, sVd, (k - 16) >> 1, wave, lane);
-    }
+    if (k >= 5 && k < 13) dma_k_row(ks, sKd, k - 5, wave, lane);
+    if (k >= 13 && k < 21) dma_v_row(vs, sVd, k - 13, wave, lane);
     sm_slice(a, st, x, sPn, k, lane, wave);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -500,47 +480,52 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, const bf16x8 
 // Gate and normalise the wave's output block (dims 128w.., all 128 rows), with
 // the gate logits staged in `region` by dma_quarter.  bf16 output is written
 // back over the logits (same size, same place) and stored later as row
-// quarters; f32 output is stored from registers.
+// quarters; f32 output is stored from registers.  The 16 logit pieces of a
+// row block are read before any result of that block is written back, so the
+// reads are not ordered behind the writes.  If next_q is set, a quarter of
+// the next item's Q fragments is loaded before each row block.
 template <bool kF32>
 __device__ __forceinline__ void gate_block(const Args& a, const WaveState& st, const Item& it,
-                                           uint8_t* region, const float* sInv, int lane,
-                                           int wave) {
+                                           uint8_t* region, const float* sL, int lane, int wave,
+                                           const uint16_t* next_q, bf16x8 (&qf)[32]) {
   asm volatile("" : "+v"(lane));
   constexpr float kLog2e = 1.4426950408889634f;
   const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
+    if (next_q) load_q(next_q, 8 * rb, 8, qf);
     const int r = 32 * rb + l32;  // item row
-    const float inv = sInv[r];
+    const float l = sL[r];
     uint8_t* row = region + r * 256 + 8 * g;
+    uint2 gw[16];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
+    for (int j = 0; j < 16; ++j)  // j = 4 bb + q: dims 32bb + 8q + 4g .. +3
+      gw[j] = *reinterpret_cast<const uint2*>(row + ((j ^ (r & 15)) << 4));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint8_t* p = row + (((4 * bb + q) ^ (r & 15)) << 4);
-        const uint2 gw = *reinterpret_cast<const uint2*>(p);
-        const float gv[4] = {bf16_bits_to_f32(gw.x & 0xFFFFu), bf16_bits_to_f32(gw.x >> 16),
-                             bf16_bits_to_f32(gw.y & 0xFFFFu), bf16_bits_to_f32(gw.y >> 16)};
-        float o[4];
+    for (int j = 0; j < 16; ++j) {
+      const int bb = j >> 2, q = j & 3;
+      const float gv[4] = {bf16_bits_to_f32(gw[j].x & 0xFFFFu), bf16_bits_to_f32(gw[j].x >> 16),
+                           bf16_bits_to_f32(gw[j].y & 0xFFFFu), bf16_bits_to_f32(gw[j].y >> 16)};
+      float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[e] * kLog2e));
-          o[e] = st.o[4 * bb + rb][4 * q + e] * inv * sig;
-        }
-        if (kF32) {
-          if (it.row0 + r <= it.last)
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) +
-                                       (size_t)(it.row0 + r) * kD + 128 * wave + 32 * bb +
-                                       8 * q + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
-        } else {
-          const bf16x2 lo = __builtin_convertvector((f32x2){o[0], o[1]}, bf16x2);
-          const bf16x2 hi = __builtin_convertvector((f32x2){o[2], o[3]}, bf16x2);
-          *reinterpret_cast<uint2*>(p) =
-              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-        }
+      for (int e = 0; e < 4; ++e) {
+        // O / l * sigmoid(g) = O / (l + l * 2^(-g log2 e))
+        const float den = __builtin_fmaf(l, __builtin_amdgcn_exp2f(-gv[e] * kLog2e), l);
+        o[e] = st.o[4 * bb + rb][4 * q + e] * __builtin_amdgcn_rcpf(den);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (kF32) {
+        if (it.row0 + r <= it.last)
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (size_t)(it.row0 + r) * kD +
+                                     128 * wave + 32 * bb + 8 * q + 4 * g) =
+              make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        const bf16x2 lo = __builtin_convertvector((f32x2){o[0], o[1]}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2){o[2], o[3]}, bf16x2);
+        *reinterpret_cast<uint2*>(row + ((j ^ (r & 15)) << 4)) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -572,7 +557,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTile * 1024];
   __shared__ __attribute__((aligned(1024))) uint8_t sP0[8 * 1024];
   __shared__ __attribute__((aligned(1024))) uint8_t sP1[8 * 1024];
-  __shared__ float sInv[kRowsPerItem];
+  __shared__ float sL[kRowsPerItem];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l32 = lane & 31;
@@ -607,10 +592,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
   uint8_t* const region = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
 
   bf16x8 qf[32];
-  dma_rows(a.q, it.row0 + wave * 32, it.last, region, lane);
-  wait_vmem();
-  read_q(region, lane, qf);
-  __syncthreads();
+  load_q(q_row(a, it, wave, lane), 0, 32, qf);
 
   for (;;) {
     WaveState st;
@@ -669,27 +651,26 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
     }
 
     // Epilogue.  Row sums to every wave, gate logits in through LDS, output out
-    // through LDS (bf16), then the next item's Q rows in through LDS.  The
-    // regions alias the tile stages, which are idle here.
+    // through LDS (bf16).  The regions alias the tile stages, which are idle
+    // here.
     {
       const float l_tot = st.l + __shfl_xor(st.l, 32);
-      if (lane < 32) sInv[wave * 32 + lane] = 1.0f / l_tot;
+      if (lane < 32) sL[wave * 32 + lane] = l_tot;
     }
     dma_quarter(a.g, it.row0, it.last, wave, region, lane);
-    __syncthreads();  // sInv complete
+    __syncthreads();  // sL complete
     wait_vmem();
-    gate_block<kF32>(a, st, it, region, sInv, lane, wave);
-    if (!kF32) store_block(a, it, region, lane, wave);
+    // The next item's Q is loaded while the gate is computed (a quarter of it
+    // before each row block).
     p = next_p();
     const bool more = p >= 0;
-    if (more) {
-      it = make_item(a, a.n_items - 1 - p, wave, l32);
-      dma_rows(a.q, it.row0 + wave * 32, it.last, region, lane);
-      wait_vmem();
-      read_q(region, lane, qf);
-    }
-    __syncthreads();  // every wave is done with its region and with sInv
+    const Item nx = more ? make_item(a, a.n_items - 1 - p, wave, l32) : it;
+    gate_block<kF32>(a, st, it, region, sL, lane, wave, more ? q_row(a, nx, wave, lane) : nullptr,
+                     qf);
+    if (!kF32) store_block(a, it, region, lane, wave);
+    __syncthreads();  // every wave is done with its region and with sL
     if (!more) break;
+    it = nx;
   }
 }
 
