@@ -10,6 +10,7 @@ namespace hca {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -65,5 +66,17 @@ __device__ __forceinline__ void store16_buf(__amdgpu_buffer_rsrc_t r, int voff, 
 // including LDS DMA (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8; expcnt and lgkmcnt left at their "no wait" maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier without the memory fence of __syncthreads() (which waits
+// for every outstanding vector-memory operation, in-flight LDS copies
+// included).  The caller orders memory itself: each wave waits (vmcnt) for
+// the copies the other waves will read, and LDS reads before the barrier are
+// consumed (lgkmcnt waits) before it.  The asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 }  // namespace hca

@@ -67,7 +67,6 @@ constexpr float kHeadroom = 64.0f;  // p = 2^(x - m) stays below 2^64 in a pass
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(8))) short i16x8;
 
 struct Args {
   const uint16_t* q;
