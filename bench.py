@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 METRIC = "HCA attn TFLOP/s (128K prefill, % bf16 MFMA peak); decode HBM GB/s"
 COUNTERS = os.path.join(ROOT, "profiles", "prefill_128k_counters.json")
 PREFILL_SRC = os.path.join(ROOT, "long_context_compressed_hca_amd", "csrc", "prefill.hip")
+COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
 
 
 def visible_keys(t0: int, t1: int, Nc_cap: int | None = None) -> int:
@@ -69,6 +70,72 @@ def load_traffic():
     if c.get("kernel_source_sha256") != sha256(PREFILL_SRC):
         return None
     return c.get("hbm_bytes_per_launch")
+
+
+def counters_workload(args, torch, hca, synth):
+    """One 128K compress + prefill launch and one plain copy of COPY_BYTES, for
+    rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE)."""
+    dev = torch.device("cuda:0")
+    T, H = args.T, 64
+    gen = lambda tid, shape: synth.normal_bf16_device(3, tid, shape, dev)
+    q, g = gen(synth.Q, (T, H, D)), gen(synth.G, (T, H, D))
+    k, v = gen(synth.K, (T, D)), gen(synth.V, (T, D))
+    ck = torch.empty((T // BLOCK, D), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    hca.hca_compress(k, v, ck, cv)
+    hca.hca_attn_prefill(q, g, k, v, ck, cv, out)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print("counters workload done", flush=True)
+
+
+def _pmc_per_kernel(csv_dir, counter):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc csv output dir,
+    grouped by kernel name."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def write_counters(fetch_dir, write_dir):
+    """Scale the prefill kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by
+    what the same counters read for the plain copy of COPY_BYTES, and write
+    the per-launch HBM bytes next to the source hash they belong to."""
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    pick = lambda d, key: [v for n, vs in d.items() if key in n for v in vs]
+    pf_f, pf_w = pick(fetch, "prefill_kernel"), pick(write, "prefill_kernel")
+    cp_f = pick(fetch, "copy") or pick(fetch, "elementwise")
+    cp_w = pick(write, "copy") or pick(write, "elementwise")
+    if not (pf_f and pf_w and cp_f and cp_w):
+        raise SystemExit(f"missing counters: {sorted(fetch)} {sorted(write)}")
+    f_scale = COPY_BYTES / (max(cp_f) * 1024.0)
+    w_scale = COPY_BYTES / (max(cp_w) * 1024.0)
+    rd = float(np.median(pf_f)) * 1024.0 * f_scale
+    wr = float(np.median(pf_w)) * 1024.0 * w_scale
+    T, H = 131072, 64
+    algo = 3 * T * H * D * 2 + 2 * T * D * 2 + 2 * (T // BLOCK) * D * 2
+    rec = {"kernel": "hca prefill_kernel (bf16 out), 128K tokens, 64 heads",
+           "kernel_source_sha256": sha256(PREFILL_SRC),
+           "fetch_kib_per_dispatch": float(np.median(pf_f)),
+           "write_kib_per_dispatch": float(np.median(pf_w)),
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": max(cp_f), "copy_write_kib": max(cp_w),
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+           "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": algo,
+           "traffic_over_algorithmic": (rd + wr) / algo}
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def bench_prefill(args, torch, hca, synth):
@@ -186,7 +253,14 @@ def main():
     ap.add_argument("--cpu-positions", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--counters-workload", action="store_true",
+                    help="one prefill launch + one calibration copy, for rocprofv3 --pmc")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc csv dirs into " + COUNTERS)
     args = ap.parse_args()
+    if args.write_counters:
+        write_counters(*args.write_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
@@ -199,6 +273,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     hca.lib()  # fail loudly if the HIP library is missing
+    if args.counters_workload:
+        counters_workload(args, torch, hca, synth)
+        return
 
     pf = bench_prefill(args, torch, hca, synth)
     value = pf["flops"] / (pf["ms_per_step"] * 1e-3) / 1e12
