@@ -171,42 +171,57 @@ def test_zero_query_averages_visible_values(oracle_mod):
         np.testing.assert_allclose(got[t, 0], rows.mean(axis=0), rtol=1e-13, atol=1e-15)
 
 
+def _golden(name):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        return json.load(f)
+
+
 def test_worked_example_uniform_weights(oracle_mod):
-    # Hand-derived, block = window = 2, D = 2: v_p = (p, -2p); q = 0; G = 0 (gate 1/2).
-    # Entries: e0 = mean(v0, v1) = (0.5, -1), e1 = mean(v2, v3) = (2.5, -5).
-    #   t=0: {v0}            -> (0, 0)
-    #   t=1: {e0, v0, v1}    -> (0.5, -1)
-    #   t=2: {e0, v1, v2}    -> (7/6, -7/3)
-    #   t=3: {e0, e1, v2, v3} -> (2, -4)
-    #   t=4: {e0, e1, v3, v4} -> (2.5, -5)
-    T = 5
-    v = synth.f32_to_bf16_bits(np.array([[p, -2 * p] for p in range(T)], dtype=np.float32))
-    k = synth.f32_to_bf16_bits(np.ones((T, 2), np.float32))
-    q = np.zeros((T, 1, 2), np.uint16)
-    g = np.zeros((T, 1, 2), np.uint16)
-    ck, cv = oracle_mod.compress(k, 2), oracle_mod.compress(v, 2)
-    got = oracle_mod.attn(q, g, np.arange(T), k, v, 0, ck, cv, block=2, window=2, scale=1.0)
-    want = 0.5 * np.array([[0, 0], [0.5, -1], [7 / 6, -7 / 3], [2, -4], [2.5, -5]])
+    # Hand-derived example (tests/golden/worked_uniform_weights.json): q = 0, G = 0.
+    gd = _golden("worked_uniform_weights.json")
+    T, D = len(gd["v"]), gd["D"]
+    v = synth.f32_to_bf16_bits(np.array(gd["v"], dtype=np.float32))
+    k = synth.f32_to_bf16_bits(np.array(gd["k"], dtype=np.float32))
+    q = np.zeros((T, 1, D), np.uint16)
+    g = np.zeros((T, 1, D), np.uint16)
+    b = gd["block"]
+    ck, cv = oracle_mod.compress(k, b), oracle_mod.compress(v, b)
+    got = oracle_mod.attn(q, g, np.arange(T), k, v, 0, ck, cv, block=b, window=gd["window"],
+                          scale=gd["scale"])
+    want = np.array([[float(Fraction(x)) for x in row] for row in gd["expected"]])
     np.testing.assert_allclose(got[:, 0, :], want, rtol=1e-15, atol=1e-15)
 
 
 def test_worked_example_softmax_weights(oracle_mod):
-    # Hand-derived, block = window = 2, D = 1, scale = 1, q = 1, gate = 1 (G = +inf).
-    # k = (0, 1, 0, 2) -> entry keys (0.5, 1); v = (1, 2, 3, 4) -> entry values (1.5, 3.5).
-    e = np.e
-    want = [
-        1.0,                                                                   # t=0: {k0}
-        (e ** .5 * 1.5 + 1 * 1 + e * 2) / (e ** .5 + 1 + e),                   # t=1: {e0,k0,k1}
-        (e ** .5 * 1.5 + e * 2 + 1 * 3) / (e ** .5 + e + 1),                   # t=2: {e0,k1,k2}
-        (e ** .5 * 1.5 + e * 3.5 + 1 * 3 + e ** 2 * 4) / (e ** .5 + e + 1 + e ** 2),  # t=3
-    ]
-    k = synth.f32_to_bf16_bits(np.array([[0], [1], [0], [2]], np.float32))
-    v = synth.f32_to_bf16_bits(np.array([[1], [2], [3], [4]], np.float32))
-    q = synth.f32_to_bf16_bits(np.ones((4, 1, 1), np.float32))
-    g = np.full((4, 1, 1), 0x7F80, np.uint16)
-    ck, cv = oracle_mod.compress(k, 2), oracle_mod.compress(v, 2)
-    got = oracle_mod.attn(q, g, np.arange(4), k, v, 0, ck, cv, block=2, window=2, scale=1.0)
+    # Hand-derived example (tests/golden/worked_softmax_weights.json): q = 1, G = +inf;
+    # expected value of row t = sum_j e^{s_j} v_j / sum_j e^{s_j} over its (s_j, v_j).
+    gd = _golden("worked_softmax_weights.json")
+    want = [sum(np.exp(s) * val for s, val in terms) / sum(np.exp(s) for s, _ in terms)
+            for terms in gd["expected_terms"]]
+    T, b = len(gd["k"]), gd["block"]
+    k = synth.f32_to_bf16_bits(np.array(gd["k"], np.float32))
+    v = synth.f32_to_bf16_bits(np.array(gd["v"], np.float32))
+    q = synth.f32_to_bf16_bits(np.ones((T, 1, 1), np.float32))
+    g = np.full((T, 1, 1), 0x7F80, np.uint16)
+    ck, cv = oracle_mod.compress(k, b), oracle_mod.compress(v, b)
+    got = oracle_mod.attn(q, g, np.arange(T), k, v, 0, ck, cv, block=b, window=gd["window"],
+                          scale=gd["scale"])
     np.testing.assert_allclose(got[:, 0, 0], want, rtol=1e-14)
+
+
+def test_oracle_regression_fixture():
+    # Records the oracle (not an independent pin): tests/golden/make_oracle_fixture.py
+    import importlib.util
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "make_oracle_fixture.py")
+    spec = importlib.util.spec_from_file_location("make_oracle_fixture", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    gd = _golden("oracle_regression_small.json")
+    want = np.array([float.fromhex(x) for x in gd["out"]])
+    np.testing.assert_array_equal(mod.compute().ravel(), want)
 
 
 # ---------------------------------------------------------------- cross-entry identities
