@@ -63,10 +63,20 @@ namespace {
 
 constexpr int kRowsPerItem = 128;
 constexpr int kTile = 32;
+// Bytes between key rows in the LDS stages.  The padding (16 bytes for K, 64
+// for V) spreads the rows over the LDS banks so the MFMA operand reads are
+// conflict free, and every read address is a per-lane base plus an immediate:
+//   K: b128 reads of one 16-byte chunk by 16 consecutive key rows land in 16
+//      different bank groups (row r starts 16 r bytes further round the banks);
+//   V: transpose reads of 64 bytes from each of 4 consecutive key rows cover
+//      all banks once (row r starts 64 r bytes further round).
+constexpr int kKRow = 1024 + 16;
+constexpr int kVRow = 1024 + 64;
 constexpr float kHeadroom = 64.0f;  // p = 2^(x - m) stays below 2^64 in a pass
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 struct Args {
   const uint16_t* q;
@@ -151,33 +161,48 @@ __device__ __forceinline__ TileSrc tile_src(const Args& a, const Item& it, int i
   return s;
 }
 
-// Copy key row u (0..7) of this wave's quarter of a K tile / a V tile.
-__device__ __forceinline__ void dma_k_row(const TileSrc& s, uint8_t* sK, int u, int wave,
-                                          int lane) {
+// Copy key row u (0..7) of this wave's quarter of a tile into a stage whose
+// rows are kRow bytes apart; lane16 = 16 * lane.
+template <int kRow>
+__device__ __forceinline__ void dma_row(const TileSrc& s, uint8_t* stage, int u, int wave,
+                                        int lane16) {
   const int r = wave * (kTile / 4) + u;
-  dma16_buf(s.rs, r * 1024 + ((lane ^ (r & 15)) << 4), (lds_void*)(sK + r * 1024));
-}
-__device__ __forceinline__ void dma_v_row(const TileSrc& s, uint8_t* sV, int u, int wave,
-                                          int lane) {
-  const int r = wave * (kTile / 4) + u;
-  dma16_buf(s.rs, r * 1024 + ((lane ^ ((r & 3) << 2)) << 4), (lds_void*)(sV + r * 1024));
+  dma16_buf(s.rs, lane16 + r * 1024, (lds_void*)(stage + r * kRow));
 }
 
-// Copy dims 128w .. 128w+127 (256 bytes) of the item's 128 rows of a
-// [rows, 512] bf16 tensor into a 32 KiB LDS region: row r at r*256, chunk c of
-// the quarter stored at c ^ (r & 15).  One instruction moves 4 rows.
-__device__ __forceinline__ void dma_quarter(const uint16_t* base, int row0, int last, int wave,
-                                            uint8_t* region, int lane) {
-  asm volatile("" : "+v"(lane));
-  const int nrows = last - row0 + 1;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)row0 * kD, nrows * kD * 2);
+// 256-byte column slices of 32-row blocks move between HBM and 8 KiB LDS
+// regions (row r at r*256, 16-byte chunk c stored at c ^ (r & 15)): the gate
+// logits of row block rb, dims 128w .. 128w+127, for wave w; and quarter qq
+// of the next item's Q (dims 128qq ..) of wave w's 32 score rows.
+// Instruction j (0..7) moves rows 4j .. 4j+3.  The descriptor covers the
+// item's rows of the block only, so rows past the last arrive as zeros (and
+// stores there are dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base, const Item& it,
+                                                             int rb) {
+  const int r0 = it.row0 + 32 * rb;
+  int n = it.last - r0 + 1;
+  n = n < 0 ? 0 : n > 32 ? 32 : n;
+  // Uniform values, kept in scalar registers so the descriptor is scalar.
+  return make_rsrc(static_cast<const uint8_t*>(base) +
+                       (size_t)__builtin_amdgcn_readfirstlane(r0) * (kD * 2),
+                   __builtin_amdgcn_readfirstlane(n * (kD * 2)));
+}
+__device__ __forceinline__ void dma_rows(const __amdgpu_buffer_rsrc_t& rs, int j, int col,
+                                         uint8_t* region, int lane) {
+  const int r = 4 * j + (lane >> 4);
+  dma16_buf(rs, r * 1024 + col + (((lane & 15) ^ (r & 15)) << 4), (lds_void*)(region + j * 1024));
+}
+// Q fragments qf[8qq .. 8qq+7] of the lane's score row from quarter qq staged
+// by dma_rows: dims 128qq + 16j + 8(lane/32) .. +7 = chunk 2j + lane/32.
+__device__ __forceinline__ void read_q_quarter(const uint8_t* region, int qq, int lane,
+                                               bf16x8 (&qf)[32]) {
+  asm volatile("" : "+v"(lane));  // addresses recomputed here, not kept across the loop
+  const int l32 = lane & 31;
+  const uint8_t* row = region + l32 * 256;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const int r = 4 * j + (lane >> 4);
-    const int src = (r < nrows ? r : nrows - 1) * 1024 + 256 * wave;
-    dma16_buf(rs, src + (((lane & 15) ^ (r & 15)) << 4), (lds_void*)(region + j * 1024));
-    if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int j = 0; j < 8; ++j)
+    qf[8 * qq + j] =
+        *reinterpret_cast<const bf16x8*>(row + (((2 * j + (lane >> 5)) ^ (l32 & 15)) << 4));
 }
 
 // Q fragments of the wave's score rows (B operand of S^T), loaded from global
@@ -243,12 +268,11 @@ __device__ __forceinline__ bool tile_full(const Args& a, const Item& it, int i) 
 // last MFMA of a chain carries the 20 that a VALU read of its result needs
 // (the compiler itself emits 12 for this opcode), and no VALU instruction may
 // write an operand within 2 wait states before one of these MFMAs (their
-// operands come from LDS reads; a test checks the generated code for this).
-// A chain accumulating into the same registers issues back to back.
-// The first MFMA of a chain accumulates into the score bias, written by VALU
-// instructions just before: it waits the 2 wait states that needs.
-__device__ __forceinline__ void mfma_s_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+// operands come from LDS and global reads; a test checks the generated code
+// for this).  A chain accumulating into the same registers issues back to
+// back.  The first MFMA of a chain starts from the inline constant 0.
+__device__ __forceinline__ void mfma_s_zero(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_s_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
@@ -259,40 +283,35 @@ __device__ __forceinline__ void mfma_s_last(f32x16& d, const bf16x8& a, const bf
                : "v"(a), "v"(b));
 }
 
+// K fragment of score MFMA ss for this lane (key row lane%32, k-slots
+// 16ss + 8(lane/32) ..): krow = k_row(sK, lane), fragment at krow + 32 ss.
+__device__ __forceinline__ const uint8_t* k_row(const uint8_t* sK, int lane) {
+  return sK + (lane & 31) * kKRow + 16 * (lane >> 5);
+}
+__device__ __forceinline__ bf16x8 k_frag(const uint8_t* krow, int ss) {
+  return *reinterpret_cast<const bf16x8*>(krow + 32 * ss);
+}
+
 // S^T (32 keys x the wave's 32 rows) = K . Q^T for the K tile in sK, with K
-// fragments read kAhead MFMAs ahead; `copy(ss)` is called after MFMA ss
-// (copies of later tiles, spread over the chain).  The order of MFMAs, reads
-// and copies is fixed with scheduling barriers.
-template <int kAhead, typename Copy>
-__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&qf)[32], const uint8_t* sK,
-                                           const f32x16& bias, int lane, Copy copy) {
-  const int l32 = lane & 31, g = lane >> 5;
-  // Step ss reads chunk 2ss+g of key row l32, stored at (2ss+g) ^ (l32&15);
-  // with ss = 8j + i that is 16j + ((2i + g) ^ (l32&15)), so 8 lane offsets
-  // serve all steps (j becomes an immediate offset).
-  const uint8_t* krow = sK + l32 * 1024;
-  int koff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) koff[i] = ((2 * i + g) ^ (l32 & 15)) << 4;
+// fragments read kAhead MFMAs ahead.  The order of MFMAs and reads is fixed
+// with scheduling barriers.
+template <int kAhead>
+__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&qf)[32], const uint8_t* sK, int lane) {
+  const uint8_t* krow = k_row(sK, lane);
   bf16x8 kf[kAhead];
 #pragma unroll
-  for (int ss = 0; ss < kAhead; ++ss)
-    kf[ss] = *reinterpret_cast<const bf16x8*>(krow + koff[ss & 7] + 256 * (ss >> 3));
+  for (int ss = 0; ss < kAhead; ++ss) kf[ss] = k_frag(krow, ss);
   __builtin_amdgcn_sched_barrier(0);
-  f32x16 s = bias;
+  f32x16 s;
 #pragma unroll
   for (int ss = 0; ss < 32; ++ss) {
     if (ss == 0)
-      mfma_s_first(s, kf[0], qf[0]);
+      mfma_s_zero(s, kf[0], qf[0]);
     else if (ss == 31)
       mfma_s_last(s, kf[ss % kAhead], qf[ss]);
     else
       mfma_s_acc(s, kf[ss % kAhead], qf[ss]);
-    if (ss + kAhead < 32) {
-      const int n = ss + kAhead;
-      kf[ss % kAhead] = *reinterpret_cast<const bf16x8*>(krow + koff[n & 7] + 256 * (n >> 3));
-    }
-    copy(ss);
+    if (ss + kAhead < 32) kf[ss % kAhead] = k_frag(krow, ss + kAhead);
     __builtin_amdgcn_sched_barrier(0);
   }
   return s;
@@ -304,10 +323,12 @@ __device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&qf)[32], const uint8_t
 // block `wave`.  Keys outside the lane's visible interval get weight 0 (as
 // does every key of a tile the lane's row cannot see).
 struct SoftmaxTile {
-  f32x16 s;   // scores (-inf where the key is not visible)
-  float mt;   // running max of the scores, then the row max (exp2 domain)
-  float msub;
-  bf16x2 pk[8];
+  f32x16 s;        // scores (-inf where the key is not visible)
+  float mt;        // running max of the scores, then the row max (exp2 domain)
+  float r0, r1;    // the row max of both wave halves
+  float msub;      // the reference subtracted in the exponent
+  f32x2 e;         // two weights in fp32
+  bf16x2 pk[8];    // the weights in bf16
 };
 
 __device__ __forceinline__ void sm_init(SoftmaxTile& x, const f32x16& s) {
@@ -315,45 +336,55 @@ __device__ __forceinline__ void sm_init(SoftmaxTile& x, const f32x16& s) {
   x.mt = -INFINITY;
 }
 
-// The mask of tile i as an additive score bias: 0 for the lane's visible keys,
-// -inf for the others (score register r holds key 8(r/4) + 4(lane/32) + r%4 of
-// the tile).  It is the initial accumulator of the tile's score MFMAs, so the
-// masked scores come out of the MFMAs.  Tiles every score row of the wave sees
-// in full get zeros without the per-key tests.
-__device__ __forceinline__ f32x16 score_bias(const Args& a, const Item& it, int i, int lane) {
-  f32x16 b;
-  if (tile_full(a, it, i)) {
+// Mask tile i's scores: keys the lane's row does not see get -inf (score
+// register r holds key 8(r/4) + 4(lane/32) + r%4 of the tile).  Tiles that
+// every score row of the wave sees in full are left as they are (a
+// wave-uniform branch), so only the few partial tiles of an item pay for it.
+__device__ __forceinline__ void mask_scores(const Args& a, const Item& it, int i, int lane,
+                                            f32x16& s) {
+  if (tile_full(a, it, i)) return;
+  const ScoreTile sc = score_tile(a, it, i);
+  const unsigned width = (unsigned)sc.width;
+  const int d0 = sc.first - sc.lo + 4 * (lane >> 5);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) b[r] = 0.0f;
-  } else {
-    const ScoreTile sc = score_tile(a, it, i);
-    const unsigned width = (unsigned)sc.width;
-    const int d0 = sc.first - sc.lo + 4 * (lane >> 5);
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      b[r] = (unsigned)(d0 + 8 * (r >> 2) + (r & 3)) < width ? 0.0f : -INFINITY;
-  }
-  return b;
+  for (int r = 0; r < 16; ++r)
+    s[r] = (unsigned)(d0 + 8 * (r >> 2) + (r & 3)) < width ? s[r] : -INFINITY;
 }
 
-// Row max over both wave halves (lanes l and l^32 hold the same row), and the
-// reference update: fixed at the row's first tile with a visible key.
-__device__ __forceinline__ void sm_reduce(const Args& a, WaveState& st, SoftmaxTile& x) {
-  float mt = x.mt * a.c;
+// Parts of the softmax that a pipeline step places between its MFMAs:
+//   max j (0..7)       running max over scores 2j, 2j+1
+//   reduce a, b, c     row max over both wave halves (lanes l and l^32 hold
+//                      the same row) and the reference update: fixed at the
+//                      row's first tile with a visible key
+//   exp j (0..7)       weights of scores 2j, 2j+1
+//   pack j             weights to bf16, added to the row sum
+//   write c2 (0, 1)    the weights of key half c2 to LDS
+__device__ __forceinline__ void sm_max(SoftmaxTile& x, int j) {
+  x.mt = fmaxf(fmaxf(x.mt, x.s[2 * j]), x.s[2 * j + 1]);
+}
+__device__ __forceinline__ void sm_reduce_a(const Args& a, SoftmaxTile& x) {
+  const float mt = x.mt * a.c;
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                    false, false);
-  mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  st.mseen = fmaxf(st.mseen, mt);
-  st.m = st.m == -INFINITY ? mt : st.m;
-  st.over |= mt > st.m + kHeadroom;
+  x.r0 = __uint_as_float(sw[0]);
+  x.r1 = __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ void sm_reduce_b(WaveState& st, SoftmaxTile& x) {
+  x.mt = fmaxf(x.r0, x.r1);
+  st.mseen = fmaxf(st.mseen, x.mt);
+  st.m = st.m == -INFINITY ? x.mt : st.m;
+}
+__device__ __forceinline__ void sm_reduce_c(WaveState& st, SoftmaxTile& x) {
+  st.over |= x.mt > st.m + kHeadroom;
   x.msub = st.m == -INFINITY ? 0.0f : st.m;
 }
-
-__device__ __forceinline__ void sm_exp(const Args& a, WaveState& st, SoftmaxTile& x, int j) {
+__device__ __forceinline__ void sm_exp(const Args& a, SoftmaxTile& x, int j) {
+  x.e[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(x.s[2 * j], a.c, -x.msub));
+  x.e[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(x.s[2 * j + 1], a.c, -x.msub));
+}
+__device__ __forceinline__ void sm_pack(WaveState& st, SoftmaxTile& x, int j) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  const f32x2 pr = {__builtin_amdgcn_exp2f(__builtin_fmaf(x.s[2 * j], a.c, -x.msub)),
-                    __builtin_amdgcn_exp2f(__builtin_fmaf(x.s[2 * j + 1], a.c, -x.msub))};
-  x.pk[j] = __builtin_convertvector(pr, bf16x2);
+  x.pk[j] = __builtin_convertvector(x.e, bf16x2);
   st.l = __builtin_amdgcn_fdot2_f32_bf16(x.pk[j], ones, st.l, false);
 }
 
@@ -371,34 +402,42 @@ __device__ __forceinline__ void sm_write(const SoftmaxTile& x, uint8_t* sP, int 
   *reinterpret_cast<bf16x8*>(sP + (wave * 2 + c2) * 1024 + lane * 16) = pf;
 }
 
-// Slice k (0..31) of the softmax.
-__device__ __forceinline__ void sm_slice(const Args& a, WaveState& st, SoftmaxTile& x,
-                                         uint8_t* sP, int k, int lane, int wave) {
-  if (k < 16)
-    x.mt = fmaxf(x.mt, x.s[k]);
-  else if (k == 16)
-    sm_reduce(a, st, x);
-  else if (k < 25)
-    sm_exp(a, st, x, k - 17);
-  else if (k < 27)
-    sm_write(x, sP, k - 25, lane, wave);
+// The softmax parts of pipeline group k: part A goes between the group's
+// score MFMA and its value MFMA, part B after the value MFMA.  Dependent
+// instructions sit in different parts, an MFMA apart.
+__device__ __forceinline__ void sm_part_a(const Args& a, WaveState& st, SoftmaxTile& x,
+                                          uint8_t* sP, int k, int lane, int wave) {
+  if (k == 8)
+    sm_reduce_a(a, x);
+  else if (k == 9)
+    sm_reduce_c(st, x);
+  else if (k >= 10 && k < 18)
+    sm_exp(a, x, k - 10);
+  else if (k == 18 || k == 19)
+    sm_write(x, sP, k - 18, lane, wave);
+}
+__device__ __forceinline__ void sm_part_b(WaveState& st, SoftmaxTile& x, int k) {
+  if (k < 8)
+    sm_max(x, k);
+  else if (k == 8)
+    sm_reduce_b(st, x);
+  else if (k >= 10 && k < 18)
+    sm_pack(st, x, k - 10);
 }
 
-// V^T fragment of PV block n = 4 c2 + bb (keys 16c2.., dims 128w + 32bb..)
-// from the V tile in sV.  Transpose reads: in each 16-lane group, source lane
-// s16 addresses key row 4(lane/32) + s16/4 (+16 c2 + 8 r) and dims 32b +
-// 16((lane/16)&1) + 4(s16&3); the result lane holds 4 keys of one dim.  Dim
-// block b = 4w + bb sits at chunk (4b + cbase) ^ 4sw = 16w + 4(bb ^ sw) + cbase.
-__device__ __forceinline__ bf16x8 v_frag(const uint8_t* sV, int n, int lane, int wave) {
+// V^T fragments of PV block n = 4 c2 + bb (keys 16c2.., dims 128w + 32bb..)
+// from the V tile in sV, by transpose reads: in each 16-lane group, source
+// lane s16 addresses key row 4(lane/32) + s16/4 (+ 16 c2, + 8 for the second
+// read) and dims 128w + 32bb + 16((lane/16)&1) + 4(s16&3); the result lane
+// holds 4 keys of one dim.  vb = v_base(sV, lane, wave).
+__device__ __forceinline__ const uint8_t* v_base(const uint8_t* sV, int lane, int wave) {
   const int s16 = lane & 15, q4 = lane >> 4;
-  const int sw = (s16 >> 2) & 3;
-  const int cbase = 2 * (q4 & 1) + ((s16 & 3) >> 1);
-  const int half = (s16 & 1) << 3;
-  const int c2 = n >> 2, bb = n & 3;
-  const uint8_t* p = sV + (4 * (q4 >> 1) + (s16 >> 2)) * 1024 + 256 * wave + 16384 * c2 +
-                     ((4 * (bb ^ sw) + cbase) << 4) + half;
+  return sV + (4 * (q4 >> 1) + (s16 >> 2)) * kVRow + 256 * wave + 32 * (q4 & 1) + 8 * (s16 & 3);
+}
+__device__ __forceinline__ bf16x8 v_frag(const uint8_t* vb, int n) {
+  const uint8_t* p = vb + 16 * kVRow * (n >> 2) + 64 * (n & 3);
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8192));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * kVRow));
   const i16x8 w8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, w8);
 }
@@ -408,152 +447,186 @@ __device__ __forceinline__ bf16x8 p_frag(const uint8_t* sP, int rb, int c2, int 
   return *reinterpret_cast<const bf16x8*>(sP + (rb * 2 + c2) * 1024 + lane * 16);
 }
 
+// Step kinds.  A full step is the one described below.  The last two steps of
+// an item have no scores left to compute (their score tiles lie past the last
+// tile), so they compute none and leave the Q registers free: the next item's
+// Q comes in through the stages they leave idle (each quarter of it in one
+// stage, each wave's 32 rows x 256 bytes in its own 8 KiB of it), as do the
+// gate logits of row block 2.  Tail steps run with stage parities 0, 1.
+//   kFull:  O += V(i) P(i); softmax of tile i+1; scores of tile i+2; copies
+//   kTailA: O += V(i) P(i); softmax of tile i+1; copy of V(i+1); next Q
+//           quarters 0, 1 into K stages 0, 1
+//   kTailB: O += V(i) P(i); next Q quarters 0, 1 into registers; quarters
+//           2, 3 into the K stages; gate logits of row block 2 into V stage 0
+enum StepKind { kFull, kTailA, kTailB };
+
 // One step of the three-stage tile pipeline.  With tile i's weights P(i) in
 // sP, V(i) in sV, K(i+2) in sK and the scores of tile i+1 in `carry`:
 //   O += V(i) P(i)                         32 MFMAs (accumulator registers)
-//   softmax of tile i+1 -> P(i+1) in sPn    VALU, in slices
+//   softmax of tile i+1 -> P(i+1) in sPn    VALU, in parts
 //   carry = scores of tile i+2              32 MFMAs (one VGPR chain)
 //   copies of K(i+3) into sKd, V(i+1) into sVd (empty past the last tile).
-// The three parts are independent; group k issues score MFMA k, PV MFMA k,
-// softmax slice k, the K read three MFMAs ahead, and groups 5..20 one copy
-// row each.  Scheduling barriers keep that
-// order, so the softmax arithmetic and the score chain's latency hide behind
-// the MFMAs.
-__device__ __forceinline__ void step(const Args& a, WaveState& st, const bf16x8 (&qf)[32],
+// The three parts are independent.  Group k issues score MFMA k, the K read
+// three MFMAs ahead, softmax part A, then value MFMA k, one copy row (groups
+// 5..20) and softmax part B; scheduling barriers keep that order, so the
+// other instructions fill the MFMAs' issue gaps.  The V^T fragments are all
+// read before the first copy: the compiler cannot tell transpose reads from
+// the copies' LDS writes and would make a transpose read after a copy wait
+// for every copy.
+template <int kKind>
+__device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[32],
                                      f32x16& carry, const Item& it, int i, const uint8_t* sV,
                                      const uint8_t* sP, const uint8_t* sK, uint8_t* sPn,
-                                     uint8_t* sKd, uint8_t* sVd, int lane, int wave) {
+                                     uint8_t* sKd, uint8_t* sVd, int lane, int wave,
+                                     const __amdgpu_buffer_rsrc_t& qs) {
   asm volatile("" : "+v"(lane));
   asm volatile("" : "+s"(wave));  // per-row LDS addresses recomputed, not kept in registers
-  const int l32 = lane & 31, g = lane >> 5;
-  const TileSrc ks = tile_src(a, it, i + 3, false);
-  const TileSrc vs = tile_src(a, it, i + 1, true);
+  constexpr bool kScores = kKind == kFull;
+  constexpr bool kSoftmax = kKind != kTailB;
   SoftmaxTile x;
-  sm_init(x, carry);
-  f32x16 s = score_bias(a, it, i + 2, lane);  // scores of tile i+2 accumulate onto its mask
-
-  // K fragment for score MFMA ss: chunk 2ss+g of key row l32, stored at
-  // (2ss+g) ^ (l32&15) = 16j + ((2i + g) ^ (l32&15)) for ss = 8j + i.
-  const uint8_t* krow = sK + l32 * 1024;
-  const int kx = (g ^ (l32 & 15)) << 4;  // chunk offset of step 0; step ss: ^ (32 (ss & 7))
-  auto kread = [&](int ss) {
-    return *reinterpret_cast<const bf16x8*>(krow + (kx ^ (32 * (ss & 7))) + 256 * (ss >> 3));
-  };
-  // The V^T fragments of key half 0 are read first, those of half 1 in
-  // groups 1..4, and the copies issued from group 5 on: the compiler cannot
-  // tell transpose reads from the copies' LDS writes and would make every
-  // transpose read after a copy wait for all copies.
+  if (kSoftmax) sm_init(x, carry);
   constexpr int kAhead = 3;
+  const uint8_t* krow = k_row(sK, lane);
+  const uint8_t* vb = v_base(sV, lane, wave);
   bf16x8 kf[kAhead], vf[8], pf[4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) vf[n] = v_frag(sV, n, lane, wave);
+  for (int n = 0; n < (kScores ? 4 : 8); ++n) vf[n] = v_frag(vb, n);
+  if (kScores) {
 #pragma unroll
-  for (int ss = 0; ss < kAhead; ++ss) kf[ss] = kread(ss);
+    for (int ss = 0; ss < kAhead; ++ss) kf[ss] = k_frag(krow, ss);
+  }
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) pf[rb] = p_frag(sP, rb, 0, lane);
+  const int greg = wave * 8192;
+  if (kKind == kTailB) {  // K stages: parity 1 has sKd = K stage 0
+    read_q_quarter(sKd + greg, 0, lane, qf);
+    read_q_quarter(sK + greg, 1, lane, qf);
+  }
+  if (kSoftmax) mask_scores(a, it, i + 1, lane, x.s);
   __builtin_amdgcn_sched_barrier(0);
 
+  const int lane16 = lane << 4;
+  TileSrc ks, vs;
+  __amdgpu_buffer_rsrc_t gs;
+  if (kKind == kTailB) gs = block_rsrc(a.g, it, 2);
+  f32x16 s;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    if (k == 0)
-      mfma_s_first(s, kf[0], qf[0]);
-    else if (k == 31)
-      mfma_s_last(s, kf[k % kAhead], qf[k]);
-    else
-      mfma_s_acc(s, kf[k % kAhead], qf[k]);
-    // PV MFMA k: block n = k/4 (key half n/4, dim block n%4), row block k%4
+    if (kScores) {
+      if (k == 0)
+        mfma_s_zero(s, kf[0], qf[0]);
+      else if (k == 31)
+        mfma_s_last(s, kf[k % kAhead], qf[k]);
+      else
+        mfma_s_acc(s, kf[k % kAhead], qf[k]);
+      if (k + kAhead < 32) kf[k % kAhead] = k_frag(krow, k + kAhead);
+      if (k >= 1 && k < 5) vf[k + 3] = v_frag(vb, k + 3);
+    }
+    if (kSoftmax) sm_part_a(a, st, x, sPn, k, lane, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    // value MFMA k: block n = k/4 (key half n/4, dim block n%4), row block k%4
     const int n = k >> 2, rb = k & 3;
     st.o[4 * (n & 3) + rb] =
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n], pf[rb], st.o[4 * (n & 3) + rb], 0, 0, 0);
-    if (k + kAhead < 32) kf[k % kAhead] = kread(k + kAhead);
-    if (k >= 1 && k < 5) vf[k + 3] = v_frag(sV, k + 3, lane, wave);
     if (k >= 12 && k < 16) pf[rb] = p_frag(sP, rb, 1, lane);  // last use of half 0 was MFMA k
-    if (k >= 5 && k < 13) dma_k_row(ks, sKd, k - 5, wave, lane);
-    if (k >= 13 && k < 21) dma_v_row(vs, sVd, k - 13, wave, lane);
-    sm_slice(a, st, x, sPn, k, lane, wave);
+    if (kScores) {
+      if (k == 2) ks = tile_src(a, it, i + 3, false);
+      if (k >= 5 && k < 13) dma_row<kKRow>(ks, sKd, k - 5, wave, lane16);
+    }
+    if (kSoftmax) {
+      if (k == 9) vs = tile_src(a, it, i + 1, true);
+      if (k >= 13 && k < 21) dma_row<kVRow>(vs, sVd, k - 13, wave, lane16);
+    }
+    // Tail A (parity 0): K stage 0 = sK, 1 = sKd.  Tail B (parity 1): K
+    // stage 0 = sKd, 1 = sK; the quarters it copies overwrite the ones it
+    // read into registers, so it waits for those reads first.
+    if (kKind == kTailA && k < 8) dma_rows(qs, k, 0, const_cast<uint8_t*>(sK) + greg, lane);
+    if (kKind == kTailA && k >= 8 && k < 16) dma_rows(qs, k - 8, 256, sKd + greg, lane);
+    if (kKind == kTailB && k < 8) dma_rows(gs, k, 256 * wave, sVd + greg, lane);
+    if (kKind == kTailB && k == 8) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (kKind == kTailB && k >= 8 && k < 16) dma_rows(qs, k - 8, 512, sKd + greg, lane);
+    if (kKind == kTailB && k >= 16 && k < 24) dma_rows(qs, k - 16, 768, const_cast<uint8_t*>(sK) + greg, lane);
+    if (kSoftmax) sm_part_b(st, x, k);
     __builtin_amdgcn_sched_barrier(0);
   }
-  carry = s;
+  if (kScores) carry = s;
 }
 
-// Gate and normalise the wave's output block (dims 128w.., all 128 rows), with
-// the gate logits staged in `region` by dma_quarter.  bf16 output is written
-// back over the logits (same size, same place) and stored later as row
-// quarters; f32 output is stored from registers.  The 16 logit pieces of a
-// row block are read before any result of that block is written back, so the
-// reads are not ordered behind the writes.  If next_q is set, a quarter of
-// the next item's Q fragments is loaded before each row block.
+// Gate and normalise row block rb of the wave's output block (dims 128w..,
+// rows 32rb + lane%32), with the gate logits of those rows staged in the
+// wave's region by dma_g_rows.  bf16 output is written back over the logits
+// (same size, same place) and stored by store_rb; f32 output is stored from
+// registers.  The 16 logit pieces are read before any result is written back,
+// so the reads are not ordered behind the writes.
+//   out = O / l * sigmoid(G) = O / (l + l * 2^(-G log2 e))
 template <bool kF32>
-__device__ __forceinline__ void gate_block(const Args& a, const WaveState& st, const Item& it,
-                                           uint8_t* region, const float* sL, int lane, int wave,
-                                           const uint16_t* next_q, bf16x8 (&qf)[32]) {
+__device__ __forceinline__ void gate_rb(const Args& a, const WaveState& st, const Item& it, int rb,
+                                        uint8_t* region, const float* sL, int lane, int wave) {
   asm volatile("" : "+v"(lane));
   constexpr float kLog2e = 1.4426950408889634f;
   const int l32 = lane & 31, g = lane >> 5;
+  const float l = sL[32 * rb + l32];
+  uint8_t* row = region + l32 * 256 + 8 * g;
+  uint2 gw[16];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    if (next_q) load_q(next_q, 8 * rb, 8, qf);
-    const int r = 32 * rb + l32;  // item row
-    const float l = sL[r];
-    uint8_t* row = region + r * 256 + 8 * g;
-    uint2 gw[16];
+  for (int j = 0; j < 16; ++j)  // j = 4 bb + q: dims 32bb + 8q + 4g .. +3
+    gw[j] = *reinterpret_cast<const uint2*>(row + ((j ^ (l32 & 15)) << 4));
 #pragma unroll
-    for (int j = 0; j < 16; ++j)  // j = 4 bb + q: dims 32bb + 8q + 4g .. +3
-      gw[j] = *reinterpret_cast<const uint2*>(row + ((j ^ (r & 15)) << 4));
+  for (int j = 0; j < 16; ++j) {
+    const int bb = j >> 2, q = j & 3;
+    const float gv[4] = {bf16_bits_to_f32(gw[j].x & 0xFFFFu), bf16_bits_to_f32(gw[j].x >> 16),
+                         bf16_bits_to_f32(gw[j].y & 0xFFFFu), bf16_bits_to_f32(gw[j].y >> 16)};
+    float o[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int bb = j >> 2, q = j & 3;
-      const float gv[4] = {bf16_bits_to_f32(gw[j].x & 0xFFFFu), bf16_bits_to_f32(gw[j].x >> 16),
-                           bf16_bits_to_f32(gw[j].y & 0xFFFFu), bf16_bits_to_f32(gw[j].y >> 16)};
-      float o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // O / l * sigmoid(g) = O / (l + l * 2^(-g log2 e))
-        const float den = __builtin_fmaf(l, __builtin_amdgcn_exp2f(-gv[e] * kLog2e), l);
-        o[e] = st.o[4 * bb + rb][4 * q + e] * __builtin_amdgcn_rcpf(den);
-      }
-      if (kF32) {
-        if (it.row0 + r <= it.last)
-          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + (size_t)(it.row0 + r) * kD +
-                                     128 * wave + 32 * bb + 8 * q + 4 * g) =
-              make_float4(o[0], o[1], o[2], o[3]);
-      } else {
-        const bf16x2 lo = __builtin_convertvector((f32x2){o[0], o[1]}, bf16x2);
-        const bf16x2 hi = __builtin_convertvector((f32x2){o[2], o[3]}, bf16x2);
-        *reinterpret_cast<uint2*>(row + ((j ^ (r & 15)) << 4)) =
-            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float den = __builtin_fmaf(l, __builtin_amdgcn_exp2f(-gv[e] * kLog2e), l);
+      o[e] = st.o[4 * bb + rb][4 * q + e] * __builtin_amdgcn_rcpf(den);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (kF32) {
+      if (it.row0 + 32 * rb + l32 <= it.last)
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) +
+                                   (size_t)(it.row0 + 32 * rb + l32) * kD + 128 * wave + 32 * bb +
+                                   8 * q + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+      const bf16x2 lo = __builtin_convertvector((f32x2){o[0], o[1]}, bf16x2);
+      const bf16x2 hi = __builtin_convertvector((f32x2){o[2], o[3]}, bf16x2);
+      // Written with inline asm: the compiler cannot tell this region from
+      // the one the gate logits of row block 3 are being copied into, and
+      // would make an ordinary LDS store wait for that copy.  The asm's
+      // memory clobber keeps later LDS reads behind it.
+      const u32x2 w2 = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      const uint32_t addr = (uint32_t)(uintptr_t)(row + ((j ^ (l32 & 15)) << 4));
+      asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(w2) : "memory");
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Store the wave's bf16 output block (dims 128w.., 128 rows) from its region,
-// 4 row quarters (256 bytes each) per instruction.  The descriptor covers the
-// item's rows only, so stores of rows past the last one are dropped.
-__device__ __forceinline__ void store_block(const Args& a, const Item& it, const uint8_t* region,
-                                            int lane, int wave) {
+// Store row block rb of the wave's bf16 output block from its region, 4 row
+// quarters (256 bytes each) per instruction.  The descriptor covers the
+// item's rows of the block only, so stores of rows past the last are dropped.
+__device__ __forceinline__ void store_rb(const Args& a, const Item& it, int rb,
+                                         const uint8_t* region, int lane, int wave) {
   asm volatile("" : "+v"(lane));
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(static_cast<uint16_t*>(a.out) + (size_t)it.row0 * kD, (it.last - it.row0 + 1) * 1024);
+  const __amdgpu_buffer_rsrc_t rs = block_rsrc(a.out, it, rb);
   const int c = lane & 15;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < 8; ++j) {
     const int r = 4 * j + (lane >> 4);
     const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * 256 + ((c ^ (r & 15)) << 4));
     store16_buf(rs, r * 1024 + 256 * wave + 16 * c, v);
-    if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <bool kF32>
 __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
   // Separate arrays per stage: the compiler then knows a copy into one stage
   // cannot alias reads of another and inserts no wait between them.
-  __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTile * 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTile * 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV0[kTile * 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTile * 1024];
+  __shared__ __attribute__((aligned(256))) uint8_t sK0[kTile * kKRow];
+  __shared__ __attribute__((aligned(256))) uint8_t sK1[kTile * kKRow];
+  __shared__ __attribute__((aligned(256))) uint8_t sV0[kTile * kVRow];
+  __shared__ __attribute__((aligned(256))) uint8_t sV1[kTile * kVRow];
   __shared__ __attribute__((aligned(1024))) uint8_t sP0[8 * 1024];
   __shared__ __attribute__((aligned(1024))) uint8_t sP1[8 * 1024];
   __shared__ float sL[kRowsPerItem];
@@ -586,88 +659,164 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
   if (p < 0) return;
   Item it = make_item(a, a.n_items - 1 - p, wave, l32);
 
-  // The wave's 32 KiB staging region for Q, gate and output (the tile stages
-  // are free between items).
-  uint8_t* const region = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
+  // K(0) and K(1) of an item are copied ahead: for the first item here, for
+  // the next item during the epilogue.
+  auto first_k_copies = [&](const Item& x) {
+    int ln = lane;  // recomputed lane-dependent offsets rather than kept across the loop
+    asm volatile("" : "+v"(ln));
+    const int ln16 = ln << 4;
+    const TileSrc k0 = tile_src(a, x, 0, false), k1 = tile_src(a, x, 1, false);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dma_row<kKRow>(k0, sK0, u, wave, ln16);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dma_row<kKRow>(k1, sK1, u, wave, ln16);
+  };
+  // The wave's 8 KiB slice of an LDS stage for staged Q quarters and gate
+  // logits (and bf16 output).
+  const int greg = wave * 8192;
 
   bf16x8 qf[32];
   load_q(q_row(a, it, wave, lane), 0, 32, qf);
+  first_k_copies(it);
 
   for (;;) {
     WaveState st;
     st.m = -INFINITY;
     st.mseen = -INFINITY;
+    p = next_p();
+    const bool more = p >= 0;
+    const Item nx = more ? make_item(a, a.n_items - 1 - p, wave, l32) : it;
+    // The next item's Q rows of this wave (none past the last item).
+    const __amdgpu_buffer_rsrc_t next_qs = make_rsrc(
+        a.q + (size_t)__builtin_amdgcn_readfirstlane(nx.row0 + 32 * wave) * kD,
+        more ? __builtin_amdgcn_readfirstlane(
+                   (nx.last - nx.row0 - 32 * wave + 1 < 0    ? 0
+                    : nx.last - nx.row0 - 32 * wave + 1 > 32 ? 32
+                                                             : nx.last - nx.row0 - 32 * wave + 1) *
+                   (kD * 2))
+             : 0);
     for (int pass = 0;; ++pass) {
 #pragma unroll
       for (int b = 0; b < 16; ++b) st.o[b] = f32x16{};
       st.l = 0.0f;
       st.over = false;
-      // Prologue: K(0), V(0), K(1) in; scores of tiles 0 and 1; K(2) in;
-      // weights of tile 0.
+      // Steps: N = max(n_tiles, 2) of them (an item with a single tile runs a
+      // second on a tile past its last, which adds zeros); the last two are
+      // tail steps, the M = N - 2 before them full steps.  Step i reads V(i),
+      // P(i) and K(i+2) from the stages of parity (i + M) & 1, so the tail
+      // steps always use parities 0 and 1.
+      const int M = (it.n_tiles > 2 ? it.n_tiles : 2) - 2;
+      const bool odd = M & 1;
+      // Prologue: scores of tiles 0 and 1; K(2) and V(0) in; weights of tile 0.
       f32x16 carry;
       {
-        int ln = lane;  // recomputed lane-dependent offsets rather than kept across the loop
+        if (pass) {
+          load_q(q_row(a, it, wave, lane), 0, 32, qf);
+          first_k_copies(it);
+        }
+        int ln = lane;
         asm volatile("" : "+v"(ln));
-        const TileSrc k0 = tile_src(a, it, 0, false), v0 = tile_src(a, it, 0, true);
-        const TileSrc k1 = tile_src(a, it, 1, false);
+        const int ln16 = ln << 4;
+        // This wave's copies of K(0), K(1) and its Q done, then everyone's.
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        barrier_no_fence();
+        f32x16 s0 = qk_chain<4>(qf, sK0, ln);
+        carry = qk_chain<4>(qf, sK1, ln);
+        barrier_no_fence();  // every wave's reads of K(0) are done
+        const TileSrc k2 = tile_src(a, it, 2, false), v0 = tile_src(a, it, 0, true);
+        uint8_t* const sK2 = odd ? sK1 : sK0;
+        uint8_t* const sVs = odd ? sV1 : sV0;
+        uint8_t* const sPs = odd ? sP1 : sP0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dma_k_row(k0, sK0, u, wave, ln);
+        for (int u = 0; u < 8; ++u) dma_row<kKRow>(k2, sK2, u, wave, ln16);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dma_v_row(v0, sV0, u, wave, ln);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) dma_k_row(k1, sK1, u, wave, ln);
-        wait_vmem();
-        __syncthreads();
-        const f32x16 s0 = qk_chain<4>(qf, sK0, score_bias(a, it, 0, ln), ln, [](int) {});
-        carry = qk_chain<4>(qf, sK1, score_bias(a, it, 1, ln), ln, [](int) {});
-        __syncthreads();
-        const TileSrc k2 = tile_src(a, it, 2, false);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) dma_k_row(k2, sK0, u, wave, ln);
+        for (int u = 0; u < 8; ++u) dma_row<kVRow>(v0, sVs, u, wave, ln16);
+        mask_scores(a, it, 0, ln, s0);
         SoftmaxTile x;
         sm_init(x, s0);
 #pragma unroll
-        for (int k = 0; k < 27; ++k) sm_slice(a, st, x, sP0, k, ln, wave);
+        for (int k = 0; k < 20; ++k) {
+          sm_part_a(a, st, x, sPs, k, ln, wave);
+          sm_part_b(st, x, k);
+        }
         wait_vmem();
         __syncthreads();
       }
-      // Step i: V(i) in sV[i&1], P(i) in sP[i&1], K(i+2) in sK[i&1]; it
-      // writes P(i+1) into sP[(i+1)&1] and copies K(i+3) and V(i+1) into the
-      // other stages.  Steps past the last tile only add zeros.
-      for (int i = 0; i < it.n_tiles; i += 2) {
-        step(a, st, qf, carry, it, i, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave);
+      // Full step i (parity p): V(i) in sV[p], P(i) in sP[p], K(i+2) in sK[p];
+      // it writes P(i+1) into sP[1-p] and copies K(i+3) and V(i+1) into the
+      // other stages.  With M odd, the first step runs in the parity-1 slot.
+      int i = 0;
+      bool slot0 = !odd;
+      for (;;) {
+        if (slot0) {
+          if (i >= M) break;
+          step<kFull>(a, st, qf, carry, it, i, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs);
+          wait_vmem();
+          __syncthreads();
+          ++i;
+        }
+        slot0 = true;
+        if (i >= M) break;
+        step<kFull>(a, st, qf, carry, it, i, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs);
         wait_vmem();
         __syncthreads();
-        step(a, st, qf, carry, it, i + 1, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave);
-        wait_vmem();
-        __syncthreads();
+        ++i;
       }
+      step<kTailA>(a, st, qf, carry, it, M, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs);
+      wait_vmem();
+      __syncthreads();
+      step<kTailB>(a, st, qf, carry, it, M + 1, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs);
+      wait_vmem();
+      __syncthreads();
       // Only if some score rose more than 2^kHeadroom above its row reference
       // (possible only for extreme score ranges) is the pass repeated, with the
       // exact row maximum of the first pass as reference; that cannot overflow.
+      // The tail steps have started on the next item's Q: the repeat loads
+      // this item's again.
       if (pass == 1 || !__syncthreads_or(st.over)) break;
       st.m = st.mseen;
     }
 
-    // Epilogue.  Row sums to every wave, gate logits in through LDS, output out
-    // through LDS (bf16).  The regions alias the tile stages, which are idle
-    // here.
+    // Epilogue.  Row sums to every wave through LDS.  The next item's Q
+    // quarters 2, 3 are read from the K stages, which then take the gate
+    // logits of row blocks 0, 1; those of block 2 arrived during the last
+    // step, those of block 3 are copied into V stage 1 now.  Blocks 2, 3 are
+    // gated while the logits of 0, 1 arrive.
+    read_q_quarter(sK0 + greg, 2, lane, qf);
+    read_q_quarter(sK1 + greg, 3, lane, qf);
     {
       const float l_tot = st.l + __shfl_xor(st.l, 32);
       if (lane < 32) sL[wave * 32 + lane] = l_tot;
     }
-    dma_quarter(a.g, it.row0, it.last, wave, region, lane);
-    __syncthreads();  // sL complete
-    wait_vmem();
-    // The next item's Q is loaded while the gate is computed (a quarter of it
-    // before each row block).
-    p = next_p();
-    const bool more = p >= 0;
-    const Item nx = more ? make_item(a, a.n_items - 1 - p, wave, l32) : it;
-    gate_block<kF32>(a, st, it, region, sL, lane, wave, more ? q_row(a, nx, wave, lane) : nullptr,
-                     qf);
-    if (!kF32) store_block(a, it, region, lane, wave);
-    __syncthreads();  // every wave is done with its region and with sL
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const __amdgpu_buffer_rsrc_t gs = block_rsrc(a.g, it, 3);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) dma_rows(gs, jj, 256 * wave, sV1 + greg, ln);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): row sums written, Q read
+    barrier_no_fence();                  // everyone's
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const __amdgpu_buffer_rsrc_t g0 = block_rsrc(a.g, it, 0), g1 = block_rsrc(a.g, it, 1);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) dma_rows(g0, jj, 256 * wave, sK0 + greg, ln);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) dma_rows(g1, jj, 256 * wave, sK1 + greg, ln);
+    }
+    gate_rb<kF32>(a, st, it, 2, sV0 + greg, sL, lane, wave);
+    if (!kF32) store_rb(a, it, 2, sV0 + greg, lane, wave);
+    gate_rb<kF32>(a, st, it, 3, sV1 + greg, sL, lane, wave);
+    if (!kF32) store_rb(a, it, 3, sV1 + greg, lane, wave);
+    gate_rb<kF32>(a, st, it, 0, sK0 + greg, sL, lane, wave);
+    if (!kF32) store_rb(a, it, 0, sK0 + greg, lane, wave);
+    gate_rb<kF32>(a, st, it, 1, sK1 + greg, sL, lane, wave);
+    if (!kF32) store_rb(a, it, 1, sK1 + greg, lane, wave);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the K stages are done
+    barrier_no_fence();                  // everyone's
+    if (more) first_k_copies(nx);
     if (!more) break;
     it = nx;
   }
