@@ -109,8 +109,11 @@ struct Item {
   int tw_min, tw_max;  // positions of the wave's first and last score rows
   int nc_wg;           // entries visible to the last row of the item
   int w_lo;            // first raw position of the item's window union
+  int wlen;            // raw positions in the window union
   int n_ct;            // compressed tiles
   int n_tiles;
+  int e_full;          // tiles 0 .. e_full-1 and wf_lo .. wf_hi are seen in full
+  int wf_lo, wf_hi;    // by every score row of the wave
 };
 
 __device__ __forceinline__ Item make_item(const Args& a, int idx, int wave, int l32) {
@@ -127,8 +130,17 @@ __device__ __forceinline__ Item make_item(const Args& a, int idx, int wave, int 
   it.t_max = a.q_start + it.last / a.H;
   it.nc_wg = n_entries(it.t_max, a.Nc);
   it.w_lo = t_min - (kWindow - 1) > 0 ? t_min - (kWindow - 1) : 0;
+  it.wlen = it.t_max - it.w_lo + 1;
   it.n_ct = (it.nc_wg + kTile - 1) / kTile;
-  it.n_tiles = it.n_ct + (it.t_max - it.w_lo + 1 + kTile - 1) / kTile;
+  it.n_tiles = it.n_ct + (it.wlen + kTile - 1) / kTile;
+  // Entry tile i is full if its last entry is visible to the wave's first
+  // row; window tile j (keys w_lo + 32j ..) if its keys lie within the
+  // windows of both the wave's first and last rows.
+  it.e_full = n_entries(it.tw_min, a.Nc) / kTile;
+  const int x = it.tw_max - (kWindow - 1) - it.w_lo;  // first full: 32j >= x
+  const int y = it.tw_min - (kTile - 1) - it.w_lo;    // last full: 32j <= y
+  it.wf_lo = it.n_ct + (x <= 0 ? 0 : (x + kTile - 1) / kTile);
+  it.wf_hi = it.n_ct + (y < 0 ? -1 : y / kTile);
   return it;
 }
 
@@ -143,21 +155,17 @@ struct TileSrc {
 };
 
 __device__ __forceinline__ TileSrc tile_src(const Args& a, const Item& it, int i, bool v) {
-  const uint16_t* base;
-  int first, last;
-  if (i < it.n_ct) {
-    base = v ? a.cv : a.ck;
-    first = i * kTile;
-    last = it.nc_wg - 1;
-  } else {
-    base = v ? a.v : a.k;
-    first = it.w_lo + (i - it.n_ct) * kTile - a.kv_start;
-    last = it.t_max - a.kv_start;
-  }
-  TileSrc s;
-  const int nrows = last - first + 1 < kTile ? last - first + 1 : kTile;
-  const int bytes = i < it.n_tiles ? nrows * kD * 2 : 0;
-  s.rs = make_rsrc(i < it.n_tiles ? base + (size_t)first * kD : base, bytes);
+  // Tile i is tile rel of the entries (rows 0 .. nc_wg-1) or of the window
+  // (rows w_lo .. t_max); past the last tile it has no rows.
+  const bool ent = i < it.n_ct;
+  const int rel = ent ? i : i - it.n_ct;
+  int n = (ent ? it.nc_wg : it.wlen) - rel * kTile;
+  n = n < 0 ? 0 : n > kTile ? kTile : n;
+  const uint16_t* base = ent ? (v ? a.cv : a.ck) : (v ? a.v : a.k);
+  const int r0 = (ent ? 0 : it.w_lo - a.kv_start) + rel * kTile;
+  TileSrc s;  // uniform values, kept in scalar registers so the descriptor is scalar
+  s.rs = make_rsrc(base + (size_t)__builtin_amdgcn_readfirstlane(r0) * kD,
+                   __builtin_amdgcn_readfirstlane(n * kD * 2));
   return s;
 }
 
@@ -254,10 +262,7 @@ __device__ __forceinline__ ScoreTile score_tile(const Args& a, const Item& it, i
 // Whether every score row of the wave sees every key of tile i (no masking
 // needed).  Wave-uniform.
 __device__ __forceinline__ bool tile_full(const Args& a, const Item& it, int i) {
-  if (i >= it.n_tiles) return false;
-  if (i < it.n_ct) return i * kTile + kTile <= n_entries(it.tw_min, a.Nc);
-  const int first = it.w_lo + (i - it.n_ct) * kTile;
-  return first >= it.tw_max - (kWindow - 1) && first + kTile - 1 <= it.tw_min;
+  return i < it.e_full || (i >= it.wf_lo && i <= it.wf_hi);
 }
 
 // The score accumulator S^T is kept in VGPRs: the 256 accumulator registers
@@ -283,11 +288,25 @@ __device__ __forceinline__ void mfma_s_last(f32x16& d, const bf16x8& a, const bf
                : "v"(a), "v"(b));
 }
 
-// K fragment of score MFMA ss for this lane (key row lane%32, k-slots
-// 16ss + 8(lane/32) ..): krow = k_row(sK, lane), fragment at krow + 32 ss.
-__device__ __forceinline__ const uint8_t* k_row(const uint8_t* sK, int lane) {
-  return sK + (lane & 31) * kKRow + 16 * (lane >> 5);
+// Lane-dependent byte offsets of the operand reads, computed once per kernel
+// (the step adds the stage base, and for V the wave's 256-byte column):
+//   k: K row lane%32, chunk lane/32 (k_row)
+//   v: V^T transpose-read source of the lane (v_base)
+//   p: 16 * lane (weights, copies)
+struct LaneOff {
+  int k, v, p;
+};
+__device__ __forceinline__ LaneOff lane_offsets(int lane) {
+  const int s16 = lane & 15, q4 = lane >> 4;
+  LaneOff o;
+  o.k = (lane & 31) * kKRow + 16 * (lane >> 5);
+  o.v = (4 * (q4 >> 1) + (s16 >> 2)) * kVRow + 32 * (q4 & 1) + 8 * (s16 & 3);
+  o.p = lane * 16;
+  return o;
 }
+
+// K fragment of score MFMA ss for this lane (key row lane%32, k-slots
+// 16ss + 8(lane/32) ..): krow = sK + LaneOff::k, fragment at krow + 32 ss.
 __device__ __forceinline__ bf16x8 k_frag(const uint8_t* krow, int ss) {
   return *reinterpret_cast<const bf16x8*>(krow + 32 * ss);
 }
@@ -296,8 +315,8 @@ __device__ __forceinline__ bf16x8 k_frag(const uint8_t* krow, int ss) {
 // fragments read kAhead MFMAs ahead.  The order of MFMAs and reads is fixed
 // with scheduling barriers.
 template <int kAhead>
-__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&qf)[32], const uint8_t* sK, int lane) {
-  const uint8_t* krow = k_row(sK, lane);
+__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&qf)[32], const uint8_t* sK, int koff) {
+  const uint8_t* krow = sK + koff;
   bf16x8 kf[kAhead];
 #pragma unroll
   for (int ss = 0; ss < kAhead; ++ss) kf[ss] = k_frag(krow, ss);
@@ -429,11 +448,7 @@ __device__ __forceinline__ void sm_part_b(WaveState& st, SoftmaxTile& x, int k) 
 // from the V tile in sV, by transpose reads: in each 16-lane group, source
 // lane s16 addresses key row 4(lane/32) + s16/4 (+ 16 c2, + 8 for the second
 // read) and dims 128w + 32bb + 16((lane/16)&1) + 4(s16&3); the result lane
-// holds 4 keys of one dim.  vb = v_base(sV, lane, wave).
-__device__ __forceinline__ const uint8_t* v_base(const uint8_t* sV, int lane, int wave) {
-  const int s16 = lane & 15, q4 = lane >> 4;
-  return sV + (4 * (q4 >> 1) + (s16 >> 2)) * kVRow + 256 * wave + 32 * (q4 & 1) + 8 * (s16 & 3);
-}
+// holds 4 keys of one dim.  vb = sV + LaneOff::v + 256 * wave.
 __device__ __forceinline__ bf16x8 v_frag(const uint8_t* vb, int n) {
   const uint8_t* p = vb + 16 * kVRow * (n >> 2) + 64 * (n & 3);
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
@@ -442,9 +457,9 @@ __device__ __forceinline__ bf16x8 v_frag(const uint8_t* vb, int n) {
   return __builtin_bit_cast(bf16x8, w8);
 }
 
-// P^T fragment of row block rb, key half c2.
-__device__ __forceinline__ bf16x8 p_frag(const uint8_t* sP, int rb, int c2, int lane) {
-  return *reinterpret_cast<const bf16x8*>(sP + (rb * 2 + c2) * 1024 + lane * 16);
+// P^T fragment of row block rb, key half c2 (poff = 16 * lane).
+__device__ __forceinline__ bf16x8 p_frag(const uint8_t* sP, int rb, int c2, int poff) {
+  return *reinterpret_cast<const bf16x8*>(sP + poff + (rb * 2 + c2) * 1024);
 }
 
 // Step kinds.  A full step is the one described below.  The last two steps of
@@ -478,16 +493,17 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
                                      f32x16& carry, const Item& it, int i, const uint8_t* sV,
                                      const uint8_t* sP, const uint8_t* sK, uint8_t* sPn,
                                      uint8_t* sKd, uint8_t* sVd, int lane, int wave,
-                                     const __amdgpu_buffer_rsrc_t& qs) {
+                                     const __amdgpu_buffer_rsrc_t& qs, LaneOff lo) {
   asm volatile("" : "+v"(lane));
   asm volatile("" : "+s"(wave));  // per-row LDS addresses recomputed, not kept in registers
+  asm volatile("" : "+v"(lo.k), "+v"(lo.v), "+v"(lo.p));  // one register each
   constexpr bool kScores = kKind == kFull;
   constexpr bool kSoftmax = kKind != kTailB;
   SoftmaxTile x;
   if (kSoftmax) sm_init(x, carry);
   constexpr int kAhead = 3;
-  const uint8_t* krow = k_row(sK, lane);
-  const uint8_t* vb = v_base(sV, lane, wave);
+  const uint8_t* krow = sK + lo.k;
+  const uint8_t* vb = sV + lo.v + 256 * wave;
   bf16x8 kf[kAhead], vf[8], pf[4];
 #pragma unroll
   for (int n = 0; n < (kScores ? 4 : 8); ++n) vf[n] = v_frag(vb, n);
@@ -496,7 +512,7 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
     for (int ss = 0; ss < kAhead; ++ss) kf[ss] = k_frag(krow, ss);
   }
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) pf[rb] = p_frag(sP, rb, 0, lane);
+  for (int rb = 0; rb < 4; ++rb) pf[rb] = p_frag(sP, rb, 0, lo.p);
   const int greg = wave * 8192;
   if (kKind == kTailB) {  // K stages: parity 1 has sKd = K stage 0
     read_q_quarter(sKd + greg, 0, lane, qf);
@@ -505,7 +521,7 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
   if (kSoftmax) mask_scores(a, it, i + 1, lane, x.s);
   __builtin_amdgcn_sched_barrier(0);
 
-  const int lane16 = lane << 4;
+  const int lane16 = lo.p;
   TileSrc ks, vs;
   __amdgpu_buffer_rsrc_t gs;
   if (kKind == kTailB) gs = block_rsrc(a.g, it, 2);
@@ -528,7 +544,7 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
     const int n = k >> 2, rb = k & 3;
     st.o[4 * (n & 3) + rb] =
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n], pf[rb], st.o[4 * (n & 3) + rb], 0, 0, 0);
-    if (k >= 12 && k < 16) pf[rb] = p_frag(sP, rb, 1, lane);  // last use of half 0 was MFMA k
+    if (k >= 12 && k < 16) pf[rb] = p_frag(sP, rb, 1, lo.p);  // last use of half 0 was MFMA k
     if (kScores) {
       if (k == 2) ks = tile_src(a, it, i + 3, false);
       if (k >= 5 && k < 13) dma_row<kKRow>(ks, sKd, k - 5, wave, lane16);
@@ -675,6 +691,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
   // logits (and bf16 output).
   const int greg = wave * 8192;
 
+  const LaneOff lo = lane_offsets(lane);
   bf16x8 qf[32];
   load_q(q_row(a, it, wave, lane), 0, 32, qf);
   first_k_copies(it);
@@ -720,8 +737,8 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
         // This wave's copies of K(0), K(1) and its Q done, then everyone's.
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
         barrier_no_fence();
-        f32x16 s0 = qk_chain<4>(qf, sK0, ln);
-        carry = qk_chain<4>(qf, sK1, ln);
+        f32x16 s0 = qk_chain<4>(qf, sK0, (ln & 31) * kKRow + 16 * (ln >> 5));
+        carry = qk_chain<4>(qf, sK1, (ln & 31) * kKRow + 16 * (ln >> 5));
         barrier_no_fence();  // every wave's reads of K(0) are done
         const TileSrc k2 = tile_src(a, it, 2, false), v0 = tile_src(a, it, 0, true);
         uint8_t* const sK2 = odd ? sK1 : sK0;
@@ -750,22 +767,22 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
       for (;;) {
         if (slot0) {
           if (i >= M) break;
-          step<kFull>(a, st, qf, carry, it, i, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs);
+          step<kFull>(a, st, qf, carry, it, i, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs, lo);
           wait_vmem();
           __syncthreads();
           ++i;
         }
         slot0 = true;
         if (i >= M) break;
-        step<kFull>(a, st, qf, carry, it, i, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs);
+        step<kFull>(a, st, qf, carry, it, i, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs, lo);
         wait_vmem();
         __syncthreads();
         ++i;
       }
-      step<kTailA>(a, st, qf, carry, it, M, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs);
+      step<kTailA>(a, st, qf, carry, it, M, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs, lo);
       wait_vmem();
       __syncthreads();
-      step<kTailB>(a, st, qf, carry, it, M + 1, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs);
+      step<kTailB>(a, st, qf, carry, it, M + 1, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs, lo);
       wait_vmem();
       __syncthreads();
       // Only if some score rose more than 2^kHeadroom above its row reference
