@@ -346,7 +346,8 @@ struct SoftmaxTile {
   float mt;        // running max of the scores, then the row max (exp2 domain)
   float r0, r1;    // the row max of both wave halves
   float msub;      // the reference subtracted in the exponent
-  f32x2 e;         // two weights in fp32
+  f32x2 f[2];      // exponents of score pairs j (in f[j & 1])
+  f32x2 e[2];      // their weights in fp32
   bf16x2 pk[8];    // the weights in bf16
 };
 
@@ -372,38 +373,59 @@ __device__ __forceinline__ void mask_scores(const Args& a, const Item& it, int i
 
 // Parts of the softmax that a pipeline step places between its MFMAs:
 //   max j (0..7)       running max over scores 2j, 2j+1
-//   reduce a, b, c     row max over both wave halves (lanes l and l^32 hold
+//   reduce 0..6        row max over both wave halves (lanes l and l^32 hold
 //                      the same row) and the reference update: fixed at the
 //                      row's first tile with a visible key
-//   exp j (0..7)       weights of scores 2j, 2j+1
-//   pack j             weights to bf16, added to the row sum
+//   fma, exp, cvt, sum j (0..7)  weights of scores 2j, 2j+1: exponent,
+//                      weight, bf16, added to the row sum
 //   write c2 (0, 1)    the weights of key half c2 to LDS
 __device__ __forceinline__ void sm_max(SoftmaxTile& x, int j) {
   x.mt = fmaxf(fmaxf(x.mt, x.s[2 * j]), x.s[2 * j + 1]);
 }
-__device__ __forceinline__ void sm_reduce_a(const Args& a, SoftmaxTile& x) {
-  const float mt = x.mt * a.c;
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                   false, false);
-  x.r0 = __uint_as_float(sw[0]);
-  x.r1 = __uint_as_float(sw[1]);
+// The row max reduction in single dependent operations (r = 0..6).
+__device__ __forceinline__ void sm_reduce(const Args& a, WaveState& st, SoftmaxTile& x, int r) {
+  switch (r) {
+    case 0:
+      x.mt *= a.c;
+      break;
+    case 1: {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.mt),
+                                                       __float_as_uint(x.mt), false, false);
+      x.r0 = __uint_as_float(sw[0]);
+      x.r1 = __uint_as_float(sw[1]);
+      break;
+    }
+    case 2:
+      x.mt = fmaxf(x.r0, x.r1);
+      break;
+    case 3:
+      st.mseen = fmaxf(st.mseen, x.mt);
+      break;
+    case 4:
+      st.m = st.m == -INFINITY ? x.mt : st.m;
+      break;
+    case 5:
+      st.over |= x.mt > st.m + kHeadroom;
+      break;
+    default:
+      x.msub = st.m == -INFINITY ? 0.0f : st.m;
+      break;
+  }
 }
-__device__ __forceinline__ void sm_reduce_b(WaveState& st, SoftmaxTile& x) {
-  x.mt = fmaxf(x.r0, x.r1);
-  st.mseen = fmaxf(st.mseen, x.mt);
-  st.m = st.m == -INFINITY ? x.mt : st.m;
+// Weights of score pair j in four dependent stages, each placed a part
+// (an MFMA) or more after the one before it.
+__device__ __forceinline__ void sm_fma(const Args& a, SoftmaxTile& x, int j) {
+  x.f[j & 1] = (f32x2){__builtin_fmaf(x.s[2 * j], a.c, -x.msub),
+                       __builtin_fmaf(x.s[2 * j + 1], a.c, -x.msub)};
 }
-__device__ __forceinline__ void sm_reduce_c(WaveState& st, SoftmaxTile& x) {
-  st.over |= x.mt > st.m + kHeadroom;
-  x.msub = st.m == -INFINITY ? 0.0f : st.m;
+__device__ __forceinline__ void sm_exp(SoftmaxTile& x, int j) {
+  x.e[j & 1] = (f32x2){__builtin_amdgcn_exp2f(x.f[j & 1][0]), __builtin_amdgcn_exp2f(x.f[j & 1][1])};
 }
-__device__ __forceinline__ void sm_exp(const Args& a, SoftmaxTile& x, int j) {
-  x.e[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(x.s[2 * j], a.c, -x.msub));
-  x.e[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(x.s[2 * j + 1], a.c, -x.msub));
+__device__ __forceinline__ void sm_cvt(SoftmaxTile& x, int j) {
+  x.pk[j] = __builtin_convertvector(x.e[j & 1], bf16x2);
 }
-__device__ __forceinline__ void sm_pack(WaveState& st, SoftmaxTile& x, int j) {
+__device__ __forceinline__ void sm_sum(WaveState& st, const SoftmaxTile& x, int j) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  x.pk[j] = __builtin_convertvector(x.e, bf16x2);
   st.l = __builtin_amdgcn_fdot2_f32_bf16(x.pk[j], ones, st.l, false);
 }
 
@@ -424,24 +446,25 @@ __device__ __forceinline__ void sm_write(const SoftmaxTile& x, uint8_t* sP, int 
 // The softmax parts of pipeline group k: part A goes between the group's
 // score MFMA and its value MFMA, part B after the value MFMA.  Dependent
 // instructions sit in different parts, an MFMA apart.
+//   group  part A                 part B
+//   0..7   -                      max k
+//   8..10  reduce 0, 2, 4         reduce 1, 3, 5
+//   11     reduce 6               -
+//   12..21 fma k-12, sum k-14     exp k-12, cvt k-13   (pairs j = 0..7 only)
+//   21, 22 write 0, 1             -
 __device__ __forceinline__ void sm_part_a(const Args& a, WaveState& st, SoftmaxTile& x,
                                           uint8_t* sP, int k, int lane, int wave) {
-  if (k == 8)
-    sm_reduce_a(a, x);
-  else if (k == 9)
-    sm_reduce_c(st, x);
-  else if (k >= 10 && k < 18)
-    sm_exp(a, x, k - 10);
-  else if (k == 18 || k == 19)
-    sm_write(x, sP, k - 18, lane, wave);
+  if (k >= 8 && k < 11) sm_reduce(a, st, x, 2 * (k - 8));
+  if (k == 11) sm_reduce(a, st, x, 6);
+  if (k >= 12 && k < 20) sm_fma(a, x, k - 12);
+  if (k >= 14 && k < 22) sm_sum(st, x, k - 14);
+  if (k == 21 || k == 22) sm_write(x, sP, k - 21, lane, wave);
 }
-__device__ __forceinline__ void sm_part_b(WaveState& st, SoftmaxTile& x, int k) {
-  if (k < 8)
-    sm_max(x, k);
-  else if (k == 8)
-    sm_reduce_b(st, x);
-  else if (k >= 10 && k < 18)
-    sm_pack(st, x, k - 10);
+__device__ __forceinline__ void sm_part_b(const Args& a, WaveState& st, SoftmaxTile& x, int k) {
+  if (k < 8) sm_max(x, k);
+  if (k >= 8 && k < 11) sm_reduce(a, st, x, 2 * (k - 8) + 1);
+  if (k >= 12 && k < 20) sm_exp(x, k - 12);
+  if (k >= 13 && k < 21) sm_cvt(x, k - 13);
 }
 
 // V^T fragments of PV block n = 4 c2 + bb (keys 16c2.., dims 128w + 32bb..)
@@ -493,7 +516,8 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
                                      f32x16& carry, const Item& it, int i, const uint8_t* sV,
                                      const uint8_t* sP, const uint8_t* sK, uint8_t* sPn,
                                      uint8_t* sKd, uint8_t* sVd, int lane, int wave,
-                                     const __amdgpu_buffer_rsrc_t& qs, LaneOff lo) {
+                                     const __amdgpu_buffer_rsrc_t& qs, LaneOff lo, TileSrc& ks,
+                                     TileSrc& vs) {
   asm volatile("" : "+v"(lane));
   asm volatile("" : "+s"(wave));  // per-row LDS addresses recomputed, not kept in registers
   asm volatile("" : "+v"(lo.k), "+v"(lo.v), "+v"(lo.p));  // one register each
@@ -505,14 +529,19 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
   const uint8_t* krow = sK + lo.k;
   const uint8_t* vb = sV + lo.v + 256 * wave;
   bf16x8 kf[kAhead], vf[8], pf[4];
+  // The operands of the first two MFMAs are read first.
+  if (kScores) kf[0] = k_frag(krow, 0);
+  vf[0] = v_frag(vb, 0);
+  pf[0] = p_frag(sP, 0, 0, lo.p);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int n = 0; n < (kScores ? 4 : 8); ++n) vf[n] = v_frag(vb, n);
+  for (int n = 1; n < (kScores ? 4 : 8); ++n) vf[n] = v_frag(vb, n);
   if (kScores) {
 #pragma unroll
-    for (int ss = 0; ss < kAhead; ++ss) kf[ss] = k_frag(krow, ss);
+    for (int ss = 1; ss < kAhead; ++ss) kf[ss] = k_frag(krow, ss);
   }
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) pf[rb] = p_frag(sP, rb, 0, lo.p);
+  for (int rb = 1; rb < 4; ++rb) pf[rb] = p_frag(sP, rb, 0, lo.p);
   const int greg = wave * 8192;
   if (kKind == kTailB) {  // K stages: parity 1 has sKd = K stage 0
     read_q_quarter(sKd + greg, 0, lane, qf);
@@ -522,7 +551,6 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
   __builtin_amdgcn_sched_barrier(0);
 
   const int lane16 = lo.p;
-  TileSrc ks, vs;
   __amdgpu_buffer_rsrc_t gs;
   if (kKind == kTailB) gs = block_rsrc(a.g, it, 2);
   f32x16 s;
@@ -545,14 +573,14 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
     st.o[4 * (n & 3) + rb] =
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[n], pf[rb], st.o[4 * (n & 3) + rb], 0, 0, 0);
     if (k >= 12 && k < 16) pf[rb] = p_frag(sP, rb, 1, lo.p);  // last use of half 0 was MFMA k
+    // The copies use descriptors made by the previous step (ks: K(i+3), vs:
+    // V(i+1)); this step makes the next step's in its MFMA-bound last groups.
     if (kScores) {
-      if (k == 2) ks = tile_src(a, it, i + 3, false);
       if (k >= 5 && k < 13) dma_row<kKRow>(ks, sKd, k - 5, wave, lane16);
+      if (k == 25) ks = tile_src(a, it, i + 4, false);
     }
-    if (kSoftmax) {
-      if (k == 9) vs = tile_src(a, it, i + 1, true);
-      if (k >= 13 && k < 21) dma_row<kVRow>(vs, sVd, k - 13, wave, lane16);
-    }
+    if (kSoftmax && k >= 13 && k < 21) dma_row<kVRow>(vs, sVd, k - 13, wave, lane16);
+    if (kScores && k == 28) vs = tile_src(a, it, i + 2, true);
     // Tail A (parity 0): K stage 0 = sK, 1 = sKd.  Tail B (parity 1): K
     // stage 0 = sKd, 1 = sK; the quarters it copies overwrite the ones it
     // read into registers, so it waits for those reads first.
@@ -562,7 +590,7 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
     if (kKind == kTailB && k == 8) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     if (kKind == kTailB && k >= 8 && k < 16) dma_rows(qs, k - 8, 512, sKd + greg, lane);
     if (kKind == kTailB && k >= 16 && k < 24) dma_rows(qs, k - 16, 768, const_cast<uint8_t*>(sK) + greg, lane);
-    if (kSoftmax) sm_part_b(st, x, k);
+    if (kSoftmax) sm_part_b(a, st, x, k);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (kScores) carry = s;
@@ -726,6 +754,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
       const bool odd = M & 1;
       // Prologue: scores of tiles 0 and 1; K(2) and V(0) in; weights of tile 0.
       f32x16 carry;
+      TileSrc ks, vs;
       {
         if (pass) {
           load_q(q_row(a, it, wave, lane), 0, 32, qf);
@@ -748,13 +777,15 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
         for (int u = 0; u < 8; ++u) dma_row<kKRow>(k2, sK2, u, wave, ln16);
 #pragma unroll
         for (int u = 0; u < 8; ++u) dma_row<kVRow>(v0, sVs, u, wave, ln16);
+        ks = tile_src(a, it, 3, false);  // copies of the first step
+        vs = tile_src(a, it, 1, true);
         mask_scores(a, it, 0, ln, s0);
         SoftmaxTile x;
         sm_init(x, s0);
 #pragma unroll
-        for (int k = 0; k < 20; ++k) {
+        for (int k = 0; k < 23; ++k) {
           sm_part_a(a, st, x, sPs, k, ln, wave);
-          sm_part_b(st, x, k);
+          sm_part_b(a, st, x, k);
         }
         wait_vmem();
         __syncthreads();
@@ -767,22 +798,22 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
       for (;;) {
         if (slot0) {
           if (i >= M) break;
-          step<kFull>(a, st, qf, carry, it, i, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs, lo);
+          step<kFull>(a, st, qf, carry, it, i, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs, lo, ks, vs);
           wait_vmem();
           __syncthreads();
           ++i;
         }
         slot0 = true;
         if (i >= M) break;
-        step<kFull>(a, st, qf, carry, it, i, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs, lo);
+        step<kFull>(a, st, qf, carry, it, i, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs, lo, ks, vs);
         wait_vmem();
         __syncthreads();
         ++i;
       }
-      step<kTailA>(a, st, qf, carry, it, M, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs, lo);
+      step<kTailA>(a, st, qf, carry, it, M, sV0, sP0, sK0, sP1, sK1, sV1, lane, wave, next_qs, lo, ks, vs);
       wait_vmem();
       __syncthreads();
-      step<kTailB>(a, st, qf, carry, it, M + 1, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs, lo);
+      step<kTailB>(a, st, qf, carry, it, M + 1, sV1, sP1, sK1, sP0, sK0, sV0, lane, wave, next_qs, lo, ks, vs);
       wait_vmem();
       __syncthreads();
       // Only if some score rose more than 2^kHeadroom above its row reference
