@@ -24,16 +24,16 @@
 // Q, stays split by rows.  O (256 accumulator registers) and Q (128 VGPRs)
 // stay in registers for the whole item.
 //
-// Pipeline.  K runs one tile ahead of V: step i computes O += V(i) P(i) and,
-// in the same straight-line block, the scores and weights P(i+1) of the next
-// tile, so the softmax arithmetic fills the gaps between MFMAs.  Meanwhile
-// DMA brings K(i+2) and V(i+1) into the stages freed by step i-1.  LDS:
-// 2 K stages + 2 V stages (32 keys x 1 KiB each) + 2 P buffers (8 KiB).
+// Pipeline.  Step i computes O += V(i) P(i), the softmax of tile i+1 (its
+// scores carried in registers from the step before) and the scores of tile
+// i+2; meanwhile DMA brings K(i+3) and V(i+1) into the stages freed by step
+// i-1.  LDS: 2 K stages + 2 V stages (32 keys each) + 2 P buffers (8 KiB).
 // Tiles are copied global -> LDS by DMA (buffer_load_dwordx4 ... lds, no
-// VGPRs), one 1 KiB key row per wave instruction, with an XOR swizzle of the
-// 16-byte chunks chosen so the read patterns are bank-conflict free:
-//   K: chunk c of key r stored at c ^ (r & 15)   (b128 reads, 16 keys x 1 chunk)
-//   V: chunk c of key r stored at c ^ 4(r & 3)   (b64 transpose reads, 4 keys x 4 chunks)
+// VGPRs), one 1 KiB key row per wave instruction, into padded rows (K:
+// 1040 bytes apart, V: 1088) that keep the operand reads bank-conflict free
+// with immediate offsets.  The last two steps of an item compute no scores;
+// they stage the next item's Q and the first gate logits through the stages
+// they leave idle.
 //
 // Persistent schedule.  The kernel runs one workgroup per CU; each workgroup
 // loops over items.  Items are dealt so that the workgroups of one XCD take
@@ -50,8 +50,9 @@
 //
 // Epilogue: out = O / l * sigmoid(G), sigmoid(x) = 1/(1 + 2^(-x log2 e)),
 // which is exactly 0 at G = -inf and 1 at G = +inf.  bf16 (nearest even) or
-// f32 output.  Q, G and bf16 output move between HBM and registers through
-// LDS so that global traffic is whole rows (or 256-byte row quarters).
+// f32 output.  Q, G and bf16 output move between HBM and LDS as 256-byte row
+// quarters (LDS copies move several times more bytes per CU than loads into
+// registers), gated one 32-row block at a time as their logits arrive.
 //
 // Roofline: 4*512 flop per (row, visible key); at 128K context the kernel is
 // MFMA bound (about 420 flop per HBM byte).
