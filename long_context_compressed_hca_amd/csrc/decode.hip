@@ -84,6 +84,7 @@ __device__ __forceinline__ TileRef tile_ref(const Keys& ks, int i) {
 // entry arrive as zeros (buffer range check); window rows wrap round the ring.
 __device__ __forceinline__ void copy_tile(const Keys& ks, int i, uint8_t* sK, uint8_t* sV,
                                           int wave, int lane16) {
+  asm volatile("" : "+s"(wave), "+s"(i));  // addresses computed here, not kept in registers
   const TileRef tr = tile_ref(ks, i);
   const int bytes = (tr.ent ? ks.nc : kWindow) * 1024;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(tr.ent ? ks.ek : ks.wk, bytes);
@@ -167,6 +168,23 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
 
+  // Q and the gate logits do not depend on the position: their loads go out
+  // first, so their latency overlaps the position's and the first copies'.
+  const int64_t head0 = (int64_t)b * a.H + hg * kHeads;
+  // Q fragments (B operand of the partial scores): head l16, dims 128w +
+  // 32ss + 8g4 .. +8.
+  bf16x8 qf[4];
+  {
+    const uint16_t* qrow = a.q + (head0 + l16) * kD + 128 * wave + 8 * g4;
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss) qf[ss] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ss);
+  }
+  // Gate logits of this lane's output dims (see the epilogue).
+  const int64_t rowo = (head0 + l16) * kD + 128 * wave + 4 * g4;
+  uint2 gw[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) gw[db] = *reinterpret_cast<const uint2*>(a.g + rowo + 16 * db);
+
   // Positions below 2^31 (negative ones read as 0); wave-uniform.
   int64_t t64 = a.pos[b];
   t64 = t64 < 0 ? 0 : (t64 > 0x7FFFFFFF ? 0x7FFFFFFF : t64);
@@ -183,7 +201,6 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   ks.wk = a.wk + (int64_t)b * kWindow * kD;
   ks.wv = a.wv + (int64_t)b * kWindow * kD;
   const int n_tiles = ks.n_tiles;
-  const int64_t head0 = (int64_t)b * a.H + hg * kHeads;
 
   // Lane offsets: K fragment source (row l16, dims 128w + 8g4); V^T
   // transpose read source (key row 4g4 + l16/4, dims 128w + 4(l16&3)); the
@@ -192,15 +209,7 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   const int voff = (4 * g4 + (l16 >> 2)) * kVRow + 256 * wave + 8 * (l16 & 3);
   const int lane16 = lane * 16;
 
-  // Q fragments (B operand of the partial scores): head l16, dims 128w +
-  // 32ss + 8g4 .. +8.
-  bf16x8 qf[4];
-  {
-    const uint16_t* qrow = a.q + (head0 + l16) * kD + 128 * wave + 8 * g4;
-#pragma unroll
-    for (int ss = 0; ss < 4; ++ss) qf[ss] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ss);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // Q in (the copies below are counted from here)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // Q and G in (the copies below are counted from here)
 
   // O^T blocks: o[db] lane (head l16, g4), reg r -> dim 128w + 16db + 4g4 + r
   f32x4 o[8];
@@ -212,6 +221,8 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   // copies tile i+3 into (dK, dV), the stage of tile i-1.
   auto step = [&](int i, const uint8_t* sV, const uint8_t* sKn, const uint8_t* sS,
                   uint8_t* sSn, uint8_t* dK, uint8_t* dV) {
+    int w = wave;
+    asm volatile("" : "+s"(w), "+s"(i));  // per-step values computed here, not kept in registers
     // All LDS reads first (a read after a copy would wait for it), the K
     // fragments of the next tile's scores ahead of the rest so its MFMAs can
     // start while the others are in flight.  Past the last tile, K and
@@ -220,7 +231,7 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     k_frags(sKn, koff, kf);
     f32x4 sp[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) sp[w] = *reinterpret_cast<const f32x4*>(sS + w * 1024 + lane16);
+    for (int u = 0; u < 4; ++u) sp[u] = *reinterpret_cast<const f32x4*>(sS + u * 1024 + lane16);
     i16x4 vf[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db)
@@ -228,7 +239,7 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     __builtin_amdgcn_sched_barrier(0);
     const bool next = i + 1 < n_tiles;
     const f32x4 sn = partial_scores(kf, qf);
-    if (i + 3 < n_tiles) copy_tile(ks, i + 3, dK, dV, wave, lane16);
+    if (i + 3 < n_tiles) copy_tile(ks, i + 3, dK, dV, w, lane16);
     // Scores of tile i (exp2 domain), masked past its valid keys.
     const TileRef tr = tile_ref(ks, i);
     f32x4 s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
@@ -303,10 +314,6 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   l = xsum32(xsum16(l));
   const float inv = 1.0f / l;
   constexpr float kLog2e = 1.4426950408889634f;
-  const int64_t rowo = (head0 + l16) * kD + 128 * wave + 4 * g4;
-  uint2 gw[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) gw[db] = *reinterpret_cast<const uint2*>(a.g + rowo + 16 * db);
   float r[8][4];
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
