@@ -7,37 +7,39 @@
 // section 43 层里，37 层只读摘要).  The output is gated by sigmoid(G)
 // (blog.derekhsu.net, section 低秩閘控注意力).
 //
-// Decomposition.  One workgroup per (sequence, group of 16 heads); the head
-// groups of a sequence run on the same XCD, so its K/V bytes come from HBM once
-// and from that XCD's L2 for the other groups.  The keys are walked in 16-key
-// tiles: first the entries (the last entry tile masked past the last entry),
-// then the window, so every tile comes from one buffer.  The four waves copy
-// each tile into LDS together by DMA, three tiles ahead of the one whose value
-// product is computed (four LDS stages of K + V).  Wave w owns head dims
-// 128w .. 128w+127:
-//   scores  partial S^T[key][head] over the wave's dims (4 MFMA 16x16x32, K
-//           from LDS, Q of the 16 heads in VGPRs), summed across the waves
-//           through LDS, so each wave holds the full scores of the tile;
-//   values  O^T[dv][head] for the wave's dims (8 MFMA 16x16x16, V^T by one
-//           LDS transpose read each, P^T straight from the score registers).
-// Step i sums the scores of tile i, takes its weights and adds its value
-// product, while computing the partial scores of tile i+1.
+// Decomposition.  One workgroup per sequence, all H = 16 * NHB heads, so each
+// K/V byte is copied from memory into one CU only and every tile feeds the
+// MFMAs of all heads.  The keys are walked in 16-key tiles: first the entries
+// (the last entry tile masked past the last entry), then the window, so every
+// tile comes from one buffer.  The four waves copy each tile into LDS together
+// by DMA: K three and V two tiles ahead of the step that reads them (four LDS
+// stages each).  The two products are split differently across the waves:
+//   scores  wave w < NHB owns heads 16w .. 16w+15: S^T[key][head] over all 512
+//           dims (16 MFMA 16x16x32, K from LDS, Q^T in VGPRs), its softmax,
+//           and the bf16 weights P^T, written to LDS (512 bytes per wave);
+//   values  wave w owns output dims 128w .. 128w+127 for all heads:
+//           O^T[dv][head] += V^T P^T (8 * NHB MFMA 16x16x16, V^T by LDS
+//           transpose reads, P^T of every head block read back from LDS).
+// Step s adds the value product of tile s and computes the scores and weights
+// of tile s+1; one barrier per step publishes the weights.
 //
 // Softmax (as in prefill): scores in the exp2 domain; each head's reference m
-// is the maximum of its first tile, and every key is weighed by 2^(x - m).  If
-// a score rises more than 2^64 above it, the sequence is run again with the
-// exact maximum.  Memory bound: per sequence (nc + window) * 2 KiB of K/V plus
-// 3 * H KiB of q, g and out.
+// is the maximum of its first tile, and every key is weighed by 2^(x - m), so O
+// is never rescaled.  If a score rises more than 2^64 above it, the sequence is
+// run again with the exact maximum.  Memory bound: per sequence (nc + window)
+// * 2 KiB of K/V plus 3 * H KiB of q, g and out.
 #include "hca_common.h"
 #include "hca_kernels.h"
 
 namespace hca {
 namespace {
 
-constexpr int kHeads = 16;  // heads per workgroup
 constexpr int kTile = 16;
 constexpr int kKRow = 1024 + 16;  // LDS bytes between K rows (conflict-free b128 reads)
 constexpr int kVRow = 1024 + 64;  // between V rows (conflict-free transpose reads)
+constexpr int kPBuf = 4 * 512;    // weights of one tile: 4 head blocks x 64 lanes x 8 bytes
+constexpr int kKBytes = kTile * kKRow;
+constexpr int kVBytes = kTile * kVRow;
 constexpr float kHeadroom = 64.0f;
 
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
@@ -53,7 +55,7 @@ struct Args {
   const int64_t* pos;
   void* out;
   int64_t nc_cap;
-  int B, H, n_hg;
+  int B, H, n_hg;  // n_hg workgroups per sequence, 16 * NHB heads each
   float c;  // scale * log2(e)
   int out_f32;
 };
@@ -65,38 +67,41 @@ struct Keys {
   int nc, lo, nw, n_et, n_tiles;
 };
 
-// Tile i: entry or window tile, its first entry / window index, and its
+// Tile j: entry or window tile, its first entry / window index, and its
 // number of valid keys.  Wave-uniform.
 struct TileRef {
   bool ent;
   int first, valid;
 };
-__device__ __forceinline__ TileRef tile_ref(const Keys& ks, int i) {
+__device__ __forceinline__ TileRef tile_ref(const Keys& ks, int j) {
   TileRef r;
-  r.ent = i < ks.n_et;
-  r.first = kTile * (r.ent ? i : i - ks.n_et);
+  r.ent = j < ks.n_et;
+  r.first = kTile * (r.ent ? j : j - ks.n_et);
   const int v = (r.ent ? ks.nc : ks.nw) - r.first;
   r.valid = v < kTile ? v : kTile;
   return r;
 }
 
-// Copy rows 4w .. 4w+3 of tile i into (sK, sV).  Entry rows past the last
-// entry arrive as zeros (buffer range check); window rows wrap round the ring.
-__device__ __forceinline__ void copy_tile(const Keys& ks, int i, uint8_t* sK, uint8_t* sV,
-                                          int wave, int lane16) {
-  asm volatile("" : "+s"(wave), "+s"(i));  // addresses computed here, not kept in registers
-  const TileRef tr = tile_ref(ks, i);
-  const int bytes = (tr.ent ? ks.nc : kWindow) * 1024;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(tr.ent ? ks.ek : ks.wk, bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(tr.ent ? ks.ev : ks.wv, bytes);
-  const int base = tr.ent ? tr.first : ks.lo + tr.first;
-  const int mask = tr.ent ? 0x7FFFFFFF : kWindow - 1;
+// Copy rows 4w .. 4w+3 of tile j of one tensor (entries `ent`, ring `win`)
+// into LDS rows `stride` bytes apart.  Entry rows past the last entry arrive as
+// zeros (buffer range check); window rows past the last valid position repeat
+// it (finite data under a zero weight, whatever the unused ring slots hold).
+// Past the last tile the copies are still issued, through an empty buffer, so
+// every step issues the same number of copies; they read no memory and write
+// zeros into a stage no later step reads.
+__device__ __forceinline__ void copy_rows(const Keys& ks, int j, const uint16_t* ent,
+                                          const uint16_t* win, uint8_t* dst, int stride, int wave,
+                                          int lane16) {
+  asm volatile("" : "+s"(wave), "+s"(j));  // addresses computed here, not kept in registers
+  const TileRef tr = tile_ref(ks, j);
+  const int bytes = j < ks.n_tiles ? (tr.ent ? ks.nc : kWindow) * 1024 : 0;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tr.ent ? ent : win, bytes);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 4 * wave + u;
-    const int row = (base + r) & mask;
-    dma16_buf(rk, lane16 + row * 1024, (lds_void*)(sK + r * kKRow));
-    dma16_buf(rv, lane16 + row * 1024, (lds_void*)(sV + r * kVRow));
+    const int k = tr.first + r;
+    const int row = tr.ent ? k : ((ks.lo + (k < ks.nw ? k : ks.nw - 1)) & (kWindow - 1));
+    dma16_buf(rs, lane16 + row * 1024, (lds_void*)(dst + r * stride));
   }
 }
 
@@ -118,48 +123,64 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(w[0]) + __uint_as_float(w[1]);
 }
 
-// s_waitcnt vmcnt(n) for the copies of n tiles (8 DMA instructions each).
-__device__ __forceinline__ void wait_tiles_pending(int n) {
-  if (n >= 2)
-    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
-  else if (n == 1)
-    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-}
+// s_waitcnt vmcnt(16) / vmcnt(24): at most 4 / 6 groups of 4 copies (one
+// tensor's rows of one tile for this wave) still in flight.
+__device__ __forceinline__ void wait_4_groups() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+__device__ __forceinline__ void wait_6_groups() { __builtin_amdgcn_s_waitcnt(0x4F78); }
 
-// Partial scores of a tile over this wave's dims: lane (head l16, g4) gets
-// keys 4g4 .. 4g4+3.  koff addresses K row l16, dims 128w + 8g4; fragment ss
-// holds dims 128w + 32ss + 8g4 .. +7.
-__device__ __forceinline__ void k_frags(const uint8_t* sK, int koff, bf16x8 (&kf)[4]) {
+// Scores of one tile for a head block: lane (head l16, g4) gets keys 4g4 ..
+// 4g4+3.  koff addresses K row l16, dims 8g4; fragment ss holds dims 32ss +
+// 8g4 .. +7, like the Q fragments.  The K fragments are read in two halves so
+// the first half's MFMAs run while the second half is read.
+__device__ __forceinline__ void k_frags(const uint8_t* sK, int koff, int half, bf16x8 (&kf)[8]) {
 #pragma unroll
-  for (int ss = 0; ss < 4; ++ss) kf[ss] = *reinterpret_cast<const bf16x8*>(sK + koff + 64 * ss);
+  for (int u = 0; u < 8; ++u)
+    kf[u] = *reinterpret_cast<const bf16x8*>(sK + koff + 64 * (8 * half + u));
 }
-__device__ __forceinline__ f32x4 partial_scores(const bf16x8 (&kf)[4], const bf16x8 (&qf)[4]) {
-  f32x4 s0 = {}, s1 = {};
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[0], s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qf[1], s1, 0, 0, 0);
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2], qf[2], s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[3], qf[3], s1, 0, 0, 0);
-  return s0 + s1;
+__device__ __forceinline__ void score_half(const bf16x8 (&kf)[8], const bf16x8 (&qf)[16], int half,
+                                           f32x4& s0, f32x4& s1) {
+#pragma unroll
+  for (int u = 0; u < 8; u += 2) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[8 * half + u], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u + 1], qf[8 * half + u + 1], s1, 0, 0, 0);
+  }
 }
 
+// O^T block += V^T P^T.  Written as asm to keep the accumulator in AGPRs for
+// the whole kernel (the compiler otherwise moves the 32 * NHB accumulator
+// registers between AGPRs and VGPRs at every loop exit).  Hazards: the V^T and
+// P^T operands come from LDS reads (the compiler inserts their lgkmcnt waits);
+// the accumulators are zeroed by v_accvgpr_write long before the first MFMA
+// and read back long after the last one.
+__device__ __forceinline__ void pv_mfma(f32x4& acc, i16x4 v, i16x4 p) {
+  asm("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+}
+
+template <int NHB>
 __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
-  // Four stages of (K, V) tiles and two buffers of partial scores, separate
-  // arrays so the compiler can tell a copy into one from reads of another.
-  __shared__ __attribute__((aligned(256))) uint8_t sK0[kTile * kKRow];
-  __shared__ __attribute__((aligned(256))) uint8_t sK1[kTile * kKRow];
-  __shared__ __attribute__((aligned(256))) uint8_t sK2[kTile * kKRow];
-  __shared__ __attribute__((aligned(256))) uint8_t sK3[kTile * kKRow];
-  __shared__ __attribute__((aligned(256))) uint8_t sV0[kTile * kVRow];
-  __shared__ __attribute__((aligned(256))) uint8_t sV1[kTile * kVRow];
-  __shared__ __attribute__((aligned(256))) uint8_t sV2[kTile * kVRow];
-  __shared__ __attribute__((aligned(256))) uint8_t sV3[kTile * kVRow];
-  __shared__ __attribute__((aligned(1024))) uint8_t sS0[4 * 1024];
-  __shared__ __attribute__((aligned(1024))) uint8_t sS1[4 * 1024];
+  // Four stages of K and of V, two weight buffers and the row sums.  Array sAi
+  // holds K stage i and V stage i-1 (mod 4): step s copies into sA(s%4) only
+  // and reads sA(s+1 % 4) only, so with the arrays separate the compiler can
+  // tell every copy in flight from the reads that follow it.
+  __shared__ __attribute__((aligned(256))) uint8_t sA0[kKBytes + kVBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t sA1[kKBytes + kVBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t sA2[kKBytes + kVBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t sA3[kKBytes + kVBytes];
+  uint8_t* const sK0 = sA0;
+  uint8_t* const sK1 = sA1;
+  uint8_t* const sK2 = sA2;
+  uint8_t* const sK3 = sA3;
+  uint8_t* const sV0 = sA1 + kKBytes;
+  uint8_t* const sV1 = sA2 + kKBytes;
+  uint8_t* const sV2 = sA3 + kKBytes;
+  uint8_t* const sV3 = sA0 + kKBytes;
+  __shared__ __attribute__((aligned(256))) uint8_t sP0[kPBuf];
+  __shared__ __attribute__((aligned(256))) uint8_t sP1[kPBuf];
+  __shared__ float sL[64];
+  __shared__ int sFlag[4];
 
   // blockIdx -> (sequence, head group): XCD x = blockIdx % 8 takes sequences
-  // x, x + 8, ... with all their head groups.
+  // x, x + 8, ... with all their head groups, which share K/V in its L2.
   const int L = blockIdx.x;
   const int k8 = L >> 3;
   const int hg = k8 % a.n_hg;
@@ -167,26 +188,29 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   if (b >= a.B) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+  const bool owner = NHB == 4 || wave < NHB;  // this wave computes the scores of head block `wave`
 
-  // Q and the gate logits do not depend on the position: their loads go out
-  // first, so their latency overlaps the position's and the first copies'.
-  const int64_t head0 = (int64_t)b * a.H + hg * kHeads;
-  // Q fragments (B operand of the partial scores): head l16, dims 128w +
-  // 32ss + 8g4 .. +8.
-  bf16x8 qf[4];
-  {
-    const uint16_t* qrow = a.q + (head0 + l16) * kD + 128 * wave + 8 * g4;
-#pragma unroll
-    for (int ss = 0; ss < 4; ++ss) qf[ss] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ss);
-  }
-  // Gate logits of this lane's output dims (see the epilogue).
+  // The position first: the copies wait for it.  The loads of Q and the gate
+  // logits follow; they overlap the first copies (the copies' waits below
+  // cover them: loads complete in order).
+  const int64_t t_raw = a.pos[b];
+  const int64_t head0 = (int64_t)b * a.H + hg * 16 * NHB;
+  // Q^T fragments (B operand of the scores): head 16w + l16, dims 32ss + 8g4
+  // .. +7; loaded at the start of each pass (a value loaded before the pass
+  // loop and used in it would make the compiler wait for every load first).
+  bf16x8 qf[16];
+  const uint16_t* const qrow = a.q + (head0 + 16 * wave + l16) * kD + 8 * g4;
+  // Gate logits of this lane's outputs: head 16hb + l16, dims 128w + 16db + 4g4 .. +3.
   const int64_t rowo = (head0 + l16) * kD + 128 * wave + 4 * g4;
-  uint2 gw[8];
+  uint2 gw[NHB][8];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) gw[db] = *reinterpret_cast<const uint2*>(a.g + rowo + 16 * db);
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      gw[hb][db] = *reinterpret_cast<const uint2*>(a.g + rowo + (int64_t)16 * hb * kD + 16 * db);
 
   // Positions below 2^31 (negative ones read as 0); wave-uniform.
-  int64_t t64 = a.pos[b];
+  int64_t t64 = t_raw;
   t64 = t64 < 0 ? 0 : (t64 > 0x7FFFFFFF ? 0x7FFFFFFF : t64);
   const int t = __builtin_amdgcn_readfirstlane((int)t64);
   Keys ks;
@@ -200,56 +224,32 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   ks.ev = a.cv + (int64_t)b * a.nc_cap * kD;
   ks.wk = a.wk + (int64_t)b * kWindow * kD;
   ks.wv = a.wv + (int64_t)b * kWindow * kD;
-  const int n_tiles = ks.n_tiles;
+  const int n = ks.n_tiles;  // >= 1: the new token itself is always a key
 
-  // Lane offsets: K fragment source (row l16, dims 128w + 8g4); V^T
-  // transpose read source (key row 4g4 + l16/4, dims 128w + 4(l16&3)); the
-  // lane's 16-byte slot of a partial-score buffer.
-  const int koff = l16 * kKRow + 256 * wave + 16 * g4;
+  // Lane offsets: K fragment source (row l16, dims 8g4); V^T transpose read
+  // source (key row 4g4 + l16/4, dims 128w + 4(l16&3)); the lane's 8-byte
+  // slot of a weight buffer.
+  const int koff = l16 * kKRow + 16 * g4;
   const int voff = (4 * g4 + (l16 >> 2)) * kVRow + 256 * wave + 8 * (l16 & 3);
-  const int lane16 = lane * 16;
+  const int lane8 = lane * 8, lane16 = lane * 16;
 
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // Q and G in (the copies below are counted from here)
 
-  // O^T blocks: o[db] lane (head l16, g4), reg r -> dim 128w + 16db + 4g4 + r
-  f32x4 o[8];
+  // O^T blocks: o[hb][db] lane (head 16hb + l16, g4), reg r -> dim 128w + 16db + 4g4 + r
+  f32x4 o[NHB][8];
   float m = -INFINITY, mseen = -INFINITY, l = 0.0f;
   bool over = false, fixed_m = false;
 
-  // Step i: tile i's partial scores are in sS (all waves'), its V in sV;
-  // tile i+1's K in sKn.  Writes tile i+1's partial scores into sSn and
-  // copies tile i+3 into (dK, dV), the stage of tile i-1.
-  auto step = [&](int i, const uint8_t* sV, const uint8_t* sKn, const uint8_t* sS,
-                  uint8_t* sSn, uint8_t* dK, uint8_t* dV) {
-    int w = wave;
-    asm volatile("" : "+s"(w), "+s"(i));  // per-step values computed here, not kept in registers
-    // All LDS reads first (a read after a copy would wait for it), the K
-    // fragments of the next tile's scores ahead of the rest so its MFMAs can
-    // start while the others are in flight.  Past the last tile, K and
-    // scores are of a stale stage and unused.
-    bf16x8 kf[4];
-    k_frags(sKn, koff, kf);
-    f32x4 sp[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sp[u] = *reinterpret_cast<const f32x4*>(sS + u * 1024 + lane16);
-    i16x4 vf[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      vf[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + voff + 32 * db));
-    __builtin_amdgcn_sched_barrier(0);
-    const bool next = i + 1 < n_tiles;
-    const f32x4 sn = partial_scores(kf, qf);
-    if (i + 3 < n_tiles) copy_tile(ks, i + 3, dK, dV, w, lane16);
-    // Scores of tile i (exp2 domain), masked past its valid keys.
-    const TileRef tr = tile_ref(ks, i);
-    f32x4 s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+  // Weights of tile j from its scores (owner waves): mask, reference, exp2,
+  // bf16, row sum; P^T fragment stored at this wave's slot of sPn.
+  auto weights = [&](int j, f32x4 s, uint8_t* sPn) {
+    const TileRef tr = tile_ref(ks, j);
     float mt = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       s[r] = 4 * g4 + r < tr.valid ? s[r] * a.c : -INFINITY;
       mt = fmaxf(mt, s[r]);
     }
-    if (i == 0 && !fixed_m) m = xmax32(xmax16(mt));  // the reference: max of the first tile
+    if (j == 0 && !fixed_m) m = xmax32(xmax16(mt));  // the reference: max of the first tile
     mseen = fmaxf(mseen, mt);
     over |= mt > m + kHeadroom;
     const f32x4 e = {__builtin_amdgcn_exp2f(s[0] - m), __builtin_amdgcn_exp2f(s[1] - m),
@@ -259,82 +259,143 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     l = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pb[0], pb[1]}, ones, l, false);
     l = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pb[2], pb[3]}, ones, l, false);
-    // P^T (B operand): lane (head l16, g4) holds keys 4g4 .. 4g4+3, the same
-    // keys as the V^T fragments' k-slots.
-    const i16x4 pf = __builtin_bit_cast(i16x4, pb);
+    *reinterpret_cast<i16x4*>(sPn + wave * 512 + lane8) = __builtin_bit_cast(i16x4, pb);
+  };
+
+  // Step s: V(s) in sVc, its weights in sPc; K(s+1) in sKn.  Adds the value
+  // product of tile s, writes the weights of tile s+1 into sPn, and copies
+  // K(s+4) into dK (the stage of K(s)) and V(s+3) into dV (that of V(s-1)).
+  auto step = [&](int s, const uint8_t* sKn, const uint8_t* sVc, const uint8_t* sPc, uint8_t* sPn,
+                  uint8_t* dK, uint8_t* dV) {
+    int w = wave;
+    asm volatile("" : "+s"(w), "+s"(s));  // per-step values computed here, not kept in registers
+    // LDS reads first (a read issued after a copy would wait for it), the K
+    // fragments ahead of the rest so the score MFMAs can start early.
+    bf16x8 kf[8];
+    if (owner) k_frags(sKn, koff, 0, kf);
+    i16x4 pf[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) pf[hb] = *reinterpret_cast<const i16x4*>(sPc + hb * 512 + lane8);
+    i16x4 vf[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[db], pf, o[db], 0, 0, 0);
-    if (next) *reinterpret_cast<f32x4*>(sSn + wave * 1024 + lane16) = sn;
-    // This wave's copies of tile i+2 and its partial scores of tile i+1 are
-    // done (only the copies of tile i+3 may be in flight), then every wave's.
-    wait_tiles_pending(i + 3 < n_tiles ? 1 : 0);
+      vf[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sVc + voff + 32 * db));
+    __builtin_amdgcn_sched_barrier(0);
+    copy_rows(ks, s + 4, ks.ek, ks.wk, dK, kKRow, w, lane16);
+    copy_rows(ks, s + 3, ks.ev, ks.wv, dV, kVRow, w, lane16);
+    f32x4 s0 = {}, s1 = {};
+    if (owner) {  // past the last tile: scores of a stale stage, unused
+      score_half(kf, qf, 0, s0, s1);
+      k_frags(sKn, koff, 1, kf);
+      score_half(kf, qf, 1, s0, s1);
+    }
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        pv_mfma(o[hb][db], vf[db], pf[hb]);
+    if (owner && s + 1 < n) weights(s + 1, s0 + s1, sPn);
+    // K(s+2) and V(s+1) are in for this wave (the copies issued after them,
+    // K(s+3), V(s+2), K(s+4), V(s+3), may be in flight), the weights written;
+    // then for every wave.
+    wait_4_groups();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     barrier_no_fence();
   };
 
   for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] = f32x4{};
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[hb][db] = f32x4{};
     l = 0.0f;
     over = false;
-    // Prologue: tiles 0, 1, 2 copied; partial scores of tile 0.
-    copy_tile(ks, 0, sK0, sV0, wave, lane16);
-    if (n_tiles > 1) copy_tile(ks, 1, sK1, sV1, wave, lane16);
-    if (n_tiles > 2) copy_tile(ks, 2, sK2, sV2, wave, lane16);
-    wait_tiles_pending(n_tiles - 1 < 2 ? n_tiles - 1 : 2);  // tile 0 in
-    barrier_no_fence();
-    {
-      bf16x8 kf[4];
-      k_frags(sK0, koff, kf);
-      const f32x4 s0 = partial_scores(kf, qf);
-      *reinterpret_cast<f32x4*>(sS0 + wave * 1024 + lane16) = s0;
+    if (owner) {
+#pragma unroll
+      for (int ss = 0; ss < 16; ++ss) qf[ss] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ss);
     }
-    wait_tiles_pending(n_tiles > 2 ? 1 : 0);  // tile 1 in
+    // Prologue: K(0); K(1), V(0); K(2), V(1); K(3), V(2) copied, in that order;
+    // weights of tile 0.
+    copy_rows(ks, 0, ks.ek, ks.wk, sK0, kKRow, wave, lane16);
+    copy_rows(ks, 1, ks.ek, ks.wk, sK1, kKRow, wave, lane16);
+    copy_rows(ks, 0, ks.ev, ks.wv, sV0, kVRow, wave, lane16);
+    copy_rows(ks, 2, ks.ek, ks.wk, sK2, kKRow, wave, lane16);
+    copy_rows(ks, 1, ks.ev, ks.wv, sV1, kVRow, wave, lane16);
+    copy_rows(ks, 3, ks.ek, ks.wk, sK3, kKRow, wave, lane16);
+    copy_rows(ks, 2, ks.ev, ks.wv, sV2, kVRow, wave, lane16);
+    wait_6_groups();  // K(0) in
+    barrier_no_fence();
+    if (owner) {
+      f32x4 s0 = {}, s1 = {};
+      bf16x8 kf[8];
+      k_frags(sK0, koff, 0, kf);
+      score_half(kf, qf, 0, s0, s1);
+      k_frags(sK0, koff, 1, kf);
+      score_half(kf, qf, 1, s0, s1);
+      weights(0, s0 + s1, sP0);
+    }
+    wait_4_groups();  // K(1), V(0) in
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier_no_fence();
-    for (int i = 0; i < n_tiles; i += 4) {
-      step(i, sV0, sK1, sS0, sS1, sK3, sV3);
-      if (i + 1 >= n_tiles) break;
-      step(i + 1, sV1, sK2, sS1, sS0, sK0, sV0);
-      if (i + 2 >= n_tiles) break;
-      step(i + 2, sV2, sK3, sS0, sS1, sK1, sV1);
-      if (i + 3 >= n_tiles) break;
-      step(i + 3, sV3, sK0, sS1, sS0, sK2, sV2);
+    // Whole groups of four steps, then the rest (nested, so the compiler
+    // sees the same copies in flight on every path into a step).
+    int s = 0;
+    for (; s + 4 <= n; s += 4) {
+      step(s, sK1, sV0, sP0, sP1, sK0, sV3);
+      step(s + 1, sK2, sV1, sP1, sP0, sK1, sV0);
+      step(s + 2, sK3, sV2, sP0, sP1, sK2, sV1);
+      step(s + 3, sK0, sV3, sP1, sP0, sK3, sV2);
     }
+    if (s < n) {
+      step(s, sK1, sV0, sP0, sP1, sK0, sV3);
+      if (s + 1 < n) {
+        step(s + 1, sK2, sV1, sP1, sP0, sK1, sV0);
+        if (s + 2 < n) step(s + 2, sK3, sV2, sP0, sP1, sK2, sV1);
+      }
+    }
+    // Row sums and the repeat decision of every head block, through LDS.
+    if (owner) {
+      const float lh = xsum32(xsum16(l));
+      if (lane < 16) sL[16 * wave + lane] = lh;
+      const bool wover = __builtin_amdgcn_ballot_w64(over) != 0;
+      if (lane == 0) sFlag[wave] = wover ? 1 : 0;
+    } else if (lane == 0) {
+      sFlag[wave] = 0;
+    }
+    __syncthreads();
+    const bool redo = (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0;
     // A score more than 2^kHeadroom above its reference (extreme score ranges
     // only): run again with the exact maximum of each head as reference.
-    const bool redo = __builtin_amdgcn_ballot_w64(over) != 0;
     if (pass == 1 || !redo) break;
     m = xmax32(xmax16(mseen));
     fixed_m = true;
+    __syncthreads();  // every wave has read the flags before they are rewritten
   }
 
-  // out = O / l * sigmoid(G) for this wave's 128 dims.
-  l = xsum32(xsum16(l));
-  const float inv = 1.0f / l;
+  // out = O / l * sigmoid(G) for this wave's 128 dims of every head.
   constexpr float kLog2e = 1.4426950408889634f;
-  float r[8][4];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    const float gv[4] = {bf16_bits_to_f32(gw[db].x & 0xFFFFu), bf16_bits_to_f32(gw[db].x >> 16),
-                         bf16_bits_to_f32(gw[db].y & 0xFFFFu), bf16_bits_to_f32(gw[db].y >> 16)};
+  for (int hb = 0; hb < NHB; ++hb) {
+    const float inv = 1.0f / sL[16 * hb + l16];
+    const int64_t rowh = rowo + (int64_t)16 * hb * kD;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[e] * kLog2e));
-      r[db][e] = o[db][e] * inv * sig;
+    for (int db = 0; db < 8; ++db) {
+      const uint2 gv2 = gw[hb][db];
+      const float gv[4] = {bf16_bits_to_f32(gv2.x & 0xFFFFu), bf16_bits_to_f32(gv2.x >> 16),
+                           bf16_bits_to_f32(gv2.y & 0xFFFFu), bf16_bits_to_f32(gv2.y >> 16)};
+      float r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[e] * kLog2e));
+        r[e] = o[hb][db][e] * inv * sig;
+      }
+      if (a.out_f32)
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + rowh + 16 * db) =
+            make_float4(r[0], r[1], r[2], r[3]);
+      else
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + rowh + 16 * db) =
+            make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
     }
-  }
-  if (a.out_f32) {
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + rowo + 16 * db) =
-          make_float4(r[db][0], r[db][1], r[db][2], r[db][3]);
-  } else {
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + rowo + 16 * db) =
-          make_uint2(pack_bf16x2(r[db][0], r[db][1]), pack_bf16x2(r[db][2], r[db][3]));
   }
 }
 
@@ -354,11 +415,20 @@ hipError_t launch_decode(const DecodeProblem& p, hipStream_t stream) {
   a.nc_cap = p.nc_cap;
   a.B = p.B;
   a.H = p.H;
-  a.n_hg = p.H / kHeads;
   a.c = p.scale * 1.4426950408889634f;
   a.out_f32 = p.out_f32 ? 1 : 0;
-  const unsigned blocks = (unsigned)(((p.B + 7) / 8) * 8 * a.n_hg);
-  hipLaunchKernelGGL(decode_kernel, dim3(blocks), dim3(256), 0, stream, a);
+  // Heads per workgroup: all of them when the batch fills the chip, else
+  // fewer, so that more workgroups share the per-head loads, gate and stores.
+  int nhb = p.H / 16;
+  while (nhb > 1 && ((int64_t)p.B * (p.H / 16 / nhb) < 256 || (p.H / 16) % nhb != 0)) --nhb;
+  a.n_hg = p.H / 16 / nhb;
+  const dim3 grid((unsigned)(((p.B + 7) / 8) * 8 * a.n_hg)), block(256);
+  switch (nhb) {
+    case 1: hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

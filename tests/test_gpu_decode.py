@@ -87,6 +87,21 @@ def test_decode_matches_prefill_row():
     compare(host_f64(got), d.oracle(), "decode rows")
 
 
+def test_unused_ring_slots_and_cache_rows_are_never_read():
+    # ring slots past the new token (t < 127) and cache rows past the visible
+    # entries may hold anything, NaN included
+    positions = [0, 5, 100, 126, 127, 300, 1100]
+    d = Decode(seed=16, positions=positions, H=64, nc_cap=12, out_dtype="f32")
+    for b, t in enumerate(positions):
+        if t < 127:
+            d.wk[b, t + 1:], d.wv[b, t + 1:] = float("nan"), float("nan")
+        n = (t + 1) // 128
+        d.ck[b, n:], d.cv[b, n:] = float("nan"), float("nan")
+    got = host_f64(d.run())
+    assert np.isfinite(got).all()
+    compare(got, d.oracle(), "NaN in unused rows")
+
+
 def test_batch_zero_is_noop():
     d = Decode(seed=15, positions=[5], H=16)
     hca.hca_attn_decode(d.q[:0], d.g[:0], d.ck[:0], d.cv[:0], d.wk[:0], d.wv[:0], d.pos[:0],
