@@ -445,27 +445,32 @@ __device__ __forceinline__ void sm_write(const SoftmaxTile& x, uint8_t* sP, int 
 }
 
 // The softmax parts of pipeline group k: part A goes between the group's
-// score MFMA and its value MFMA, part B after the value MFMA.  Dependent
-// instructions sit in different parts, an MFMA apart.
-//   group  part A                 part B
-//   0..7   -                      max k
-//   8..10  reduce 0, 2, 4         reduce 1, 3, 5
-//   11     reduce 6               -
-//   12..21 fma k-12, sum k-14     exp k-12, cvt k-13   (pairs j = 0..7 only)
-//   21, 22 write 0, 1             -
+// score MFMA and its value MFMA, parts B and C after the value MFMA.
+// Dependent instructions sit in different parts, an MFMA apart, and the
+// exponentials are spread one pair per two groups.
+//   group          part A              part B           part C
+//   0..7           -                   max k            -
+//   8..10          reduce 0, 2, 4      reduce 1, 3, 5   -
+//   11             reduce 6            -                -
+//   12, 14 .. 26   fma (k-12)/2        exp (k-12)/2     -
+//   13, 15 .. 27   cvt (k-13)/2        -                sum (k-13)/2
+//   21, 29         write 0, 1          -                -
 __device__ __forceinline__ void sm_part_a(const Args& a, WaveState& st, SoftmaxTile& x,
                                           uint8_t* sP, int k, int lane, int wave) {
   if (k >= 8 && k < 11) sm_reduce(a, st, x, 2 * (k - 8));
   if (k == 11) sm_reduce(a, st, x, 6);
-  if (k >= 12 && k < 20) sm_fma(a, x, k - 12);
-  if (k >= 14 && k < 22) sm_sum(st, x, k - 14);
-  if (k == 21 || k == 22) sm_write(x, sP, k - 21, lane, wave);
+  if (k >= 12 && k < 28 && (k & 1) == 0) sm_fma(a, x, (k - 12) >> 1);
+  if (k >= 13 && k < 29 && (k & 1) == 1) sm_cvt(x, (k - 13) >> 1);
+  if (k == 21) sm_write(x, sP, 0, lane, wave);
+  if (k == 29) sm_write(x, sP, 1, lane, wave);
 }
 __device__ __forceinline__ void sm_part_b(const Args& a, WaveState& st, SoftmaxTile& x, int k) {
   if (k < 8) sm_max(x, k);
   if (k >= 8 && k < 11) sm_reduce(a, st, x, 2 * (k - 8) + 1);
-  if (k >= 12 && k < 20) sm_exp(x, k - 12);
-  if (k >= 13 && k < 21) sm_cvt(x, k - 13);
+  if (k >= 12 && k < 28 && (k & 1) == 0) sm_exp(x, (k - 12) >> 1);
+}
+__device__ __forceinline__ void sm_part_c(WaveState& st, const SoftmaxTile& x, int k) {
+  if (k >= 13 && k < 29 && (k & 1) == 1) sm_sum(st, x, (k - 13) >> 1);
 }
 
 // V^T fragments of PV block n = 4 c2 + bb (keys 16c2.., dims 128w + 32bb..)
@@ -592,6 +597,7 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
     if (kKind == kTailB && k >= 8 && k < 16) dma_rows(qs, k - 8, 512, sKd + greg, lane);
     if (kKind == kTailB && k >= 16 && k < 24) dma_rows(qs, k - 16, 768, const_cast<uint8_t*>(sK) + greg, lane);
     if (kSoftmax) sm_part_b(a, st, x, k);
+    if (kSoftmax) sm_part_c(st, x, k);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (kScores) carry = s;
@@ -784,9 +790,10 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
         SoftmaxTile x;
         sm_init(x, s0);
 #pragma unroll
-        for (int k = 0; k < 23; ++k) {
+        for (int k = 0; k < 30; ++k) {
           sm_part_a(a, st, x, sPs, k, ln, wave);
           sm_part_b(a, st, x, k);
+          sm_part_c(st, x, k);
         }
         wait_vmem();
         __syncthreads();
