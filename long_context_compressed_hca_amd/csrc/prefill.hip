@@ -92,9 +92,15 @@ struct Args {
   int n_items;
   int per_xcd;                // workgroups per XCD (grid = 8 * per_xcd)
   int H;
+  int h_shift;                // log2(H) when H is a power of two, else -1
   float c;  // scale * log2(e)
   int out_f32;
 };
+
+// Row -> query index (row / H), a shift when H is a power of two.
+__device__ __forceinline__ int row_query(const Args& a, int row) {
+  return a.h_shift >= 0 ? row >> a.h_shift : row / a.H;
+}
 
 __device__ __forceinline__ int n_entries(int t, int Nc) {
   const int n = (t + 1) / kBlock;
@@ -123,12 +129,12 @@ __device__ __forceinline__ Item make_item(const Args& a, int idx, int wave, int 
   it.last = (it.row0 + kRowsPerItem < a.rows ? it.row0 + kRowsPerItem : a.rows) - 1;
   const int r = it.row0 + wave * 32 + l32;
   it.my_row = r < it.last ? r : it.last;
-  it.t = a.q_start + it.my_row / a.H;
+  it.t = a.q_start + row_query(a, it.my_row);
   const int wr0 = it.row0 + wave * 32, wr1 = wr0 + 31;
-  it.tw_min = a.q_start + (wr0 < it.last ? wr0 : it.last) / a.H;
-  it.tw_max = a.q_start + (wr1 < it.last ? wr1 : it.last) / a.H;
-  const int t_min = a.q_start + it.row0 / a.H;
-  it.t_max = a.q_start + it.last / a.H;
+  it.tw_min = a.q_start + row_query(a, wr0 < it.last ? wr0 : it.last);
+  it.tw_max = a.q_start + row_query(a, wr1 < it.last ? wr1 : it.last);
+  const int t_min = a.q_start + row_query(a, it.row0);
+  it.t_max = a.q_start + row_query(a, it.last);
   it.nc_wg = n_entries(it.t_max, a.Nc);
   it.w_lo = t_min - (kWindow - 1) > 0 ? t_min - (kWindow - 1) : 0;
   it.wlen = it.t_max - it.w_lo + 1;
@@ -313,10 +319,11 @@ __device__ __forceinline__ bf16x8 k_frag(const uint8_t* krow, int ss) {
 }
 
 // S^T (32 keys x the wave's 32 rows) = K . Q^T for the K tile in sK, with K
-// fragments read kAhead MFMAs ahead.  The order of MFMAs and reads is fixed
-// with scheduling barriers.
-template <int kAhead>
-__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&qf)[32], const uint8_t* sK, int koff) {
+// fragments read kAhead MFMAs ahead; after_mfma(ss) places other work after
+// MFMA ss.  The order of MFMAs and reads is fixed with scheduling barriers.
+template <int kAhead, typename F>
+__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&qf)[32], const uint8_t* sK, int koff,
+                                           F&& after_mfma) {
   const uint8_t* krow = sK + koff;
   bf16x8 kf[kAhead];
 #pragma unroll
@@ -332,6 +339,7 @@ __device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&qf)[32], const uint8_t
     else
       mfma_s_acc(s, kf[ss % kAhead], qf[ss]);
     if (ss + kAhead < 32) kf[ss % kAhead] = k_frag(krow, ss + kAhead);
+    after_mfma(ss);
     __builtin_amdgcn_sched_barrier(0);
   }
   return s;
@@ -748,8 +756,6 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
                    (kD * 2))
              : 0);
     for (int pass = 0;; ++pass) {
-#pragma unroll
-      for (int b = 0; b < 16; ++b) st.o[b] = f32x16{};
       st.l = 0.0f;
       st.over = false;
       // Steps: N = max(n_tiles, 2) of them (an item with a single tile runs a
@@ -773,8 +779,16 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
         // This wave's copies of K(0), K(1) and its Q done, then everyone's.
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
         barrier_no_fence();
-        f32x16 s0 = qk_chain<4>(qf, sK0, (ln & 31) * kKRow + 16 * (ln >> 5));
-        carry = qk_chain<4>(qf, sK1, (ln & 31) * kKRow + 16 * (ln >> 5));
+        // The O accumulators are zeroed between the score MFMAs of tiles 0
+        // and 1 (four registers after each), where the VALU is idle.
+        auto zero4 = [&](int k) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.o[k >> 2][4 * (k & 3) + e] = 0.0f;
+        };
+        f32x16 s0 = qk_chain<4>(qf, sK0, (ln & 31) * kKRow + 16 * (ln >> 5),
+                                [&](int ss) { zero4(ss); });
+        carry = qk_chain<4>(qf, sK1, (ln & 31) * kKRow + 16 * (ln >> 5),
+                            [&](int ss) { zero4(32 + ss); });
         barrier_no_fence();  // every wave's reads of K(0) are done
         const TileSrc k2 = tile_src(a, it, 2, false), v0 = tile_src(a, it, 0, true);
         uint8_t* const sK2 = odd ? sK1 : sK0;
@@ -896,6 +910,7 @@ hipError_t launch_prefill(const PrefillProblem& p, hipStream_t stream) {
   a.kv_start = (int)p.kv_start;
   a.Nc = (int)p.Nc;
   a.H = p.H;
+  a.h_shift = (p.H & (p.H - 1)) == 0 ? __builtin_ctz((unsigned)p.H) : -1;
   a.c = p.scale * 1.4426950408889634f;
   a.out_f32 = p.out_f32 ? 1 : 0;
   a.n_items = (a.rows + kRowsPerItem - 1) / kRowsPerItem;
