@@ -7,21 +7,23 @@
 // section 43 层里，37 层只读摘要).  The output is gated by sigmoid(G)
 // (blog.derekhsu.net, section 低秩閘控注意力).
 //
-// Decomposition.  One workgroup per sequence, all H = 16 * NHB heads, so each
-// K/V byte is copied from memory into one CU only and every tile feeds the
-// MFMAs of all heads.  The keys are walked in 16-key tiles: first the entries
-// (the last entry tile masked past the last entry), then the window, so every
-// tile comes from one buffer.  The four waves copy each tile into LDS together
-// by DMA: K three and V two tiles ahead of the step that reads them (four LDS
-// stages each).  The two products are split differently across the waves:
-//   scores  wave w < NHB owns heads 16w .. 16w+15: S^T[key][head] over all 512
-//           dims (16 MFMA 16x16x32, K from LDS, Q^T in VGPRs), its softmax,
-//           and the bf16 weights P^T, written to LDS (512 bytes per wave);
-//   values  wave w owns output dims 128w .. 128w+127 for all heads:
-//           O^T[dv][head] += V^T P^T (8 * NHB MFMA 16x16x16, V^T by LDS
-//           transpose reads, P^T of every head block read back from LDS).
-// Step s adds the value product of tile s and computes the scores and weights
-// of tile s+1; one barrier per step publishes the weights.
+// Decomposition.  One workgroup per (sequence, 16 * NHB of its heads), NHB = 1
+// or 2, chosen so that the batch fills the chip; the head groups of a sequence
+// run on one XCD and share its K/V bytes in that XCD's L2.  The keys are walked
+// in 16-key tiles: first the entries (the last entry tile masked past the last
+// entry), then the window, so every tile comes from one buffer.  The four
+// waves copy each tile into LDS together by DMA (four stages of K and of V).
+// Each step runs three tiles at once:
+//   scores  tile s+2: wave w computes the partial scores S^T[key][head] over
+//           its dims 128w .. 128w+127 for every head (4 MFMA 16x16x32 per
+//           16 heads, K from LDS, Q^T in VGPRs) and writes them to LDS;
+//   softmax tile s+1: wave hb < NHB sums the four partial score tiles of head
+//           block hb, masks, weighs, rounds to bf16 and writes P^T to LDS;
+//   values  tile s: wave w adds O^T[dv][head] += V^T P^T for its 128 dims of
+//           every head (8 MFMA 16x16x16 per 16 heads, V^T by LDS transpose
+//           reads, P^T of every head block from LDS).
+// The three parts of a step are independent, so their latencies overlap; one
+// barrier per step publishes the partial scores and the weights.
 //
 // Softmax (as in prefill): scores in the exp2 domain; each head's reference m
 // is the maximum of its first tile, and every key is weighed by 2^(x - m), so O
@@ -37,7 +39,6 @@ namespace {
 constexpr int kTile = 16;
 constexpr int kKRow = 1024 + 16;  // LDS bytes between K rows (conflict-free b128 reads)
 constexpr int kVRow = 1024 + 64;  // between V rows (conflict-free transpose reads)
-constexpr int kPBuf = 4 * 512;    // weights of one tile: 4 head blocks x 64 lanes x 8 bytes
 constexpr int kKBytes = kTile * kKRow;
 constexpr int kVBytes = kTile * kVRow;
 constexpr float kHeadroom = 64.0f;
@@ -123,60 +124,56 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(w[0]) + __uint_as_float(w[1]);
 }
 
-// s_waitcnt vmcnt(16) / vmcnt(24): at most 4 / 6 groups of 4 copies (one
-// tensor's rows of one tile for this wave) still in flight.
+// s_waitcnt vmcnt(4n): at most n groups of 4 copies (one tensor's rows of one
+// tile for this wave) still in flight.
 __device__ __forceinline__ void wait_4_groups() { __builtin_amdgcn_s_waitcnt(0x4F70); }
-__device__ __forceinline__ void wait_6_groups() { __builtin_amdgcn_s_waitcnt(0x4F78); }
+__device__ __forceinline__ void wait_5_groups() { __builtin_amdgcn_s_waitcnt(0x4F74); }
 
-// Scores of one tile for a head block: lane (head l16, g4) gets keys 4g4 ..
-// 4g4+3.  koff addresses K row l16, dims 8g4; fragment ss holds dims 32ss +
-// 8g4 .. +7, like the Q fragments.  The K fragments are read in two halves so
-// the first half's MFMAs run while the second half is read.
-__device__ __forceinline__ void k_frags(const uint8_t* sK, int koff, int half, bf16x8 (&kf)[8]) {
+// Partial scores of one tile over this wave's dims for one head block: lane
+// (head l16, g4) gets keys 4g4 .. 4g4+3.  koff addresses K row l16, dims
+// 128w + 8g4; fragment ss holds dims 128w + 32ss + 8g4 .. +7, like the Q
+// fragments.
+__device__ __forceinline__ void k_frags(const uint8_t* sK, int koff, bf16x8 (&kf)[4]) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    kf[u] = *reinterpret_cast<const bf16x8*>(sK + koff + 64 * (8 * half + u));
+  for (int ss = 0; ss < 4; ++ss) kf[ss] = *reinterpret_cast<const bf16x8*>(sK + koff + 64 * ss);
 }
-__device__ __forceinline__ void score_half(const bf16x8 (&kf)[8], const bf16x8 (&qf)[16], int half,
-                                           f32x4& s0, f32x4& s1) {
-#pragma unroll
-  for (int u = 0; u < 8; u += 2) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[8 * half + u], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u + 1], qf[8 * half + u + 1], s1, 0, 0, 0);
-  }
+__device__ __forceinline__ f32x4 partial_scores(const bf16x8 (&kf)[4], const bf16x8 (&qf)[4]) {
+  f32x4 s0 = {}, s1 = {};
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[0], s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qf[1], s1, 0, 0, 0);
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2], qf[2], s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[3], qf[3], s1, 0, 0, 0);
+  return s0 + s1;
 }
 
 // O^T block += V^T P^T.  Written as asm to keep the accumulator in AGPRs for
-// the whole kernel (the compiler otherwise moves the 32 * NHB accumulator
-// registers between AGPRs and VGPRs at every loop exit).  Hazards: the V^T and
-// P^T operands come from LDS reads (the compiler inserts their lgkmcnt waits);
-// the accumulators are zeroed by v_accvgpr_write long before the first MFMA
-// and read back long after the last one.
+// the whole kernel (the compiler otherwise moves the accumulator registers
+// between AGPRs and VGPRs at loop exits).  Hazards: the V^T and P^T operands
+// come from LDS reads (the compiler inserts their lgkmcnt waits); the
+// accumulators are zeroed by v_accvgpr_write long before the first MFMA and
+// read back long after the last one.
 __device__ __forceinline__ void pv_mfma(f32x4& acc, i16x4 v, i16x4 p) {
   asm("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
 
 template <int NHB>
 __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
-  // Four stages of K and of V, two weight buffers and the row sums.  Array sAi
-  // holds K stage i and V stage i-1 (mod 4): step s copies into sA(s%4) only
-  // and reads sA(s+1 % 4) only, so with the arrays separate the compiler can
-  // tell every copy in flight from the reads that follow it.
+  // Array sAi holds K stage i and V stage i+2 (mod 4): K(j) is in sA(j%4) and
+  // V(j) in sA((j+2)%4).  Step s copies K(s+5) and V(s+3), both into
+  // sA((s+1)%4), and reads K(s+2) and V(s), both in sA((s+2)%4); with the
+  // arrays separate the compiler can tell every copy in flight from the reads
+  // that follow.  Two buffers each of weights (P^T of every head block) and
+  // of partial scores (every wave's, for every head block), the row sums and
+  // the repeat flags.
   __shared__ __attribute__((aligned(256))) uint8_t sA0[kKBytes + kVBytes];
   __shared__ __attribute__((aligned(256))) uint8_t sA1[kKBytes + kVBytes];
   __shared__ __attribute__((aligned(256))) uint8_t sA2[kKBytes + kVBytes];
   __shared__ __attribute__((aligned(256))) uint8_t sA3[kKBytes + kVBytes];
-  uint8_t* const sK0 = sA0;
-  uint8_t* const sK1 = sA1;
-  uint8_t* const sK2 = sA2;
-  uint8_t* const sK3 = sA3;
-  uint8_t* const sV0 = sA1 + kKBytes;
-  uint8_t* const sV1 = sA2 + kKBytes;
-  uint8_t* const sV2 = sA3 + kKBytes;
-  uint8_t* const sV3 = sA0 + kKBytes;
-  __shared__ __attribute__((aligned(256))) uint8_t sP0[kPBuf];
-  __shared__ __attribute__((aligned(256))) uint8_t sP1[kPBuf];
-  __shared__ float sL[64];
+  __shared__ __attribute__((aligned(256))) uint8_t sP0[NHB * 512];
+  __shared__ __attribute__((aligned(256))) uint8_t sP1[NHB * 512];
+  __shared__ __attribute__((aligned(256))) uint8_t sQ0[4 * NHB * 1024];
+  __shared__ __attribute__((aligned(256))) uint8_t sQ1[4 * NHB * 1024];
+  __shared__ float sL[16 * NHB];
   __shared__ int sFlag[4];
 
   // blockIdx -> (sequence, head group): XCD x = blockIdx % 8 takes sequences
@@ -188,18 +185,13 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   if (b >= a.B) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-  const bool owner = NHB == 4 || wave < NHB;  // this wave computes the scores of head block `wave`
+  const bool owner = wave < NHB;  // this wave takes the softmax of head block `wave`
 
-  // The position first: the copies wait for it.  The loads of Q and the gate
+  // The position first: the copies wait for it.  The loads of the gate
   // logits follow; they overlap the first copies (the copies' waits below
   // cover them: loads complete in order).
   const int64_t t_raw = a.pos[b];
   const int64_t head0 = (int64_t)b * a.H + hg * 16 * NHB;
-  // Q^T fragments (B operand of the scores): head 16w + l16, dims 32ss + 8g4
-  // .. +7; loaded at the start of each pass (a value loaded before the pass
-  // loop and used in it would make the compiler wait for every load first).
-  bf16x8 qf[16];
-  const uint16_t* const qrow = a.q + (head0 + 16 * wave + l16) * kD + 8 * g4;
   // Gate logits of this lane's outputs: head 16hb + l16, dims 128w + 16db + 4g4 .. +3.
   const int64_t rowo = (head0 + l16) * kD + 128 * wave + 4 * g4;
   uint2 gw[NHB][8];
@@ -208,6 +200,12 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
 #pragma unroll
     for (int db = 0; db < 8; ++db)
       gw[hb][db] = *reinterpret_cast<const uint2*>(a.g + rowo + (int64_t)16 * hb * kD + 16 * db);
+  // Q^T fragments (B operand of the partial scores): head 16hb + l16, dims
+  // 128w + 32ss + 8g4 .. +7; loaded at the start of each pass (a value loaded
+  // before the pass loop and used in it would make the compiler wait for every
+  // load first).
+  bf16x8 qf[NHB][4];
+  const uint16_t* const qrow = a.q + (head0 + l16) * kD + 128 * wave + 8 * g4;
 
   // Positions below 2^31 (negative ones read as 0); wave-uniform.
   int64_t t64 = t_raw;
@@ -226,27 +224,45 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   ks.wv = a.wv + (int64_t)b * kWindow * kD;
   const int n = ks.n_tiles;  // >= 1: the new token itself is always a key
 
-  // Lane offsets: K fragment source (row l16, dims 8g4); V^T transpose read
-  // source (key row 4g4 + l16/4, dims 128w + 4(l16&3)); the lane's 8-byte
-  // slot of a weight buffer.
-  const int koff = l16 * kKRow + 16 * g4;
+  // Lane offsets: K fragment source (row l16, dims 128w + 8g4); V^T transpose
+  // read source (key row 4g4 + l16/4, dims 128w + 4(l16&3)); the lane's slot
+  // of a weight buffer (8 bytes) and of a partial-score buffer (16 bytes).
+  const int koff = l16 * kKRow + 256 * wave + 16 * g4;
   const int voff = (4 * g4 + (l16 >> 2)) * kVRow + 256 * wave + 8 * (l16 & 3);
   const int lane8 = lane * 8, lane16 = lane * 16;
-
 
   // O^T blocks: o[hb][db] lane (head 16hb + l16, g4), reg r -> dim 128w + 16db + 4g4 + r
   f32x4 o[NHB][8];
   float m = -INFINITY, mseen = -INFINITY, l = 0.0f;
   bool over = false, fixed_m = false;
 
-  // Weights of tile j from its scores (owner waves): mask, reference, exp2,
-  // bf16, row sum; P^T fragment stored at this wave's slot of sPn.
-  auto weights = [&](int j, f32x4 s, uint8_t* sPn) {
+  // This wave's partial scores of the tile whose K is in sK, for every head
+  // block, into its slots of sQn.
+  auto scores = [&](const uint8_t* sK, uint8_t* sQn) {
+    bf16x8 kf[4];
+    k_frags(sK, koff, kf);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+      *reinterpret_cast<f32x4*>(sQn + (wave * NHB + hb) * 1024 + lane16) = partial_scores(kf, qf[hb]);
+  };
+  // The four waves' partial scores of head block `wave` from sQc.
+  auto read_partials = [&](const uint8_t* sQc, f32x4 (&sp)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      sp[u] = *reinterpret_cast<const f32x4*>(sQc + (u * NHB + wave) * 1024 + lane16);
+  };
+  // Weights of tile j for head block `wave` (owner waves) from its four
+  // partial score tiles: mask, reference, exp2, bf16, row sum; P^T fragment
+  // stored at this wave's slot of sPn.  Past the last tile every key is masked
+  // and nothing is added.
+  auto weights = [&](int j, const f32x4 (&sp)[4], uint8_t* sPn) {
+    f32x4 s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
     const TileRef tr = tile_ref(ks, j);
+    const int valid = j < n ? tr.valid : 0;
     float mt = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      s[r] = 4 * g4 + r < tr.valid ? s[r] * a.c : -INFINITY;
+      s[r] = 4 * g4 + r < valid ? s[r] * a.c : -INFINITY;
       mt = fmaxf(mt, s[r]);
     }
     if (j == 0 && !fixed_m) m = xmax32(xmax16(mt));  // the reference: max of the first tile
@@ -262,42 +278,43 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     *reinterpret_cast<i16x4*>(sPn + wave * 512 + lane8) = __builtin_bit_cast(i16x4, pb);
   };
 
-  // Step s: V(s) in sVc, its weights in sPc; K(s+1) in sKn.  Adds the value
-  // product of tile s, writes the weights of tile s+1 into sPn, and copies
-  // K(s+4) into dK (the stage of K(s)) and V(s+3) into dV (that of V(s-1)).
-  auto step = [&](int s, const uint8_t* sKn, const uint8_t* sVc, const uint8_t* sPc, uint8_t* sPn,
-                  uint8_t* dK, uint8_t* dV) {
+  // Step s: K(s+2) and V(s) in sAr, the partial scores of tile s+1 in sQc, the
+  // weights of tile s in sPc.  Adds the value product of tile s, writes the
+  // weights of tile s+1 into sPn and the partial scores of tile s+2 into sQn,
+  // and copies K(s+5) and V(s+3) into sAd.
+  auto step = [&](int s, const uint8_t* sAr, const uint8_t* sQc, uint8_t* sQn, const uint8_t* sPc,
+                  uint8_t* sPn, uint8_t* sAd) {
     int w = wave;
     asm volatile("" : "+s"(w), "+s"(s));  // per-step values computed here, not kept in registers
-    // LDS reads first (a read issued after a copy would wait for it), the K
-    // fragments ahead of the rest so the score MFMAs can start early.
-    bf16x8 kf[8];
-    if (owner) k_frags(sKn, koff, 0, kf);
+    // LDS reads first (a read issued after a copy would wait for it).
+    bf16x8 kf[4];
+    k_frags(sAr, koff, kf);
+    f32x4 sp[4];
+    if (owner) read_partials(sQc, sp);
     i16x4 pf[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) pf[hb] = *reinterpret_cast<const i16x4*>(sPc + hb * 512 + lane8);
     i16x4 vf[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db)
-      vf[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sVc + voff + 32 * db));
+      vf[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sAr + kKBytes + voff + 32 * db));
     __builtin_amdgcn_sched_barrier(0);
-    copy_rows(ks, s + 4, ks.ek, ks.wk, dK, kKRow, w, lane16);
-    copy_rows(ks, s + 3, ks.ev, ks.wv, dV, kVRow, w, lane16);
-    f32x4 s0 = {}, s1 = {};
-    if (owner) {  // past the last tile: scores of a stale stage, unused
-      score_half(kf, qf, 0, s0, s1);
-      k_frags(sKn, koff, 1, kf);
-      score_half(kf, qf, 1, s0, s1);
-    }
+    copy_rows(ks, s + 5, ks.ek, ks.wk, sAd, kKRow, w, lane16);
+    copy_rows(ks, s + 3, ks.ev, ks.wv, sAd + kKBytes, kVRow, w, lane16);
+    // scores of tile s+2
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+      *reinterpret_cast<f32x4*>(sQn + (w * NHB + hb) * 1024 + lane16) = partial_scores(kf, qf[hb]);
+    // weights of tile s+1 (its partial scores were read above)
+    if (owner) weights(s + 1, sp, sPn);
+    // values of tile s
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-        pv_mfma(o[hb][db], vf[db], pf[hb]);
-    if (owner && s + 1 < n) weights(s + 1, s0 + s1, sPn);
-    // K(s+2) and V(s+1) are in for this wave (the copies issued after them,
-    // K(s+3), V(s+2), K(s+4), V(s+3), may be in flight), the weights written;
-    // then for every wave.
+      for (int db = 0; db < 8; ++db) pv_mfma(o[hb][db], vf[db], pf[hb]);
+    // K(s+3) and V(s+1) are in for this wave (the copies issued after them,
+    // by steps s-1 and s, may be in flight), the LDS writes done; then for
+    // every wave.
     wait_4_groups();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     barrier_no_fence();
@@ -310,47 +327,50 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
       for (int db = 0; db < 8; ++db) o[hb][db] = f32x4{};
     l = 0.0f;
     over = false;
-    if (owner) {
 #pragma unroll
-      for (int ss = 0; ss < 16; ++ss) qf[ss] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ss);
-    }
-    // Prologue: K(0); K(1), V(0); K(2), V(1); K(3), V(2) copied, in that order;
-    // weights of tile 0.
-    copy_rows(ks, 0, ks.ek, ks.wk, sK0, kKRow, wave, lane16);
-    copy_rows(ks, 1, ks.ek, ks.wk, sK1, kKRow, wave, lane16);
-    copy_rows(ks, 0, ks.ev, ks.wv, sV0, kVRow, wave, lane16);
-    copy_rows(ks, 2, ks.ek, ks.wk, sK2, kKRow, wave, lane16);
-    copy_rows(ks, 1, ks.ev, ks.wv, sV1, kVRow, wave, lane16);
-    copy_rows(ks, 3, ks.ek, ks.wk, sK3, kKRow, wave, lane16);
-    copy_rows(ks, 2, ks.ev, ks.wv, sV2, kVRow, wave, lane16);
-    wait_6_groups();  // K(0) in
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss)
+        qf[hb][ss] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)16 * hb * kD + 32 * ss);
+    // Prologue.  Copies in the order of the steps that would issue them
+    // (step c copies K(c+5), V(c+3)): K(0); K(1); K(2), V(0); K(3), V(1).
+    copy_rows(ks, 0, ks.ek, ks.wk, sA0, kKRow, wave, lane16);
+    copy_rows(ks, 1, ks.ek, ks.wk, sA1, kKRow, wave, lane16);
+    copy_rows(ks, 2, ks.ek, ks.wk, sA2, kKRow, wave, lane16);
+    copy_rows(ks, 0, ks.ev, ks.wv, sA2 + kKBytes, kVRow, wave, lane16);
+    copy_rows(ks, 3, ks.ek, ks.wk, sA3, kKRow, wave, lane16);
+    copy_rows(ks, 1, ks.ev, ks.wv, sA3 + kKBytes, kVRow, wave, lane16);
+    wait_5_groups();  // K(0) in (and Q, G: loads complete in order)
     barrier_no_fence();
+    scores(sA0, sQ0);
+    wait_4_groups();  // K(1) in
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier_no_fence();  // partial scores of tile 0 written, K(0) read by every wave
+    scores(sA1, sQ1);
     if (owner) {
-      f32x4 s0 = {}, s1 = {};
-      bf16x8 kf[8];
-      k_frags(sK0, koff, 0, kf);
-      score_half(kf, qf, 0, s0, s1);
-      k_frags(sK0, koff, 1, kf);
-      score_half(kf, qf, 1, s0, s1);
-      weights(0, s0 + s1, sP0);
+      f32x4 sp[4];
+      read_partials(sQ0, sp);
+      weights(0, sp, sP0);
     }
-    wait_4_groups();  // K(1), V(0) in
+    copy_rows(ks, 4, ks.ek, ks.wk, sA0, kKRow, wave, lane16);
+    copy_rows(ks, 2, ks.ev, ks.wv, sA0 + kKBytes, kVRow, wave, lane16);
+    wait_4_groups();  // K(2), V(0) in
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier_no_fence();
     // Whole groups of four steps, then the rest (nested, so the compiler
     // sees the same copies in flight on every path into a step).
     int s = 0;
     for (; s + 4 <= n; s += 4) {
-      step(s, sK1, sV0, sP0, sP1, sK0, sV3);
-      step(s + 1, sK2, sV1, sP1, sP0, sK1, sV0);
-      step(s + 2, sK3, sV2, sP0, sP1, sK2, sV1);
-      step(s + 3, sK0, sV3, sP1, sP0, sK3, sV2);
+      step(s, sA2, sQ1, sQ0, sP0, sP1, sA1);
+      step(s + 1, sA3, sQ0, sQ1, sP1, sP0, sA2);
+      step(s + 2, sA0, sQ1, sQ0, sP0, sP1, sA3);
+      step(s + 3, sA1, sQ0, sQ1, sP1, sP0, sA0);
     }
     if (s < n) {
-      step(s, sK1, sV0, sP0, sP1, sK0, sV3);
+      step(s, sA2, sQ1, sQ0, sP0, sP1, sA1);
       if (s + 1 < n) {
-        step(s + 1, sK2, sV1, sP1, sP0, sK1, sV0);
-        if (s + 2 < n) step(s + 2, sK3, sV2, sP0, sP1, sK2, sV1);
+        step(s + 1, sA3, sQ0, sQ1, sP1, sP0, sA2);
+        if (s + 2 < n) step(s + 2, sA0, sQ1, sQ0, sP0, sP1, sA3);
       }
     }
     // Row sums and the repeat decision of every head block, through LDS.
@@ -417,18 +437,15 @@ hipError_t launch_decode(const DecodeProblem& p, hipStream_t stream) {
   a.H = p.H;
   a.c = p.scale * 1.4426950408889634f;
   a.out_f32 = p.out_f32 ? 1 : 0;
-  // Heads per workgroup: all of them when the batch fills the chip, else
-  // fewer, so that more workgroups share the per-head loads, gate and stores.
-  int nhb = p.H / 16;
-  while (nhb > 1 && ((int64_t)p.B * (p.H / 16 / nhb) < 256 || (p.H / 16) % nhb != 0)) --nhb;
+  // Heads per workgroup: 32 when the batch still fills the chip with them,
+  // else 16.
+  const int nhb = (p.H % 32 == 0 && (int64_t)p.B * (p.H / 32) >= 256) ? 2 : 1;
   a.n_hg = p.H / 16 / nhb;
   const dim3 grid((unsigned)(((p.B + 7) / 8) * 8 * a.n_hg)), block(256);
-  switch (nhb) {
-    case 1: hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, a); break;
-  }
+  if (nhb == 2)
+    hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
