@@ -7,16 +7,18 @@
 // section 43 层里，37 层只读摘要).  The output is gated by sigmoid(G)
 // (blog.derekhsu.net, section 低秩閘控注意力).
 //
-// Decomposition.  One workgroup per (sequence, 16 * NHB of its heads), NHB = 1
-// or 2, chosen so that the batch fills the chip; the head groups of a sequence
+// Decomposition.  One workgroup per (sequence, 16 * NHB of its heads), NHB = 1,
+// 2 or 4, chosen so that the batch fills the chip; the head groups of a sequence
 // run on one XCD and share its K/V bytes in that XCD's L2.  The keys are walked
 // in 16-key tiles: first the entries (the last entry tile masked past the last
-// entry), then the window, so every tile comes from one buffer.  The four
-// waves copy each tile into LDS together by DMA (four stages of K and of V).
+// entry), then the window, so every tile comes from one buffer.  Each wave
+// loads the K fragments of its dims straight into registers (a ring of six
+// tiles); the four waves copy each V tile into LDS together by DMA (six
+// stages).  Both run four or more steps ahead of their use.
 // Each step runs three tiles at once:
 //   scores  tile s+2: wave w computes the partial scores S^T[key][head] over
 //           its dims 128w .. 128w+127 for every head (4 MFMA 16x16x32 per
-//           16 heads, K from LDS, Q^T in VGPRs) and writes them to LDS;
+//           16 heads, K and Q^T in VGPRs) and writes them to LDS;
 //   softmax tile s+1: wave hb < NHB sums the four partial score tiles of head
 //           block hb, masks, weighs, rounds to bf16 and writes P^T to LDS;
 //   values  tile s: wave w adds O^T[dv][head] += V^T P^T for its 128 dims of
@@ -37,9 +39,7 @@ namespace hca {
 namespace {
 
 constexpr int kTile = 16;
-constexpr int kKRow = 1024 + 16;  // LDS bytes between K rows (conflict-free b128 reads)
 constexpr int kVRow = 1024 + 64;  // between V rows (conflict-free transpose reads)
-constexpr int kKBytes = kTile * kKRow;
 constexpr int kVBytes = kTile * kVRow;
 constexpr float kHeadroom = 64.0f;
 
@@ -124,18 +124,27 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(w[0]) + __uint_as_float(w[1]);
 }
 
-// s_waitcnt vmcnt(4n): at most n groups of 4 copies (one tensor's rows of one
-// tile for this wave) still in flight.
-__device__ __forceinline__ void wait_4_groups() { __builtin_amdgcn_s_waitcnt(0x4F70); }
-__device__ __forceinline__ void wait_5_groups() { __builtin_amdgcn_s_waitcnt(0x4F74); }
+// s_waitcnt vmcnt(8n): at most n steps' worth of this wave's loads (4 K
+// fragment loads and 4 V row copies each) still in flight.
+__device__ __forceinline__ void wait_4_steps() { __builtin_amdgcn_s_waitcnt(0x8F70); }  // vmcnt(32)
 
-// Partial scores of one tile over this wave's dims for one head block: lane
-// (head l16, g4) gets keys 4g4 .. 4g4+3.  koff addresses K row l16, dims
-// 128w + 8g4; fragment ss holds dims 128w + 32ss + 8g4 .. +7, like the Q
-// fragments.
-__device__ __forceinline__ void k_frags(const uint8_t* sK, int koff, bf16x8 (&kf)[4]) {
+// K fragments of tile j for this wave's dims, loaded into registers: lane
+// (key l16, g4) gets dims 128w + 32ss + 8g4 .. +7 of the tile's key l16
+// (ss = 0..3).  Through a buffer descriptor: entry rows past the last entry,
+// and every row of a tile past the last, read as zeros; window rows past the
+// last valid position repeat it.
+__device__ __forceinline__ void load_k(const Keys& ks, int j, int wave, int l16, int g4,
+                                       bf16x8 (&kf)[4]) {
+  asm volatile("" : "+s"(wave), "+s"(j));  // addresses computed here, not kept in registers
+  const TileRef tr = tile_ref(ks, j);
+  const int bytes = j < ks.n_tiles ? (tr.ent ? ks.nc : kWindow) * 1024 : 0;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tr.ent ? ks.ek : ks.wk, bytes);
+  const int k = tr.first + l16;
+  const int row = tr.ent ? k : ((ks.lo + (k < ks.nw ? k : ks.nw - 1)) & (kWindow - 1));
+  const int off = row * 1024 + 256 * wave + 16 * g4;
 #pragma unroll
-  for (int ss = 0; ss < 4; ++ss) kf[ss] = *reinterpret_cast<const bf16x8*>(sK + koff + 64 * ss);
+  for (int ss = 0; ss < 4; ++ss)
+    kf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * ss, 0, 0));
 }
 __device__ __forceinline__ f32x4 partial_scores(const bf16x8 (&kf)[4], const bf16x8 (&qf)[4]) {
   f32x4 s0 = {}, s1 = {};
@@ -158,17 +167,16 @@ __device__ __forceinline__ void pv_mfma(f32x4& acc, i16x4 v, i16x4 p) {
 
 template <int NHB>
 __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
-  // Array sAi holds K stage i and V stage i+2 (mod 4): K(j) is in sA(j%4) and
-  // V(j) in sA((j+2)%4).  Step s copies K(s+5) and V(s+3), both into
-  // sA((s+1)%4), and reads K(s+2) and V(s), both in sA((s+2)%4); with the
-  // arrays separate the compiler can tell every copy in flight from the reads
-  // that follow.  Two buffers each of weights (P^T of every head block) and
-  // of partial scores (every wave's, for every head block), the row sums and
-  // the repeat flags.
-  __shared__ __attribute__((aligned(256))) uint8_t sA0[kKBytes + kVBytes];
-  __shared__ __attribute__((aligned(256))) uint8_t sA1[kKBytes + kVBytes];
-  __shared__ __attribute__((aligned(256))) uint8_t sA2[kKBytes + kVBytes];
-  __shared__ __attribute__((aligned(256))) uint8_t sA3[kKBytes + kVBytes];
+  // Six V stages (V(j) in stage j % 6), two buffers each of weights (P^T of
+  // every head block) and of partial scores (every wave's, for every head
+  // block), the row sums and the repeat flags.  Separate arrays, so the
+  // compiler can tell a copy into one stage from reads of another.
+  __shared__ __attribute__((aligned(256))) uint8_t sV0[kVBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t sV1[kVBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t sV2[kVBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t sV3[kVBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t sV4[kVBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t sV5[kVBytes];
   __shared__ __attribute__((aligned(256))) uint8_t sP0[NHB * 512];
   __shared__ __attribute__((aligned(256))) uint8_t sP1[NHB * 512];
   __shared__ __attribute__((aligned(256))) uint8_t sQ0[4 * NHB * 1024];
@@ -185,11 +193,25 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   if (b >= a.B) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
-  const bool owner = wave < NHB;  // this wave takes the softmax of head block `wave`
+  const bool owner = NHB == 4 || wave < NHB;  // this wave takes the softmax of head block `wave`
 
   // The position first: the copies wait for it.  The loads of the gate
-  // logits follow; they overlap the first copies (the copies' waits below
-  // cover them: loads complete in order).
+  // logits follow; they overlap the first copies.
+  bf16x8 kr[6][4];  // K fragments in registers, tile j in slot j % 6
+  auto prologue_loads = [&](const Keys& kk) {
+    const int lane16 = lane * 16;
+    load_k(kk, 0, wave, l16, g4, kr[0]);
+    load_k(kk, 1, wave, l16, g4, kr[1]);
+    copy_rows(kk, 0, kk.ev, kk.wv, sV0, kVRow, wave, lane16);
+    load_k(kk, 2, wave, l16, g4, kr[2]);
+    copy_rows(kk, 1, kk.ev, kk.wv, sV1, kVRow, wave, lane16);
+    load_k(kk, 3, wave, l16, g4, kr[3]);
+    copy_rows(kk, 2, kk.ev, kk.wv, sV2, kVRow, wave, lane16);
+    load_k(kk, 4, wave, l16, g4, kr[4]);
+    copy_rows(kk, 3, kk.ev, kk.wv, sV3, kVRow, wave, lane16);
+    load_k(kk, 5, wave, l16, g4, kr[5]);
+    copy_rows(kk, 4, kk.ev, kk.wv, sV4, kVRow, wave, lane16);
+  };
   const int64_t t_raw = a.pos[b];
   const int64_t head0 = (int64_t)b * a.H + hg * 16 * NHB;
   // Gate logits of this lane's outputs: head 16hb + l16, dims 128w + 16db + 4g4 .. +3.
@@ -224,10 +246,9 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   ks.wv = a.wv + (int64_t)b * kWindow * kD;
   const int n = ks.n_tiles;  // >= 1: the new token itself is always a key
 
-  // Lane offsets: K fragment source (row l16, dims 128w + 8g4); V^T transpose
-  // read source (key row 4g4 + l16/4, dims 128w + 4(l16&3)); the lane's slot
-  // of a weight buffer (8 bytes) and of a partial-score buffer (16 bytes).
-  const int koff = l16 * kKRow + 256 * wave + 16 * g4;
+  // Lane offsets: V^T transpose read source (key row 4g4 + l16/4, dims 128w +
+  // 4(l16&3)); the lane's slot of a weight buffer (8 bytes) and of a
+  // partial-score buffer (16 bytes).
   const int voff = (4 * g4 + (l16 >> 2)) * kVRow + 256 * wave + 8 * (l16 & 3);
   const int lane8 = lane * 8, lane16 = lane * 16;
 
@@ -236,11 +257,9 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   float m = -INFINITY, mseen = -INFINITY, l = 0.0f;
   bool over = false, fixed_m = false;
 
-  // This wave's partial scores of the tile whose K is in sK, for every head
-  // block, into its slots of sQn.
-  auto scores = [&](const uint8_t* sK, uint8_t* sQn) {
-    bf16x8 kf[4];
-    k_frags(sK, koff, kf);
+  // This wave's partial scores of a tile for every head block, from its K
+  // fragments, into its slots of sQn.
+  auto scores = [&](const bf16x8 (&kf)[4], uint8_t* sQn) {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
       *reinterpret_cast<f32x4*>(sQn + (wave * NHB + hb) * 1024 + lane16) = partial_scores(kf, qf[hb]);
@@ -278,17 +297,16 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     *reinterpret_cast<i16x4*>(sPn + wave * 512 + lane8) = __builtin_bit_cast(i16x4, pb);
   };
 
-  // Step s: K(s+2) and V(s) in sAr, the partial scores of tile s+1 in sQc, the
-  // weights of tile s in sPc.  Adds the value product of tile s, writes the
-  // weights of tile s+1 into sPn and the partial scores of tile s+2 into sQn,
-  // and copies K(s+5) and V(s+3) into sAd.
-  auto step = [&](int s, const uint8_t* sAr, const uint8_t* sQc, uint8_t* sQn, const uint8_t* sPc,
-                  uint8_t* sPn, uint8_t* sAd) {
+  // Step s: K(s+2) in registers kc, V(s) in sVc, the partial scores of tile s+1
+  // in sQc, the weights of tile s in sPc.  Writes the partial scores of tile
+  // s+2 into sQn and the weights of tile s+1 into sPn, adds the value product
+  // of tile s, and loads K(s+6) into kn (the slot of K(s)) and V(s+5) into sVd
+  // (the stage of V(s-1)).
+  auto step = [&](int s, const bf16x8 (&kc)[4], bf16x8 (&kn)[4], const uint8_t* sVc, uint8_t* sVd,
+                  const uint8_t* sQc, uint8_t* sQn, const uint8_t* sPc, uint8_t* sPn) {
     int w = wave;
     asm volatile("" : "+s"(w), "+s"(s));  // per-step values computed here, not kept in registers
     // LDS reads first (a read issued after a copy would wait for it).
-    bf16x8 kf[4];
-    k_frags(sAr, koff, kf);
     f32x4 sp[4];
     if (owner) read_partials(sQc, sp);
     i16x4 pf[NHB];
@@ -297,25 +315,19 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     i16x4 vf[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db)
-      vf[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sAr + kKBytes + voff + 32 * db));
+      vf[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sVc + voff + 32 * db));
     __builtin_amdgcn_sched_barrier(0);
-    copy_rows(ks, s + 5, ks.ek, ks.wk, sAd, kKRow, w, lane16);
-    copy_rows(ks, s + 3, ks.ev, ks.wv, sAd + kKBytes, kVRow, w, lane16);
-    // scores of tile s+2
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-      *reinterpret_cast<f32x4*>(sQn + (w * NHB + hb) * 1024 + lane16) = partial_scores(kf, qf[hb]);
-    // weights of tile s+1 (its partial scores were read above)
-    if (owner) weights(s + 1, sp, sPn);
-    // values of tile s
+    scores(kc, sQn);  // tile s+2
+    load_k(ks, s + 6, w, l16, g4, kn);
+    copy_rows(ks, s + 5, ks.ev, ks.wv, sVd, kVRow, w, lane16);
+    if (owner) weights(s + 1, sp, sPn);  // tile s+1
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) pv_mfma(o[hb][db], vf[db], pf[hb]);
-    // K(s+3) and V(s+1) are in for this wave (the copies issued after them,
-    // by steps s-1 and s, may be in flight), the LDS writes done; then for
-    // every wave.
-    wait_4_groups();
+      for (int db = 0; db < 8; ++db) pv_mfma(o[hb][db], vf[db], pf[hb]);  // tile s
+    // V(s+1) is in for this wave (the loads and copies of steps s-3 .. s may
+    // be in flight), the LDS writes done; then for every wave.
+    wait_4_steps();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     barrier_no_fence();
   };
@@ -332,47 +344,48 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss)
         qf[hb][ss] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)16 * hb * kD + 32 * ss);
-    // Prologue.  Copies in the order of the steps that would issue them
-    // (step c copies K(c+5), V(c+3)): K(0); K(1); K(2), V(0); K(3), V(1).
-    copy_rows(ks, 0, ks.ek, ks.wk, sA0, kKRow, wave, lane16);
-    copy_rows(ks, 1, ks.ek, ks.wk, sA1, kKRow, wave, lane16);
-    copy_rows(ks, 2, ks.ek, ks.wk, sA2, kKRow, wave, lane16);
-    copy_rows(ks, 0, ks.ev, ks.wv, sA2 + kKBytes, kVRow, wave, lane16);
-    copy_rows(ks, 3, ks.ek, ks.wk, sA3, kKRow, wave, lane16);
-    copy_rows(ks, 1, ks.ev, ks.wv, sA3 + kKBytes, kVRow, wave, lane16);
-    wait_5_groups();  // K(0) in (and Q, G: loads complete in order)
-    barrier_no_fence();
-    scores(sA0, sQ0);
-    wait_4_groups();  // K(1) in
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    barrier_no_fence();  // partial scores of tile 0 written, K(0) read by every wave
-    scores(sA1, sQ1);
+    // Prologue: the loads that steps -6 .. -1 would issue (step c loads
+    // K(c+6) and V(c+5)), the partial scores of tiles 0 and 1, the weights of
+    // tile 0.
+    prologue_loads(ks);
+    scores(kr[0], sQ0);
+    scores(kr[1], sQ1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    barrier_no_fence();  // every wave's partial scores of tiles 0, 1
     if (owner) {
       f32x4 sp[4];
       read_partials(sQ0, sp);
       weights(0, sp, sP0);
     }
-    copy_rows(ks, 4, ks.ek, ks.wk, sA0, kKRow, wave, lane16);
-    copy_rows(ks, 2, ks.ev, ks.wv, sA0 + kKBytes, kVRow, wave, lane16);
-    wait_4_groups();  // K(2), V(0) in
+    wait_4_steps();  // V(0) in
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier_no_fence();
-    // Whole groups of four steps, then the rest (nested, so the compiler
-    // sees the same copies in flight on every path into a step).
+    // Whole groups of six steps, then the rest (nested, so the compiler sees
+    // the same loads in flight on every path into a step).
     int s = 0;
-    for (; s + 4 <= n; s += 4) {
-      step(s, sA2, sQ1, sQ0, sP0, sP1, sA1);
-      step(s + 1, sA3, sQ0, sQ1, sP1, sP0, sA2);
-      step(s + 2, sA0, sQ1, sQ0, sP0, sP1, sA3);
-      step(s + 3, sA1, sQ0, sQ1, sP1, sP0, sA0);
+    for (; s + 6 <= n; s += 6) {
+      step(s, kr[2], kr[0], sV0, sV5, sQ1, sQ0, sP0, sP1);
+      step(s + 1, kr[3], kr[1], sV1, sV0, sQ0, sQ1, sP1, sP0);
+      step(s + 2, kr[4], kr[2], sV2, sV1, sQ1, sQ0, sP0, sP1);
+      step(s + 3, kr[5], kr[3], sV3, sV2, sQ0, sQ1, sP1, sP0);
+      step(s + 4, kr[0], kr[4], sV4, sV3, sQ1, sQ0, sP0, sP1);
+      step(s + 5, kr[1], kr[5], sV5, sV4, sQ0, sQ1, sP1, sP0);
     }
     if (s < n) {
-      step(s, sA2, sQ1, sQ0, sP0, sP1, sA1);
+      step(s, kr[2], kr[0], sV0, sV5, sQ1, sQ0, sP0, sP1);
       if (s + 1 < n) {
-        step(s + 1, sA3, sQ0, sQ1, sP1, sP0, sA2);
-        if (s + 2 < n) step(s + 2, sA0, sQ1, sQ0, sP0, sP1, sA3);
+        step(s + 1, kr[3], kr[1], sV1, sV0, sQ0, sQ1, sP1, sP0);
+        if (s + 2 < n) {
+          step(s + 2, kr[4], kr[2], sV2, sV1, sQ1, sQ0, sP0, sP1);
+          if (s + 3 < n) {
+            step(s + 3, kr[5], kr[3], sV3, sV2, sQ0, sQ1, sP1, sP0);
+            if (s + 4 < n) step(s + 4, kr[0], kr[4], sV4, sV3, sQ1, sQ0, sP0, sP1);
+          }
+        }
       }
     }
+    // Loads past the last tile may still be in flight into registers.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     // Row sums and the repeat decision of every head block, through LDS.
     if (owner) {
       const float lh = xsum32(xsum16(l));
@@ -437,15 +450,18 @@ hipError_t launch_decode(const DecodeProblem& p, hipStream_t stream) {
   a.H = p.H;
   a.c = p.scale * 1.4426950408889634f;
   a.out_f32 = p.out_f32 ? 1 : 0;
-  // Heads per workgroup: 32 when the batch still fills the chip with them,
-  // else 16.
-  const int nhb = (p.H % 32 == 0 && (int64_t)p.B * (p.H / 32) >= 256) ? 2 : 1;
+  // Heads per workgroup: the most (16, 32 or 64) that still give at least
+  // 256 workgroups, so each K/V byte is copied into as few CUs as the batch
+  // allows while the chip stays full.
+  int nhb = 4;
+  while (nhb > 1 && ((int64_t)p.B * (p.H / 16 / nhb) < 256 || (p.H / 16) % nhb != 0)) nhb >>= 1;
   a.n_hg = p.H / 16 / nhb;
   const dim3 grid((unsigned)(((p.B + 7) / 8) * 8 * a.n_hg)), block(256);
-  if (nhb == 2)
-    hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, stream, a);
+  switch (nhb) {
+    case 4: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 
