@@ -52,6 +52,16 @@ def test_mixed_positions(H):
     compare(host_f64(d.run()), d.oracle(), f"decode H={H}")
 
 
+@pytest.mark.parametrize("B", [128, 256])
+def test_large_batches(B):
+    # 64 heads: 128 sequences take 32 heads per workgroup, 256 take all 64
+    rng = np.random.default_rng(B)
+    positions = rng.integers(0, 3000, size=B)
+    positions[:4] = [0, 127, 128, 2999]
+    d = Decode(seed=17 + B, positions=positions, H=64, out_dtype="f32")
+    compare(host_f64(d.run()), d.oracle(), f"decode B={B}")
+
+
 def test_cache_larger_than_needed():
     d = Decode(seed=12, positions=[200, 700, 50], H=32, nc_cap=40)
     compare(host_f64(d.run()), d.oracle(), "nc_cap 40")
