@@ -134,3 +134,42 @@ def decode(q, g, ck, cv, wk, wv, pos, *, block=128, window=128, scale=None,
     if rc:
         raise OracleError(f"hca_oracle_decode: {rc}")
     return out
+
+
+def decode_multi(q, g, ck, cv, wk, wv, nk, nv, pos, *, block=128, window=128, scale=None,
+                 nthreads=0) -> np.ndarray:
+    """Multi-token decode: M new tokens per sequence at positions pos .. pos+M-1, as
+    when a drafter's tokens are verified in one pass (the ECHO layer doubles as a
+    speculative-decoding drafter: blog.derekhsu.net, section "ECHO：取代 MTP 模組";
+    two-step drafts in low-latency serving: lininn.cn, section "把 MTP 模块删了").
+    Each new token is an ordinary query at its own
+    position, so it attends to the entries of the blocks completed at or before it,
+    to the committed raw rows of its window, and to the new tokens up to itself.
+
+      q, g    [B, M, H, D]        queries and gate logits of the new tokens
+      ck, cv  [B, nc_cap, D]      entries (the first floor((pos+M)/block) are used)
+      wk, wv  [B, window, D]      ring of committed rows: position p < pos in slot p % window
+      nk, nv  [B, M, D]           raw rows of the new tokens (positions pos .. pos+M-1)
+      pos     [B]                 position of the first new token
+
+    Composed from ``attn``: per sequence the raw rows max(0, pos-window+1) .. pos-1 are
+    taken from the ring, followed by the M new rows, and ``attn`` is called with the
+    queries at positions pos .. pos+M-1.  Returns float64 [B, M, H, D]."""
+    q, g, wk, wv, nk, nv = _u16(q), _u16(g), _u16(wk), _u16(wv), _u16(nk), _u16(nv)
+    ck, cv = _u16(ck), _u16(cv)
+    B, M, H, D = q.shape
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    assert pos.shape == (B,) and nk.shape == (B, M, D) and wk.shape == (B, window, D)
+    out = np.empty((B, M, H, D), dtype=np.float64)
+    for b in range(B):
+        t = int(pos[b])
+        if t < 0 or (t + M) // block > ck.shape[1]:
+            raise OracleError("decode_multi: position out of range")
+        lo = max(0, t - window + 1)
+        slots = [p % window for p in range(lo, t)]
+        k = np.concatenate([wk[b, slots], nk[b]]) if slots else nk[b]
+        v = np.concatenate([wv[b, slots], nv[b]]) if slots else nv[b]
+        nc = (t + M) // block
+        out[b] = attn(q[b], g[b], t + np.arange(M), k, v, lo, ck[b, :nc], cv[b, :nc],
+                      block=block, window=window, scale=scale, nthreads=nthreads)
+    return out
