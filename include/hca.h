@@ -130,6 +130,35 @@ hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const
                              int B, int H, int D, int block, int window, float scale, void* out,
                              hca_dtype_t out_dtype, void* stream);
 
+/*
+ * Multi-token decode: M new tokens per sequence at positions pos .. pos+M-1, for B
+ * sequences at once, as when the tokens of a drafter are verified in one pass (the
+ * ECHO layer doubles as a speculative-decoding drafter: blog.derekhsu.net, section
+ * "ECHO：取代 MTP 模組"; two-step drafts in low-latency serving: lininn.cn, section
+ * "把 MTP 模块删了").  Each new token is an ordinary query at its own position
+ * (the prefill rule), so it sees the earlier new tokens but not the later ones.
+ *   q, g     device, bf16 [B, M, H, D]       queries and gate logits of the new tokens
+ *   ck, cv   device, bf16 [B, nc_cap, D]     per-sequence entries (only the first
+ *                                            floor((pos+M)/128) are read: a block
+ *                                            completed by a new token must already
+ *                                            have its entry)
+ *   wk, wv   device, bf16 [B, window, D]     ring of committed raw rows; position p lives
+ *                                            in slot p % window, and slots of positions
+ *                                            max(0,pos-127)..pos-1 must be valid
+ *   nk, nv   device, bf16 [B, M, D]          raw rows of the new tokens
+ *   pos      device, int64 [B]               position of the first new token
+ *   out      device, [B, M, H, D]            bf16 or f32
+ * 1 <= M <= 16 and M*H <= 1024 (else HCA_ERR_UNSUPPORTED).  With M = 1 this is
+ * hca_attn_decode with the new row passed in nk, nv instead of its ring slot.
+ * As for hca_attn_decode, a pos with floor((pos+M)/128) > nc_cap or pos < 0 is
+ * clamped on the device and its output is then unspecified.  B = 0 is a no-op.
+ */
+hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck, const void* cv,
+                                   int64_t nc_cap, const void* wk, const void* wv,
+                                   const void* nk, const void* nv, const int64_t* pos, int B,
+                                   int M, int H, int D, int block, int window, float scale,
+                                   void* out, hca_dtype_t out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,9 @@ def lib():
         L.hca_attn_prefill.restype = I
         L.hca_attn_decode.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, F, P, I, P]
         L.hca_attn_decode.restype = I
+        L.hca_attn_decode_multi.argtypes = [P, P, P, P, I64, P, P, P, P, P, I, I, I, I, I, I, F,
+                                            P, I, P]
+        L.hca_attn_decode_multi.restype = I
         _lib = L
     return _lib
 
@@ -126,5 +129,31 @@ def hca_attn_decode(q, g, ck, cv, wk, wv, pos, out, *, scale: float | None = Non
         _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
         ck.shape[1], _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
         _dev_ptr(pos, "pos", torch.int64), B, H, Dd, block, window, float(scale),
+        _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
+        _stream(q.device)))
+
+
+def hca_attn_decode_multi(q, g, ck, cv, wk, wv, nk, nv, pos, out, *, scale: float | None = None,
+                          block: int = BLOCK, window: int = WINDOW):
+    """out [B, M, H, 512] <- HCA decode for M new tokens per sequence at positions
+    pos .. pos+M-1 (pos [B] int64 on the GPU), each attending causally to the earlier
+    new tokens.  Entries ck/cv [B, nc_cap, 512]; rings wk/wv [B, 128, 512] of committed
+    rows (position p < pos in slot p % 128); the new tokens' rows nk/nv [B, M, 512]."""
+    import torch
+    B, M, H, Dd = q.shape
+    if g.shape != q.shape or out.shape != q.shape:
+        raise ValueError("q, g and out must have the same shape")
+    if nk.shape != (B, M, Dd) or nv.shape != (B, M, Dd):
+        raise ValueError("nk and nv must be [B, M, D]")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    if scale is None:
+        scale = Dd ** -0.5
+    _check(lib().hca_attn_decode_multi(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
+        _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
+        ck.shape[1], _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
+        _dev_ptr(nk, "nk", torch.bfloat16), _dev_ptr(nv, "nv", torch.bfloat16),
+        _dev_ptr(pos, "pos", torch.int64), B, M, H, Dd, block, window, float(scale),
         _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
         _stream(q.device)))

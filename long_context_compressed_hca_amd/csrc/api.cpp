@@ -211,4 +211,54 @@ hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const
                     "hca_attn_decode launch");
 }
 
+hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck, const void* cv,
+                                   int64_t nc_cap, const void* wk, const void* wv,
+                                   const void* nk, const void* nv, const int64_t* pos, int B,
+                                   int M, int H, int D, int block, int window, float scale,
+                                   void* out, hca_dtype_t out_dtype, void* stream) {
+  TRY(check_shape(D, block, window));
+  if (B < 0) return fail(HCA_ERR_INVALID_ARG, "B = %d < 0", B);
+  if (M < 1 || M > 16) return fail(HCA_ERR_UNSUPPORTED, "M = %d (need 1 .. 16)", M);
+  if (H < 16 || H % 16 != 0 || M * H > 1024)
+    return fail(HCA_ERR_UNSUPPORTED, "H = %d, M = %d (need H a multiple of 16, M*H <= 1024)", H,
+                M);
+  if (nc_cap < 0) return fail(HCA_ERR_INVALID_ARG, "nc_cap = %lld < 0", (long long)nc_cap);
+  if (out_dtype != HCA_BF16 && out_dtype != HCA_F32)
+    return fail(HCA_ERR_INVALID_ARG, "unknown out_dtype %d", (int)out_dtype);
+  TRY(check_scale(scale));
+  if (B == 0) return ok();
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(g, "g"));
+  TRY(check_ptr(wk, "wk"));
+  TRY(check_ptr(wv, "wv"));
+  TRY(check_ptr(nk, "nk"));
+  TRY(check_ptr(nv, "nv"));
+  TRY(check_ptr(out, "out"));
+  if (pos == nullptr) return fail(HCA_ERR_INVALID_ARG, "pos is NULL");
+  if (reinterpret_cast<uintptr_t>(pos) % 8 != 0)
+    return fail(HCA_ERR_INVALID_ARG, "pos is not 8-byte aligned");
+  if (nc_cap > 0) {
+    TRY(check_ptr(ck, "ck"));
+    TRY(check_ptr(cv, "cv"));
+  }
+  hca::DecodeProblem p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.g = static_cast<const uint16_t*>(g);
+  p.ck = static_cast<const uint16_t*>(ck);
+  p.cv = static_cast<const uint16_t*>(cv);
+  p.wk = static_cast<const uint16_t*>(wk);
+  p.wv = static_cast<const uint16_t*>(wv);
+  p.pos = pos;
+  p.out = out;
+  p.nc_cap = nc_cap;
+  p.B = B;
+  p.H = H;
+  p.scale = scale;
+  p.out_f32 = out_dtype == HCA_F32;
+  return hip_status(hca::launch_decode_multi(p, static_cast<const uint16_t*>(nk),
+                                             static_cast<const uint16_t*>(nv), M,
+                                             static_cast<hipStream_t>(stream)),
+                    "hca_attn_decode_multi launch");
+}
+
 }  // extern "C"

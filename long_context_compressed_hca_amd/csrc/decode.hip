@@ -56,16 +56,26 @@ struct Args {
   const int64_t* pos;
   void* out;
   int64_t nc_cap;
-  int B, H, n_hg;  // n_hg workgroups per sequence, 16 * NHB heads each
+  int B, H, n_hg;  // H query rows per sequence; n_hg workgroups per sequence, 16 * NHB rows each
   float c;  // scale * log2(e)
   int out_f32;
+  // Several new tokens per sequence (MT): rows of token j are j * hpt * 16 ..
+  // (j+1) * hpt * 16 - 1; their keys and values are rows j of nk, nv [B, M, 512].
+  const uint16_t* nk;
+  const uint16_t* nv;
+  int M, hpt;
 };
 
 // The keys of one sequence: n_et entry tiles (entries 0 .. nc-1), then the
-// window tiles (positions lo .. t, ring slot = position % 128).
+// window tiles (positions lo .. lo+nw-1, ring slot = position % 128).  One new
+// token: the window ends at its position t.  M new tokens (MT): the window ends
+// at t-1 (n_rt ring tiles, possibly none), and one last tile holds the M new
+// rows.
 struct Keys {
   const uint16_t *ek, *ev, *wk, *wv;  // this sequence's entries and ring
+  const uint16_t *nk, *nv;            // MT: this sequence's new rows
   int nc, lo, nw, n_et, n_tiles;
+  int n_rt, M;                        // MT
 };
 
 // Tile j: entry or window tile, its first entry / window index, and its
@@ -83,26 +93,68 @@ __device__ __forceinline__ TileRef tile_ref(const Keys& ks, int j) {
   return r;
 }
 
-// Copy rows 4w .. 4w+3 of tile j of one tensor (entries `ent`, ring `win`)
-// into LDS rows `stride` bytes apart.  Entry rows past the last entry arrive as
+// MT tile j: 0 entry, 1 ring, 2 new rows; its first index in that segment.
+struct TileRefMT {
+  int kind, first;
+};
+__device__ __forceinline__ TileRefMT tile_ref_mt(const Keys& ks, int j) {
+  TileRefMT r;
+  r.kind = j < ks.n_et ? 0 : (j < ks.n_et + ks.n_rt ? 1 : 2);
+  r.first = kTile * (r.kind == 0 ? j : (r.kind == 1 ? j - ks.n_et : 0));
+  return r;
+}
+
+// Tile j of one tensor: its buffer (bytes = 0 past the last tile: every load
+// through it reads zeros and touches no memory) and the byte offset of key k of
+// the tile.  Entry rows past the last entry and new rows past the last read as
+// zeros (range check); ring rows past the last valid position repeat it (finite
+// data under a zero weight, whatever the unused ring slots hold).
+template <bool MT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const Keys& ks, int j,
+                                                            const uint16_t* ent,
+                                                            const uint16_t* win,
+                                                            const uint16_t* nrw) {
+  if constexpr (!MT) {
+    const TileRef tr = tile_ref(ks, j);
+    const int bytes = j < ks.n_tiles ? (tr.ent ? ks.nc : kWindow) * 1024 : 0;
+    return make_rsrc(tr.ent ? ent : win, bytes);
+  } else {
+    const TileRefMT tr = tile_ref_mt(ks, j);
+    const int rows = tr.kind == 0 ? ks.nc : (tr.kind == 1 ? kWindow : ks.M);
+    return make_rsrc(tr.kind == 0 ? ent : (tr.kind == 1 ? win : nrw),
+                     j < ks.n_tiles ? rows * 1024 : 0);
+  }
+}
+template <bool MT>
+__device__ __forceinline__ int tile_row(const Keys& ks, int j, int k) {
+  if constexpr (!MT) {
+    const TileRef tr = tile_ref(ks, j);
+    k += tr.first;
+    return tr.ent ? k : ((ks.lo + (k < ks.nw ? k : ks.nw - 1)) & (kWindow - 1));
+  } else {
+    const TileRefMT tr = tile_ref_mt(ks, j);
+    k += tr.first;
+    return tr.kind != 1 ? k : ((ks.lo + (k < ks.nw ? k : ks.nw - 1)) & (kWindow - 1));
+  }
+}
+
+// Copy rows 4w .. 4w+3 of tile j of one tensor (entries `ent`, ring `win`,
+// new rows `nrw`) into LDS rows `stride` bytes apart.  Entry rows past the last entry arrive as
 // zeros (buffer range check); window rows past the last valid position repeat
 // it (finite data under a zero weight, whatever the unused ring slots hold).
 // Past the last tile the copies are still issued, through an empty buffer, so
 // every step issues the same number of copies; they read no memory and write
 // zeros into a stage no later step reads.
+template <bool MT>
 __device__ __forceinline__ void copy_rows(const Keys& ks, int j, const uint16_t* ent,
-                                          const uint16_t* win, uint8_t* dst, int stride, int wave,
-                                          int lane16) {
+                                          const uint16_t* win, const uint16_t* nrw, uint8_t* dst,
+                                          int stride, int wave, int lane16) {
   asm volatile("" : "+s"(wave), "+s"(j));  // addresses computed here, not kept in registers
-  const TileRef tr = tile_ref(ks, j);
-  const int bytes = j < ks.n_tiles ? (tr.ent ? ks.nc : kWindow) * 1024 : 0;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tr.ent ? ent : win, bytes);
+  const __amdgpu_buffer_rsrc_t rs = tile_rsrc<MT>(ks, j, ent, win, nrw);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 4 * wave + u;
-    const int k = tr.first + r;
-    const int row = tr.ent ? k : ((ks.lo + (k < ks.nw ? k : ks.nw - 1)) & (kWindow - 1));
-    dma16_buf(rs, lane16 + row * 1024, (lds_void*)(dst + r * stride));
+    dma16_buf(rs, lane16 + tile_row<MT>(ks, j, r) * 1024, (lds_void*)(dst + r * stride));
   }
 }
 
@@ -133,15 +185,12 @@ __device__ __forceinline__ void wait_4_steps() { __builtin_amdgcn_s_waitcnt(0x8F
 // (ss = 0..3).  Through a buffer descriptor: entry rows past the last entry,
 // and every row of a tile past the last, read as zeros; window rows past the
 // last valid position repeat it.
+template <bool MT>
 __device__ __forceinline__ void load_k(const Keys& ks, int j, int wave, int l16, int g4,
                                        bf16x8 (&kf)[4]) {
   asm volatile("" : "+s"(wave), "+s"(j));  // addresses computed here, not kept in registers
-  const TileRef tr = tile_ref(ks, j);
-  const int bytes = j < ks.n_tiles ? (tr.ent ? ks.nc : kWindow) * 1024 : 0;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(tr.ent ? ks.ek : ks.wk, bytes);
-  const int k = tr.first + l16;
-  const int row = tr.ent ? k : ((ks.lo + (k < ks.nw ? k : ks.nw - 1)) & (kWindow - 1));
-  const int off = row * 1024 + 256 * wave + 16 * g4;
+  const __amdgpu_buffer_rsrc_t rs = tile_rsrc<MT>(ks, j, ks.ek, ks.wk, ks.nk);
+  const int off = tile_row<MT>(ks, j, l16) * 1024 + 256 * wave + 16 * g4;
 #pragma unroll
   for (int ss = 0; ss < 4; ++ss)
     kf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * ss, 0, 0));
@@ -165,7 +214,7 @@ __device__ __forceinline__ void pv_mfma(f32x4& acc, i16x4 v, i16x4 p) {
   asm("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
 
-template <int NHB>
+template <int NHB, bool MT>
 __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   // Six V stages (V(j) in stage j % 6), two buffers each of weights (P^T of
   // every head block) and of partial scores (every wave's, for every head
@@ -200,17 +249,17 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   bf16x8 kr[6][4];  // K fragments in registers, tile j in slot j % 6
   auto prologue_loads = [&](const Keys& kk) {
     const int lane16 = lane * 16;
-    load_k(kk, 0, wave, l16, g4, kr[0]);
-    load_k(kk, 1, wave, l16, g4, kr[1]);
-    copy_rows(kk, 0, kk.ev, kk.wv, sV0, kVRow, wave, lane16);
-    load_k(kk, 2, wave, l16, g4, kr[2]);
-    copy_rows(kk, 1, kk.ev, kk.wv, sV1, kVRow, wave, lane16);
-    load_k(kk, 3, wave, l16, g4, kr[3]);
-    copy_rows(kk, 2, kk.ev, kk.wv, sV2, kVRow, wave, lane16);
-    load_k(kk, 4, wave, l16, g4, kr[4]);
-    copy_rows(kk, 3, kk.ev, kk.wv, sV3, kVRow, wave, lane16);
-    load_k(kk, 5, wave, l16, g4, kr[5]);
-    copy_rows(kk, 4, kk.ev, kk.wv, sV4, kVRow, wave, lane16);
+    load_k<MT>(kk, 0, wave, l16, g4, kr[0]);
+    load_k<MT>(kk, 1, wave, l16, g4, kr[1]);
+    copy_rows<MT>(kk, 0, kk.ev, kk.wv, kk.nv, sV0, kVRow, wave, lane16);
+    load_k<MT>(kk, 2, wave, l16, g4, kr[2]);
+    copy_rows<MT>(kk, 1, kk.ev, kk.wv, kk.nv, sV1, kVRow, wave, lane16);
+    load_k<MT>(kk, 3, wave, l16, g4, kr[3]);
+    copy_rows<MT>(kk, 2, kk.ev, kk.wv, kk.nv, sV2, kVRow, wave, lane16);
+    load_k<MT>(kk, 4, wave, l16, g4, kr[4]);
+    copy_rows<MT>(kk, 3, kk.ev, kk.wv, kk.nv, sV3, kVRow, wave, lane16);
+    load_k<MT>(kk, 5, wave, l16, g4, kr[5]);
+    copy_rows<MT>(kk, 4, kk.ev, kk.wv, kk.nv, sV4, kVRow, wave, lane16);
   };
   const int64_t t_raw = a.pos[b];
   const int64_t head0 = (int64_t)b * a.H + hg * 16 * NHB;
@@ -229,22 +278,40 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   bf16x8 qf[NHB][4];
   const uint16_t* const qrow = a.q + (head0 + l16) * kD + 128 * wave + 8 * g4;
 
-  // Positions below 2^31 (negative ones read as 0); wave-uniform.
+  // Positions below 2^31 (below 2^31 - 16 for MT; negative ones read as 0);
+  // wave-uniform.
+  constexpr int64_t kTMax = MT ? 0x7FFFFFEF : 0x7FFFFFFF;
   int64_t t64 = t_raw;
-  t64 = t64 < 0 ? 0 : (t64 > 0x7FFFFFFF ? 0x7FFFFFFF : t64);
+  t64 = t64 < 0 ? 0 : (t64 > kTMax ? kTMax : t64);
   const int t = __builtin_amdgcn_readfirstlane((int)t64);
   Keys ks;
-  ks.nc = (int)(((int64_t)t + 1) / kBlock);
+  ks.nc = (int)(((int64_t)t + (MT ? a.M : 1)) / kBlock);
   if ((int64_t)ks.nc > a.nc_cap) ks.nc = (int)a.nc_cap;  // out-of-contract: never read past the cache
   ks.lo = t - (kWindow - 1) > 0 ? t - (kWindow - 1) : 0;
-  ks.nw = t - ks.lo + 1;
+  ks.nw = MT ? t - ks.lo : t - ks.lo + 1;
   ks.n_et = (ks.nc + kTile - 1) / kTile;
-  ks.n_tiles = ks.n_et + (ks.nw + kTile - 1) / kTile;
+  ks.n_rt = (ks.nw + kTile - 1) / kTile;
+  ks.n_tiles = ks.n_et + ks.n_rt + (MT ? 1 : 0);
+  ks.M = a.M;
   ks.ek = a.ck + (int64_t)b * a.nc_cap * kD;
   ks.ev = a.cv + (int64_t)b * a.nc_cap * kD;
   ks.wk = a.wk + (int64_t)b * kWindow * kD;
   ks.wv = a.wv + (int64_t)b * kWindow * kD;
+  ks.nk = MT ? a.nk + (int64_t)b * a.M * kD : nullptr;
+  ks.nv = MT ? a.nv + (int64_t)b * a.M * kD : nullptr;
   const int n = ks.n_tiles;  // >= 1: the new token itself is always a key
+  // MT: the keys visible to the rows of head block `wave` (owner waves), whose
+  // token j sits at position t + j: entries below ncj, ring rows from rlo on,
+  // new rows up to j.
+  int tok = 0, ncj = 0, rlo = 0;
+  if constexpr (MT) {
+    tok = (hg * NHB + wave) / a.hpt;
+    tok = tok < a.M - 1 ? tok : a.M - 1;
+    ncj = (t + tok + 1) / kBlock;
+    ncj = ncj < ks.nc ? ncj : ks.nc;
+    rlo = t + tok - (kWindow - 1) - ks.lo;
+    rlo = rlo > 0 ? rlo : 0;
+  }
 
   // Lane offsets: V^T transpose read source (key row 4g4 + l16/4, dims 128w +
   // 4(l16&3)); the lane's slot of a weight buffer (8 bytes) and of a
@@ -276,19 +343,39 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   // and nothing is added.
   auto weights = [&](int j, const f32x4 (&sp)[4], uint8_t* sPn) {
     f32x4 s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-    const TileRef tr = tile_ref(ks, j);
-    const int valid = j < n ? tr.valid : 0;
     float mt = -INFINITY;
+    float mx = m;  // exponent reference
+    if constexpr (!MT) {
+      const TileRef tr = tile_ref(ks, j);
+      const int valid = j < n ? tr.valid : 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[r] = 4 * g4 + r < valid ? s[r] * a.c : -INFINITY;
-      mt = fmaxf(mt, s[r]);
+      for (int r = 0; r < 4; ++r) {
+        s[r] = 4 * g4 + r < valid ? s[r] * a.c : -INFINITY;
+        mt = fmaxf(mt, s[r]);
+      }
+      if (j == 0 && !fixed_m) m = xmax32(xmax16(mt));  // the reference: max of the first tile
+      mx = m;
+    } else {
+      // Visible keys of the tile for this block's token: indexes lo_v .. hi_v-1.
+      const TileRefMT tr = tile_ref_mt(ks, j);
+      const int lo_v = tr.kind == 1 ? rlo - tr.first : 0;
+      const int hi_v = j >= n ? 0 : (tr.kind == 0 ? ncj : (tr.kind == 1 ? ks.nw : tok + 1)) - tr.first;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = 4 * g4 + r;
+        s[r] = kk >= lo_v && kk < hi_v ? s[r] * a.c : -INFINITY;
+        mt = fmaxf(mt, s[r]);
+      }
+      // The reference: the maximum of the first tile with a visible key (a
+      // block's first tiles may hold none: entries of blocks completed by a
+      // later new token, ring rows left of its window).
+      if (!fixed_m && m == -INFINITY) m = xmax32(xmax16(mt));
+      mx = m == -INFINITY ? 0.0f : m;  // nothing visible yet: every weight 0
     }
-    if (j == 0 && !fixed_m) m = xmax32(xmax16(mt));  // the reference: max of the first tile
     mseen = fmaxf(mseen, mt);
     over |= mt > m + kHeadroom;
-    const f32x4 e = {__builtin_amdgcn_exp2f(s[0] - m), __builtin_amdgcn_exp2f(s[1] - m),
-                     __builtin_amdgcn_exp2f(s[2] - m), __builtin_amdgcn_exp2f(s[3] - m)};
+    const f32x4 e = {__builtin_amdgcn_exp2f(s[0] - mx), __builtin_amdgcn_exp2f(s[1] - mx),
+                     __builtin_amdgcn_exp2f(s[2] - mx), __builtin_amdgcn_exp2f(s[3] - mx)};
     const bf16x4 pb = __builtin_convertvector(e, bf16x4);  // nearest even
     // l adds the rounded weights: dot products with ones.
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -318,8 +405,8 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
       vf[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sVc + voff + 32 * db));
     __builtin_amdgcn_sched_barrier(0);
     scores(kc, sQn);  // tile s+2
-    load_k(ks, s + 6, w, l16, g4, kn);
-    copy_rows(ks, s + 5, ks.ev, ks.wv, sVd, kVRow, w, lane16);
+    load_k<MT>(ks, s + 6, w, l16, g4, kn);
+    copy_rows<MT>(ks, s + 5, ks.ev, ks.wv, ks.nv, sVd, kVRow, w, lane16);
     if (owner) weights(s + 1, sp, sPn);  // tile s+1
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
@@ -453,14 +540,55 @@ hipError_t launch_decode(const DecodeProblem& p, hipStream_t stream) {
   // Heads per workgroup: the most (16, 32 or 64) that still give at least
   // 256 workgroups, so each K/V byte is copied into as few CUs as the batch
   // allows while the chip stays full.
+  a.nk = nullptr;
+  a.nv = nullptr;
+  a.M = 1;
+  a.hpt = p.H / 16;
   int nhb = 4;
   while (nhb > 1 && ((int64_t)p.B * (p.H / 16 / nhb) < 256 || (p.H / 16) % nhb != 0)) nhb >>= 1;
   a.n_hg = p.H / 16 / nhb;
   const dim3 grid((unsigned)(((p.B + 7) / 8) * 8 * a.n_hg)), block(256);
   switch (nhb) {
-    case 4: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_multi(const DecodeProblem& p, const uint16_t* nk, const uint16_t* nv,
+                               int M, hipStream_t stream) {
+  if (p.B == 0) return hipSuccess;
+  Args a;
+  a.q = p.q;
+  a.g = p.g;
+  a.ck = p.ck;
+  a.cv = p.cv;
+  a.wk = p.wk;
+  a.wv = p.wv;
+  a.pos = p.pos;
+  a.out = p.out;
+  a.nc_cap = p.nc_cap;
+  a.B = p.B;
+  a.H = M * p.H;  // rows per sequence, token-major
+  a.c = p.scale * 1.4426950408889634f;
+  a.out_f32 = p.out_f32 ? 1 : 0;
+  a.nk = nk;
+  a.nv = nv;
+  a.M = M;
+  a.hpt = p.H / 16;
+  // Blocks of 16 rows per workgroup: the most (up to 4) that divide the M * H / 16
+  // blocks of a sequence and still give at least 256 workgroups.
+  const int blocks = M * p.H / 16;
+  int nhb = 4;
+  while (nhb > 1 && ((int64_t)p.B * (blocks / nhb) < 256 || blocks % nhb != 0)) --nhb;
+  a.n_hg = blocks / nhb;
+  const dim3 grid((unsigned)(((p.B + 7) / 8) * 8 * a.n_hg)), block(256);
+  switch (nhb) {
+    case 4: hipLaunchKernelGGL((decode_kernel<4, true>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<3, true>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<1, true>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }

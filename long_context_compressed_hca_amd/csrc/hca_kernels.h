@@ -47,5 +47,9 @@ struct DecodeProblem {
   bool out_f32;
 };
 hipError_t launch_decode(const DecodeProblem& p, hipStream_t stream);
+// M new tokens per sequence: q, g, out [B, M, H, 512]; the ring holds positions
+// below pos; nk, nv [B, M, 512] hold the new tokens' rows.
+hipError_t launch_decode_multi(const DecodeProblem& p, const uint16_t* nk, const uint16_t* nv,
+                               int M, hipStream_t stream);
 
 }  // namespace hca

@@ -21,7 +21,8 @@ Only integer arithmetic and one table lookup happen per element, so the host
 (numpy) and device (``synth_device.hip``) paths agree bit for bit; no libm
 call is involved in the per-element path.
 
-Tensor ids used by the HCA workloads: Q=0, K=1, V=2, G=3, CK=4, CV=5, WK=6, WV=7.
+Tensor ids used by the HCA workloads: Q=0, K=1, V=2, G=3, CK=4, CV=5, WK=6, WV=7,
+NK=8, NV=9 (the new rows of a multi-token decode).
 """
 from __future__ import annotations
 
@@ -37,7 +38,7 @@ M2 = 0x94D049BB133111EB
 MASK64 = (1 << 64) - 1
 TABLE_BITS = 20
 
-Q, K, V, G, CK, CV, WK, WV = range(8)
+Q, K, V, G, CK, CV, WK, WV, NK, NV = range(10)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 DEV_SRC = os.path.join(HERE, "synth_device.hip")

@@ -35,7 +35,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert {"hca_compress", "hca_attn_prefill", "hca_attn_decode"} <= set(names)
+    assert {"hca_compress", "hca_attn_prefill", "hca_attn_decode",
+            "hca_attn_decode_multi"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", hca.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -111,6 +112,31 @@ def test_decode_rejects(L, kw, status):
 
 def test_decode_noop(L):
     assert decode(L, B=0) == OK
+
+
+def decode_multi(L, **kw):
+    a = dict(q=P, g=P, ck=P, cv=P, nc_cap=256, wk=P, wv=P, nk=P, nv=P, pos=P, B=64, M=3, H=64,
+             D=512, block=128, window=128, scale=512 ** -0.5, out=P, dtype=0, stream=None)
+    a.update(kw)
+    return L.hca_attn_decode_multi(a["q"], a["g"], a["ck"], a["cv"], a["nc_cap"], a["wk"],
+                                   a["wv"], a["nk"], a["nv"], a["pos"], a["B"], a["M"], a["H"],
+                                   a["D"], a["block"], a["window"], a["scale"], a["out"],
+                                   a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=128), UNSUPPORTED), (dict(M=0), UNSUPPORTED), (dict(M=17), UNSUPPORTED),
+    (dict(H=8), UNSUPPORTED), (dict(H=24), UNSUPPORTED), (dict(M=16, H=80), UNSUPPORTED),
+    (dict(B=-1), INVALID), (dict(nc_cap=-1), INVALID), (dict(pos=0), INVALID),
+    (dict(pos=P + 4), INVALID), (dict(nk=0), INVALID), (dict(nv=MIS), INVALID),
+    (dict(ck=0), INVALID), (dict(scale=0.0), INVALID), (dict(dtype=2), INVALID),
+])
+def test_decode_multi_rejects(L, kw, status):
+    assert decode_multi(L, **kw) == status
+
+
+def test_decode_multi_noop(L):
+    assert decode_multi(L, B=0) == OK
 
 
 def compress(L, k=P, v=P, T=256, ld=512, D=512, block=128, ck=P, cv=P):
