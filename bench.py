@@ -14,6 +14,8 @@ Also reported:
                 rocprofv3 counters when they were taken on the current source;
   decode        batched decode (64 sequences, 256 entries + 128 window rows, 64
                 heads) in GB/s of compulsory HBM traffic, against 8 TB/s;
+  decode_multi  the same with 3 new tokens per sequence (the verify step of
+                two-token drafts);
   cpu_baseline  the fp64 oracle timed on a bounded sample of the same workload.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -174,18 +176,22 @@ def bench_prefill(args, torch, hca, synth):
                 prefill_ms=kernel_ms, tensors=(q, g, k, v, ck, cv, out))
 
 
-def bench_decode(args, torch, hca, synth):
-    """64 sequences, new token at position 32768: 256 entries + 128 window rows each."""
+def bench_decode(args, torch, hca, synth, M=1):
+    """64 sequences, new token at position 32768: 256 entries + 128 window rows each.
+    M > 1: M new tokens at 32768 .. 32768+M-1 (the verify step of (M-1)-token drafts);
+    each still sees 256 entries and 128 raw rows."""
     dev = torch.device("cuda:0")
     B, H, nc_cap, pos = 64, 64, 256, 32768
     reps = 6
     sets = []
+    qs = (B, H, D) if M == 1 else (B, M, H, D)
     for r in range(reps):
         gen = lambda tid, shape: synth.normal_bf16_device(40 + r, tid, shape, dev)
-        sets.append(dict(q=gen(synth.Q, (B, H, D)), g=gen(synth.G, (B, H, D)),
+        sets.append(dict(q=gen(synth.Q, qs), g=gen(synth.G, qs),
                          ck=gen(synth.CK, (B, nc_cap, D)), cv=gen(synth.CV, (B, nc_cap, D)),
                          wk=gen(synth.WK, (B, WINDOW, D)), wv=gen(synth.WV, (B, WINDOW, D)),
-                         out=torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)))
+                         nk=gen(synth.NK, (B, M, D)), nv=gen(synth.NV, (B, M, D)),
+                         out=torch.empty(qs, dtype=torch.bfloat16, device=dev)))
     posd = torch.full((B,), pos, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev)
     n = 240
@@ -193,7 +199,12 @@ def bench_decode(args, torch, hca, synth):
           for _ in range(n)]
 
     def call(s):
-        hca.hca_attn_decode(s["q"], s["g"], s["ck"], s["cv"], s["wk"], s["wv"], posd, s["out"])
+        if M == 1:
+            hca.hca_attn_decode(s["q"], s["g"], s["ck"], s["cv"], s["wk"], s["wv"], posd,
+                                s["out"])
+        else:
+            hca.hca_attn_decode_multi(s["q"], s["g"], s["ck"], s["cv"], s["wk"], s["wv"],
+                                      s["nk"], s["nv"], posd, s["out"])
 
     for i in range(24):
         call(sets[i % reps])
@@ -213,16 +224,23 @@ def bench_decode(args, torch, hca, synth):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     us_alone = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
-    n_keys = (pos + 1) // BLOCK + WINDOW
-    kv_bytes = B * n_keys * D * 2 * 2
-    qgo_bytes = 3 * B * H * D * 2
+    # Compulsory bytes: every distinct key row (the entries of the last token, the
+    # ring rows and the new rows) once, q, g and out once.
+    n_rows = (pos + M) // BLOCK + (pos + M - max(0, pos - WINDOW + 1))
+    kv_bytes = B * n_rows * D * 2 * 2
+    qgo_bytes = 3 * B * M * H * D * 2
     total = kv_bytes + qgo_bytes
     gbs = total / (us * 1e-6) / 1e9
+    flops = 4 * D * H * B * sum((pos + j + 1) // BLOCK + min(pos + j + 1, WINDOW)
+                                for j in range(M))
+    what = ("HCA batched decode: 64 sequences x (256 entries + 128 window rows), 64 heads, "
+            "dim 512, bf16") if M == 1 else (
+            f"HCA multi-token decode: 64 sequences x {M} new tokens (causal among "
+            "themselves), each seeing 256 entries + 128 raw rows, 64 heads, dim 512, bf16")
     return dict(metric="decode HBM GB/s", value=round(gbs, 1), unit="GB/s",
                 us_per_call=round(us, 2), us_per_call_alone=round(us_alone, 2),
-                bytes_per_call=total,
-                config={"workload": "HCA batched decode: 64 sequences x (256 entries + 128 "
-                        "window rows), 64 heads, dim 512, bf16", "input_replicas": reps},
+                bytes_per_call=total, tflops=round(flops / (us * 1e-6) / 1e12, 2),
+                config={"workload": what, "input_replicas": reps},
                 roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                           "traffic": None})
@@ -308,6 +326,7 @@ def main():
     }
     if not args.no_decode:
         rec["decode"] = bench_decode(args, torch, hca, synth)
+        rec["decode_multi"] = bench_decode(args, torch, hca, synth, M=3)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args, torch, synth, pf["tensors"])
     print(json.dumps(rec), flush=True)

@@ -577,11 +577,23 @@ hipError_t launch_decode_multi(const DecodeProblem& p, const uint16_t* nk, const
   a.nv = nv;
   a.M = M;
   a.hpt = p.H / 16;
-  // Blocks of 16 rows per workgroup: the most (up to 4) that divide the M * H / 16
-  // blocks of a sequence and still give at least 256 workgroups.
+  // Blocks of 16 rows per workgroup (1 .. 4, dividing the M * H / 16 blocks of a
+  // sequence).  A workgroup's time grows as about 4 + its block count (the key
+  // walk, plus the MFMA and softmax work of each block), and workgroups past
+  // one per CU run in further rounds: take the count with the least
+  // rounds * (4 + blocks), the larger count on a tie (fewer copies of K/V).
   const int blocks = M * p.H / 16;
-  int nhb = 4;
-  while (nhb > 1 && ((int64_t)p.B * (blocks / nhb) < 256 || blocks % nhb != 0)) --nhb;
+  int nhb = 1;
+  int64_t best = -1;
+  for (int c = 1; c <= 4; ++c) {
+    if (blocks % c != 0) continue;
+    const int64_t rounds = ((int64_t)p.B * (blocks / c) + 255) / 256;
+    const int64_t cost = rounds * (4 + c);
+    if (best < 0 || cost <= best) {
+      best = cost;
+      nhb = c;
+    }
+  }
   a.n_hg = blocks / nhb;
   const dim3 grid((unsigned)(((p.B + 7) / 8) * 8 * a.n_hg)), block(256);
   switch (nhb) {

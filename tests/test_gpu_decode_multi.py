@@ -58,15 +58,15 @@ def test_mixed_positions(M, H):
     compare(host_f64(d.run()), d.oracle(), f"decode_multi M={M} H={H}")
 
 
-@pytest.mark.parametrize("B", [48, 64, 96])
-def test_batch_sizes(B):
-    # M = 3, H = 64: 12 blocks of 16 rows per sequence; 48, 64 and 96 sequences
-    # take 2, 3 and 4 blocks per workgroup
-    rng = np.random.default_rng(B)
+@pytest.mark.parametrize("B,M", [(16, 3), (64, 2), (64, 3), (64, 4)])
+def test_batch_sizes(B, M):
+    # H = 64: 4M blocks of 16 rows per sequence; these batches take 1, 2, 3 and
+    # 4 blocks per workgroup
+    rng = np.random.default_rng(B + M)
     positions = rng.integers(0, 3000, size=B)
     positions[:5] = [0, 126, 127, 128, 2999]
-    d = DecodeMulti(seed=30 + B, positions=positions, M=3, out_dtype="f32")
-    compare(host_f64(d.run()), d.oracle(), f"decode_multi B={B}")
+    d = DecodeMulti(seed=30 + B + M, positions=positions, M=M, out_dtype="f32")
+    compare(host_f64(d.run()), d.oracle(), f"decode_multi B={B} M={M}")
 
 
 def test_one_token_equals_decode():
