@@ -173,3 +173,33 @@ def decode_multi(q, g, ck, cv, wk, wv, nk, nv, pos, *, block=128, window=128, sc
         out[b] = attn(q[b], g[b], t + np.arange(M), k, v, lo, ck[b, :nc], cv[b, :nc],
                       block=block, window=window, scale=scale, nthreads=nthreads)
     return out
+
+
+def vha(x, up, down) -> np.ndarray:
+    """Virtual head attention: after attention, a low-rank mix across heads with an
+    identity skip (blog.derekhsu.net, section 潛在閘控稀疏注意力, the VHA item).
+    For every position t and dim d the head vector x[t, :, d] becomes
+        y[t, h, d] = x[t, h, d] + sum_k up[h, k] * z[t, k, d],
+        z[t, k, d] = sum_h' down[k, h'] * x[t, h', d],
+    i.e. y = (I + up @ down) x over the heads, the same mix for every dim.
+      x     [T, H, D]  float64 (the gated attention output)
+      up    [H, r]     bfloat16 bits
+      down  [r, H]     bfloat16 bits
+    Returns float64 [T, H, D]."""
+    x = np.asarray(x, dtype=np.float64)
+    U, W = _widen_array(up), _widen_array(down)
+    T, H, D = x.shape
+    assert U.shape[0] == H and W.shape == (U.shape[1], H)
+    z = np.einsum("kh,thd->tkd", W, x)
+    return x + np.einsum("hk,tkd->thd", U, z)
+
+
+def _widen_array(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64, exactly (the bits are the top half of a float32)."""
+    b = _u16(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def attn_vha(q, g, tpos, k, v, kv_start, ck, cv, up, down, **kw) -> np.ndarray:
+    """HCA attention rows (``attn``), gated, then the VHA head mix (``vha``)."""
+    return vha(attn(q, g, tpos, k, v, kv_start, ck, cv, **kw), up, down)
