@@ -110,6 +110,27 @@ hca_status_t hca_attn_prefill(const void* q, const void* g, const void* k, const
                               void* stream);
 
 /*
+ * Prefill attention followed by the VHA head mix (virtual head attention:
+ * blog.derekhsu.net, section 潛在閘控稀疏注意力, the VHA item: after attention a
+ * light low-rank mix across heads with an identity skip, fused into the attention
+ * kernel at inference).  With x[t, h, :] the gated output of hca_attn_prefill,
+ *   out[t, h, :] = x[t, h, :] + sum_k up[h, k] * sum_h' down[k, h'] * x[t, h', :]
+ * i.e. out = (I + up @ down) x over the heads of each query, the same for every dim.
+ *   vha_up    device, bf16 [H, vha_rank]
+ *   vha_down  device, bf16 [vha_rank, H]
+ * Other arguments and requirements as for hca_attn_prefill, and: H = 64, vha_rank a
+ * multiple of 4 from 4 to 32 (else HCA_ERR_UNSUPPORTED).  In the kernel the mix
+ * takes x rounded to bf16, and sum_h' down x rounded to bf16, as its operands,
+ * with fp32 accumulation and the identity term kept in fp32.
+ */
+hca_status_t hca_attn_prefill_vha(const void* q, const void* g, const void* k, const void* v,
+                                  const void* ck, const void* cv, int64_t Tq, int64_t q_start,
+                                  int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D,
+                                  int block, int window, float scale, const void* vha_up,
+                                  const void* vha_down, int vha_rank, void* out,
+                                  hca_dtype_t out_dtype, void* stream);
+
+/*
  * Decode attention: one new query per sequence, for B sequences at once.
  *   q, g     device, bf16 [B, H, D]          the new token's queries and gate logits
  *   ck, cv   device, bf16 [B, nc_cap, D]     per-sequence entries (only the first

@@ -50,6 +50,9 @@ def lib():
         L.hca_attn_decode_multi.argtypes = [P, P, P, P, I64, P, P, P, P, P, I, I, I, I, I, I, F,
                                             P, I, P]
         L.hca_attn_decode_multi.restype = I
+        L.hca_attn_prefill_vha.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I,
+                                           F, P, P, I, P, I, P]
+        L.hca_attn_prefill_vha.restype = I
         _lib = L
     return _lib
 
@@ -155,5 +158,32 @@ def hca_attn_decode_multi(q, g, ck, cv, wk, wv, nk, nv, pos, out, *, scale: floa
         ck.shape[1], _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
         _dev_ptr(nk, "nk", torch.bfloat16), _dev_ptr(nv, "nv", torch.bfloat16),
         _dev_ptr(pos, "pos", torch.int64), B, M, H, Dd, block, window, float(scale),
+        _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
+        _stream(q.device)))
+
+
+def hca_attn_prefill_vha(q, g, k, v, ck, cv, up, down, out, *, q_start: int = 0,
+                         kv_start: int = 0, scale: float | None = None, block: int = BLOCK,
+                         window: int = WINDOW):
+    """hca_attn_prefill followed by the VHA head mix out = (I + up @ down) x over the 64
+    heads of each query; up [64, r], down [r, 64] bf16 on the GPU, r in 4, 8, .., 32."""
+    import torch
+    Tq, H, Dd = q.shape
+    if g.shape != q.shape or out.shape != q.shape:
+        raise ValueError("q, g and out must have the same shape")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    r = up.shape[1]
+    if up.shape != (H, r) or down.shape != (r, H):
+        raise ValueError("up must be [H, r] and down [r, H]")
+    nc = 0 if ck is None else ck.shape[0]
+    if scale is None:
+        scale = Dd ** -0.5
+    _check(lib().hca_attn_prefill_vha(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
+        _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+        _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
+        Tq, q_start, k.shape[0], kv_start, nc, H, Dd, block, window, float(scale),
+        _dev_ptr(up, "up", torch.bfloat16), _dev_ptr(down, "down", torch.bfloat16), r,
         _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
         _stream(q.device)))

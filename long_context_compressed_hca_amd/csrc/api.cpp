@@ -111,13 +111,20 @@ hca_status_t hca_compress(const void* k, const void* v, int64_t T, int64_t ld, i
                     "hca_compress launch");
 }
 
-hca_status_t hca_attn_prefill(const void* q, const void* g, const void* k, const void* v,
-                              const void* ck, const void* cv, int64_t Tq, int64_t q_start,
-                              int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D, int block,
-                              int window, float scale, void* out, hca_dtype_t out_dtype,
-                              void* stream) {
+// Prefill with an optional VHA head mix (vha_rank 0: none).
+static hca_status_t prefill_impl(const void* q, const void* g, const void* k, const void* v,
+                                 const void* ck, const void* cv, int64_t Tq, int64_t q_start,
+                                 int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D,
+                                 int block, int window, float scale, const void* vha_up,
+                                 const void* vha_down, int vha_rank, void* out,
+                                 hca_dtype_t out_dtype, void* stream, const char* what) {
   TRY(check_shape(D, block, window));
   if (H < 1 || H > 64) return fail(HCA_ERR_UNSUPPORTED, "H = %d (need 1 <= H <= 64)", H);
+  if (vha_rank != 0) {
+    if (H != 64) return fail(HCA_ERR_UNSUPPORTED, "VHA needs H = 64 (got %d)", H);
+    if (vha_rank < 4 || vha_rank > 32 || vha_rank % 4 != 0)
+      return fail(HCA_ERR_UNSUPPORTED, "VHA rank %d (need a multiple of 4, 4 .. 32)", vha_rank);
+  }
   if (Tq < 0 || q_start < 0 || Tkv < 0 || kv_start < 0 || Nc < 0)
     return fail(HCA_ERR_INVALID_ARG, "negative size or position");
   if (out_dtype != HCA_BF16 && out_dtype != HCA_F32)
@@ -148,6 +155,10 @@ hca_status_t hca_attn_prefill(const void* q, const void* g, const void* k, const
     TRY(check_ptr(ck, "ck"));
     TRY(check_ptr(cv, "cv"));
   }
+  if (vha_rank != 0) {
+    TRY(check_ptr(vha_up, "vha_up"));
+    TRY(check_ptr(vha_down, "vha_down"));
+  }
   hca::PrefillProblem p;
   p.q = static_cast<const uint16_t*>(q);
   p.g = static_cast<const uint16_t*>(g);
@@ -164,8 +175,32 @@ hca_status_t hca_attn_prefill(const void* q, const void* g, const void* k, const
   p.H = H;
   p.scale = scale;
   p.out_f32 = out_dtype == HCA_F32;
-  return hip_status(hca::launch_prefill(p, static_cast<hipStream_t>(stream)),
-                    "hca_attn_prefill launch");
+  p.vha_up = static_cast<const uint16_t*>(vha_up);
+  p.vha_down = static_cast<const uint16_t*>(vha_down);
+  p.vha_rank = vha_rank;
+  return hip_status(hca::launch_prefill(p, static_cast<hipStream_t>(stream)), what);
+}
+
+hca_status_t hca_attn_prefill(const void* q, const void* g, const void* k, const void* v,
+                              const void* ck, const void* cv, int64_t Tq, int64_t q_start,
+                              int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D, int block,
+                              int window, float scale, void* out, hca_dtype_t out_dtype,
+                              void* stream) {
+  return prefill_impl(q, g, k, v, ck, cv, Tq, q_start, Tkv, kv_start, Nc, H, D, block, window,
+                      scale, nullptr, nullptr, 0, out, out_dtype, stream,
+                      "hca_attn_prefill launch");
+}
+
+hca_status_t hca_attn_prefill_vha(const void* q, const void* g, const void* k, const void* v,
+                                  const void* ck, const void* cv, int64_t Tq, int64_t q_start,
+                                  int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D,
+                                  int block, int window, float scale, const void* vha_up,
+                                  const void* vha_down, int vha_rank, void* out,
+                                  hca_dtype_t out_dtype, void* stream) {
+  if (vha_rank == 0) return fail(HCA_ERR_UNSUPPORTED, "VHA rank 0 (use hca_attn_prefill)");
+  return prefill_impl(q, g, k, v, ck, cv, Tq, q_start, Tkv, kv_start, Nc, H, D, block, window,
+                      scale, vha_up, vha_down, vha_rank, out, out_dtype, stream,
+                      "hca_attn_prefill_vha launch");
 }
 
 hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const void* cv,

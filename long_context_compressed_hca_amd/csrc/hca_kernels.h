@@ -29,6 +29,10 @@ struct PrefillProblem {
   int H;
   float scale;
   bool out_f32;
+  // VHA head mix after the gate (vha_rank 0: none): up [H, rank], down [rank, H].
+  const uint16_t* vha_up = nullptr;
+  const uint16_t* vha_down = nullptr;
+  int vha_rank = 0;
 };
 hipError_t launch_prefill(const PrefillProblem& p, hipStream_t stream);
 

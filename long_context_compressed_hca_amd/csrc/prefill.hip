@@ -95,6 +95,10 @@ struct Args {
   int h_shift;                // log2(H) when H is a power of two, else -1
   float c;  // scale * log2(e)
   int out_f32;
+  // VHA head mix (H = 64): up [64, rank], down [rank, 64], rank a multiple of 4 <= 32.
+  const uint16_t* vha_up;
+  const uint16_t* vha_down;
+  int vha_rank;
 };
 
 // Row -> query index (row / H), a shift when H is a power of two.
@@ -678,7 +682,159 @@ __device__ __forceinline__ void store_rb(const Args& a, const Item& it, int rb,
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// ---------------------------------------------------------------- VHA epilogue
+// With the head mix (H = 64, so an item is two whole queries: row blocks 0, 1
+// are the 64 heads of its first query, 2, 3 those of its second), every wave
+// holds all heads of both queries for its 128 dims, and the mix of a query is
+// two small products per 32-dim block bb:
+//   Z^T[r][dim]  = Down[r][heads] . X[heads][dim]      (M = r padded to 32, K = 64 heads)
+//   Y^T[dim][h] += Z[dim][r] . Up^T[r][h]              (M = 32 dims, K = 32, into O^T)
+// X is the gated output, rounded to bf16, read back transposed from the rows
+// gate_rb_vha wrote into the row blocks' regions; O^T holds the gated output
+// in fp32 and takes the product as its accumulator (the identity skip).
+// The k index of both products runs in the order the registers give:
+// k-slot 8g + j (lane half g = lane / 32) is head / rank index
+// 16s + 4g + j for j < 4 and 16s + 8 + 4g + (j - 4) for j >= 4, in K-step s.
+
+// Gate row block rb as gate_rb does, keep the gated values in O^T (fp32)
+// and write them, rounded to bf16, over the logits in the region.
+__device__ __forceinline__ void gate_rb_vha(WaveState& st, int rb, uint8_t* region,
+                                            const float* sL, int lane) {
+  asm volatile("" : "+v"(lane));
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int l32 = lane & 31, g = lane >> 5;
+  const float l = sL[32 * rb + l32];
+  uint8_t* row = region + l32 * 256 + 8 * g;
+  uint2 gw[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)  // j = 4 bb + q: dims 32bb + 8q + 4g .. +3
+    gw[j] = *reinterpret_cast<const uint2*>(row + ((j ^ (l32 & 15)) << 4));
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int bb = j >> 2, q = j & 3;
+    const float gv[4] = {bf16_bits_to_f32(gw[j].x & 0xFFFFu), bf16_bits_to_f32(gw[j].x >> 16),
+                         bf16_bits_to_f32(gw[j].y & 0xFFFFu), bf16_bits_to_f32(gw[j].y >> 16)};
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float den = __builtin_fmaf(l, __builtin_amdgcn_exp2f(-gv[e] * kLog2e), l);
+      o[e] = st.o[4 * bb + rb][4 * q + e] * __builtin_amdgcn_rcpf(den);
+      st.o[4 * bb + rb][4 * q + e] = o[e];
+    }
+    const bf16x2 lo = __builtin_convertvector((f32x2){o[0], o[1]}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector((f32x2){o[2], o[3]}, bf16x2);
+    const u32x2 w2 = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    const uint32_t addr = (uint32_t)(uintptr_t)(row + ((j ^ (l32 & 15)) << 4));
+    asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(w2) : "memory");
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// X fragment (B operand of Z^T = Down X) of K-step s for dim block bb, from
+// the region of heads 32(s/2) ..: transpose reads, in each 16-lane group source
+// lane s16 addressing region row 16(s&1) + 4(lane/32) + s16/4 (+ 8 for the
+// second read) at dims 32bb + 16((lane/16)&1) + 4(s16&3), through the
+// region's 16-byte chunk swizzle (chunk ^ (row & 15)).  Result lane: dim
+// 32bb + lane%32, heads of k-slots 8g .. 8g+7.
+__device__ __forceinline__ bf16x8 vha_x_frag(const uint8_t* region, int s, int bb, int lane) {
+  const int s16 = lane & 15;
+  const int d = 32 * bb + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+  const int r0 = 16 * (s & 1) + 4 * (lane >> 5) + (s16 >> 2);
+  const int r1 = r0 + 8;
+  const uint8_t* p0 = region + r0 * 256 + (((d >> 3) ^ (r0 & 15)) << 4) + 2 * (d & 7);
+  const uint8_t* p1 = region + r1 * 256 + (((d >> 3) ^ (r1 & 15)) << 4) + 2 * (d & 7);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+  const i16x8 w8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w8);
+}
+
+// 16 bytes at two 8-byte halves of a buffer (offsets past its size read 0).
+__device__ __forceinline__ bf16x8 load_2x8(__amdgpu_buffer_rsrc_t rs, int off_lo, int off_hi) {
+  const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off_lo, 0, 0));
+  const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off_hi, 0, 0));
+  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// The head mix of query qq of the item (row blocks 2qq, 2qq+1, gated by
+// gate_rb_vha into regions rlo, rhi).  The result replaces the gated output in
+// O^T; bf16 output is written back into the regions for store_rb, f32 output
+// is stored from registers.
 template <bool kF32>
+__device__ __forceinline__ void vha_query(const Args& a, WaveState& st, const Item& it, int qq,
+                                          uint8_t* rlo, uint8_t* rhi, int lane, int wave) {
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, g = lane >> 5;
+  const int rank = a.vha_rank;
+  // Down rows r >= rank lie past the buffer and read as zeros.
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.vha_down, rank * 64 * 2);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.vha_up, 64 * rank * 2);
+  bf16x8 dn[4];  // A operand of Z^T: lane (r = l32, g), heads of K-step s
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int off = (l32 * 64 + 16 * s + 4 * g) * 2;
+    dn[s] = load_2x8(rd, off, off + 16);
+  }
+  bf16x8 up[2][2];  // B operand of the mix: lane (head 32p + l32, g), r of K-step s2
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int r0 = 16 * s2 + 4 * g, r1 = r0 + 8;  // rank is a multiple of 4
+      const int base = (32 * p + l32) * rank;
+      up[p][s2] = load_2x8(ru, r0 < rank ? (base + r0) * 2 : 0x40000000,
+                           r1 < rank ? (base + r1) * 2 : 0x40000000);
+    }
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    __builtin_amdgcn_sched_barrier(0);  // one dim block at a time (register pressure)
+    f32x16 z = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dn[s], vha_x_frag(s < 2 ? rlo : rhi, s, bb, lane),
+                                                  z, 0, 0, 0);
+    // z: lane (dim 32bb + l32, g), register i = r 8(i/4) + 4g + i%4, so
+    // registers 8s2 .. 8s2+7 are the k-slots of K-step s2 in the order above.
+    bf16x8 za[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) za[s2][j] = (__bf16)z[8 * s2 + j];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        st.o[4 * bb + 2 * qq + p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            za[s2], up[p][s2], st.o[4 * bb + 2 * qq + p], 0, 0, 0);
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int rb = 2 * qq + p;
+    uint8_t* row = (p ? rhi : rlo) + l32 * 256 + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int bb = j >> 2, q = j & 3;
+      const f32x4 o = {st.o[4 * bb + rb][4 * q], st.o[4 * bb + rb][4 * q + 1],
+                       st.o[4 * bb + rb][4 * q + 2], st.o[4 * bb + rb][4 * q + 3]};
+      if (kF32) {
+        if (it.row0 + 32 * rb + l32 <= it.last)
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) +
+                                     (size_t)(it.row0 + 32 * rb + l32) * kD + 128 * wave +
+                                     32 * bb + 8 * q + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        const bf16x2 lo = __builtin_convertvector((f32x2){o[0], o[1]}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2){o[2], o[3]}, bf16x2);
+        const u32x2 w2 = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        const uint32_t addr = (uint32_t)(uintptr_t)(row + ((j ^ (l32 & 15)) << 4));
+        asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(w2) : "memory");
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool kF32, bool kVha>
 __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
   // Separate arrays per stage: the compiler then knows a copy into one stage
   // cannot alias reads of another and inserts no wait between them.
@@ -876,14 +1032,28 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) dma_rows(g1, jj, 256 * wave, sK1 + greg, ln);
     }
-    gate_rb<kF32>(a, st, it, 2, sV0 + greg, sL, lane, wave);
-    if (!kF32) store_rb(a, it, 2, sV0 + greg, lane, wave);
-    gate_rb<kF32>(a, st, it, 3, sV1 + greg, sL, lane, wave);
-    if (!kF32) store_rb(a, it, 3, sV1 + greg, lane, wave);
-    gate_rb<kF32>(a, st, it, 0, sK0 + greg, sL, lane, wave);
-    if (!kF32) store_rb(a, it, 0, sK0 + greg, lane, wave);
-    gate_rb<kF32>(a, st, it, 1, sK1 + greg, sL, lane, wave);
-    if (!kF32) store_rb(a, it, 1, sK1 + greg, lane, wave);
+    if constexpr (!kVha) {
+      gate_rb<kF32>(a, st, it, 2, sV0 + greg, sL, lane, wave);
+      if (!kF32) store_rb(a, it, 2, sV0 + greg, lane, wave);
+      gate_rb<kF32>(a, st, it, 3, sV1 + greg, sL, lane, wave);
+      if (!kF32) store_rb(a, it, 3, sV1 + greg, lane, wave);
+      gate_rb<kF32>(a, st, it, 0, sK0 + greg, sL, lane, wave);
+      if (!kF32) store_rb(a, it, 0, sK0 + greg, lane, wave);
+      gate_rb<kF32>(a, st, it, 1, sK1 + greg, sL, lane, wave);
+      if (!kF32) store_rb(a, it, 1, sK1 + greg, lane, wave);
+    } else {
+      // The item's second query (row blocks 2, 3) first: its logits are in.
+      gate_rb_vha(st, 2, sV0 + greg, sL, lane);
+      gate_rb_vha(st, 3, sV1 + greg, sL, lane);
+      vha_query<kF32>(a, st, it, 1, sV0 + greg, sV1 + greg, lane, wave);
+      if (!kF32) store_rb(a, it, 2, sV0 + greg, lane, wave);
+      if (!kF32) store_rb(a, it, 3, sV1 + greg, lane, wave);
+      gate_rb_vha(st, 0, sK0 + greg, sL, lane);
+      gate_rb_vha(st, 1, sK1 + greg, sL, lane);
+      vha_query<kF32>(a, st, it, 0, sK0 + greg, sK1 + greg, lane, wave);
+      if (!kF32) store_rb(a, it, 0, sK0 + greg, lane, wave);
+      if (!kF32) store_rb(a, it, 1, sK1 + greg, lane, wave);
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the K stages are done
     barrier_no_fence();                  // everyone's
     if (more) first_k_copies(nx);
@@ -913,6 +1083,9 @@ hipError_t launch_prefill(const PrefillProblem& p, hipStream_t stream) {
   a.h_shift = (p.H & (p.H - 1)) == 0 ? __builtin_ctz((unsigned)p.H) : -1;
   a.c = p.scale * 1.4426950408889634f;
   a.out_f32 = p.out_f32 ? 1 : 0;
+  a.vha_up = p.vha_up;
+  a.vha_down = p.vha_down;
+  a.vha_rank = p.vha_rank;
   a.n_items = (a.rows + kRowsPerItem - 1) / kRowsPerItem;
   if (a.n_items == 0) return hipSuccess;
   int dev = 0;
@@ -932,10 +1105,18 @@ hipError_t launch_prefill(const PrefillProblem& p, hipStream_t stream) {
   const int need = (a.n_items + 7) / 8;
   if (per_xcd > need) per_xcd = need;
   a.per_xcd = per_xcd;
-  if (a.out_f32)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(8 * per_xcd), dim3(256), 0, stream, a);
+  // The head mix needs whole queries per item: H = 64 (checked on the host).
+  const bool vha = p.vha_rank > 0;
+  if (vha && p.H != 64) return hipErrorInvalidValue;
+  const dim3 grid(8 * per_xcd), block(256);
+  if (a.out_f32 && vha)
+    hipLaunchKernelGGL((prefill_kernel<true, true>), grid, block, 0, stream, a);
+  else if (a.out_f32)
+    hipLaunchKernelGGL((prefill_kernel<true, false>), grid, block, 0, stream, a);
+  else if (vha)
+    hipLaunchKernelGGL((prefill_kernel<false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(8 * per_xcd), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"hca_compress", "hca_attn_prefill", "hca_attn_decode",
-            "hca_attn_decode_multi"} <= set(names)
+            "hca_attn_decode_multi", "hca_attn_prefill_vha"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", hca.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -89,6 +89,31 @@ def test_prefill_noop_and_optional_entries(L):
     # rejected here for another reason: the output pointer is misaligned)
     assert prefill(L, Tq=100, Tkv=100, Nc=0, ck=0, cv=0, out=MIS) == INVALID
     assert b"out" in L.hca_last_error()
+
+
+def prefill_vha(L, **kw):
+    a = dict(q=P, g=P, k=P, v=P, ck=P, cv=P, Tq=256, q_start=0, Tkv=256, kv_start=0, Nc=2, H=64,
+             D=512, block=128, window=128, scale=512 ** -0.5, up=P, down=P, rank=8, out=P,
+             dtype=0, stream=None)
+    a.update(kw)
+    return L.hca_attn_prefill_vha(a["q"], a["g"], a["k"], a["v"], a["ck"], a["cv"], a["Tq"],
+                                  a["q_start"], a["Tkv"], a["kv_start"], a["Nc"], a["H"], a["D"],
+                                  a["block"], a["window"], a["scale"], a["up"], a["down"],
+                                  a["rank"], a["out"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=32), UNSUPPORTED), (dict(rank=0), UNSUPPORTED), (dict(rank=6), UNSUPPORTED),
+    (dict(rank=36), UNSUPPORTED), (dict(rank=-4), UNSUPPORTED), (dict(up=0), INVALID),
+    (dict(down=MIS), INVALID), (dict(Nc=1), INVALID), (dict(q=0), INVALID),
+    (dict(D=256), UNSUPPORTED),
+])
+def test_prefill_vha_rejects(L, kw, status):
+    assert prefill_vha(L, **kw) == status
+
+
+def test_prefill_vha_noop(L):
+    assert prefill_vha(L, Tq=0, q=0, out=0, up=0, down=0) == OK
 
 
 def decode(L, **kw):
