@@ -16,6 +16,8 @@ Also reported:
                 heads) in GB/s of compulsory HBM traffic, against 8 TB/s;
   decode_multi  the same with 3 new tokens per sequence (the verify step of
                 two-token drafts);
+  prefill_vha   the prefill launch with the VHA head mix fused into its
+                epilogue, beside the plain launch;
   cpu_baseline  the fp64 oracle timed on a bounded sample of the same workload.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -176,6 +178,34 @@ def bench_prefill(args, torch, hca, synth):
                 prefill_ms=kernel_ms, tensors=(q, g, k, v, ck, cv, out))
 
 
+def bench_prefill_vha(args, torch, hca, synth, tensors, rank=16):
+    """The prefill launch of the step with the VHA head mix fused (rank 16, factors
+    N(0,1)/8), timed like the plain launch; reported beside it, not part of the step."""
+    dev = torch.device("cuda:0")
+    q, g, k, v, ck, cv, out = tensors
+    H = q.shape[1]
+    up = (synth.normal_bf16_device(9, synth.CK, (H, rank), dev) * 0.125).contiguous()
+    down = (synth.normal_bf16_device(9, synth.CV, (rank, H), dev) * 0.125).contiguous()
+    stream = torch.cuda.current_stream(dev)
+    n = max(3, args.steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    hca.hca_attn_prefill_vha(q, g, k, v, ck, cv, up, down, out)
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record(stream)
+        hca.hca_attn_prefill_vha(q, g, k, v, ck, cv, up, down, out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    T = q.shape[0]
+    mix_flops = 2 * 2 * T * H * rank * D  # down and up products, every dim
+    return {"launch_ms": round(ms, 4), "rank": rank,
+            "tflops_attention": round(prefill_flops(T, H) / (ms * 1e-3) / 1e12, 2),
+            "mix_gflop": round(mix_flops / 1e9, 1),
+            "workload": f"the 128K prefill launch with the VHA head mix fused (rank {rank})"}
+
+
 def bench_decode(args, torch, hca, synth, M=1):
     """64 sequences, new token at position 32768: 256 entries + 128 window rows each.
     M > 1: M new tokens at 32768 .. 32768+M-1 (the verify step of (M-1)-token drafts);
@@ -324,6 +354,9 @@ def main():
                      "kernel": "hca prefill_kernel", "flops_per_launch": pf["flops"],
                      "launch_ms": round(pf["prefill_ms"], 4)},
     }
+    rec["prefill_vha"] = bench_prefill_vha(args, torch, hca, synth, pf["tensors"])
+    rec["prefill_vha"]["overhead_vs_plain"] = round(
+        rec["prefill_vha"]["launch_ms"] / pf["prefill_ms"] - 1, 4)
     if not args.no_decode:
         rec["decode"] = bench_decode(args, torch, hca, synth)
         rec["decode_multi"] = bench_decode(args, torch, hca, synth, M=3)

@@ -749,6 +749,21 @@ __device__ __forceinline__ bf16x8 vha_x_frag(const uint8_t* region, int s, int b
   return __builtin_bit_cast(bf16x8, w8);
 }
 
+// The down product's MFMAs: the score chain's VGPR-accumulator forms with
+// the 2 wait states a VALU write of an operand needs in front (the compiler
+// may pass a fragment through accumulator registers right before the MFMA).
+__device__ __forceinline__ void mfma_z_zero(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_z_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_z_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 3"
+               : "+v"(d)
+               : "v"(a), "v"(b));
+}
+
 // 16 bytes at two 8-byte halves of a buffer (offsets past its size read 0).
 __device__ __forceinline__ bf16x8 load_2x8(__amdgpu_buffer_rsrc_t rs, int off_lo, int off_hi) {
   const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off_lo, 0, 0));
@@ -757,43 +772,63 @@ __device__ __forceinline__ bf16x8 load_2x8(__amdgpu_buffer_rsrc_t rs, int off_lo
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// The head mix of query qq of the item (row blocks 2qq, 2qq+1, gated by
-// gate_rb_vha into regions rlo, rhi).  The result replaces the gated output in
-// O^T; bf16 output is written back into the regions for store_rb, f32 output
-// is stored from registers.
-template <bool kF32>
-__device__ __forceinline__ void vha_query(const Args& a, WaveState& st, const Item& it, int qq,
-                                          uint8_t* rlo, uint8_t* rhi, int lane, int wave) {
+// The factor fragments of the mix (the same for every query and wave):
+//   dn[s]      A operand of Z^T: lane (r = l32, g), the heads of K-step s;
+//   up[p][s2]  B operand of the mix: lane (head 32p + l32, g), the r of K-step s2.
+struct VhaFrags {
+  bf16x8 dn[4];
+  bf16x8 up[2][2];
+};
+__device__ __forceinline__ void load_vha_frags(const Args& a, VhaFrags& f, int lane) {
   asm volatile("" : "+v"(lane));
   const int l32 = lane & 31, g = lane >> 5;
   const int rank = a.vha_rank;
   // Down rows r >= rank lie past the buffer and read as zeros.
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.vha_down, rank * 64 * 2);
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.vha_up, 64 * rank * 2);
-  bf16x8 dn[4];  // A operand of Z^T: lane (r = l32, g), heads of K-step s
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int off = (l32 * 64 + 16 * s + 4 * g) * 2;
-    dn[s] = load_2x8(rd, off, off + 16);
+    f.dn[s] = load_2x8(rd, off, off + 16);
   }
-  bf16x8 up[2][2];  // B operand of the mix: lane (head 32p + l32, g), r of K-step s2
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int r0 = 16 * s2 + 4 * g, r1 = r0 + 8;  // rank is a multiple of 4
       const int base = (32 * p + l32) * rank;
-      up[p][s2] = load_2x8(ru, r0 < rank ? (base + r0) * 2 : 0x40000000,
-                           r1 < rank ? (base + r1) * 2 : 0x40000000);
+      f.up[p][s2] = load_2x8(ru, r0 < rank ? (base + r0) * 2 : 0x40000000,
+                             r1 < rank ? (base + r1) * 2 : 0x40000000);
     }
+}
+
+// The head mix of query qq of the item (row blocks 2qq, 2qq+1, gated by
+// gate_rb_vha into regions rlo, rhi).  The result replaces the gated output in
+// O^T; bf16 output is written back into the regions for store_rb, f32 output
+// is stored from registers.
+// The factor fragments are loaded here, per query: kept live across the
+// gating of the item's other query they take registers the allocator then
+// finds by moving O blocks to scratch.
+template <bool kF32>
+__device__ __forceinline__ void vha_query(const Args& a, WaveState& st, const Item& it, int qq,
+                                          uint8_t* rlo, uint8_t* rhi, int lane, int wave) {
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, g = lane >> 5;
+  VhaFrags f;
+  load_vha_frags(a, f, lane);
+  const bf16x8 (&dn)[4] = f.dn;
+  const bf16x8 (&up)[2][2] = f.up;
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
     __builtin_amdgcn_sched_barrier(0);  // one dim block at a time (register pressure)
-    f32x16 z = {};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dn[s], vha_x_frag(s < 2 ? rlo : rhi, s, bb, lane),
-                                                  z, 0, 0, 0);
+    // Z^T in VGPRs (with the builtin the allocator takes accumulator
+    // registers for it and moves O blocks out of them); the last MFMA carries
+    // the wait states of the VALU reads below.
+    f32x16 z;
+    mfma_z_zero(z, dn[0], vha_x_frag(rlo, 0, bb, lane));
+    mfma_z_acc(z, dn[1], vha_x_frag(rlo, 1, bb, lane));
+    mfma_z_acc(z, dn[2], vha_x_frag(rhi, 2, bb, lane));
+    mfma_z_last(z, dn[3], vha_x_frag(rhi, 3, bb, lane));
     // z: lane (dim 32bb + l32, g), register i = r 8(i/4) + 4g + i%4, so
     // registers 8s2 .. 8s2+7 are the k-slots of K-step s2 in the order above.
     bf16x8 za[2];
@@ -801,13 +836,19 @@ __device__ __forceinline__ void vha_query(const Args& a, WaveState& st, const It
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int j = 0; j < 8; ++j) za[s2][j] = (__bf16)z[8 * s2 + j];
+    // Into the O^T block in its accumulator registers.  The s_nop gives the 2
+    // wait states a VALU write of za (and of the block, in gate_rb_vha) needs
+    // before an MFMA reads it.
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        st.o[4 * bb + 2 * qq + p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            za[s2], up[p][s2], st.o[4 * bb + 2 * qq + p], 0, 0, 0);
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+a"(st.o[4 * bb + 2 * qq + p])
+                     : "v"(za[s2]), "v"(up[p][s2]));
   }
+  // The wait states a VALU read of the last blocks written needs.
+  asm volatile("s_nop 15\n\ts_nop 3");
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int rb = 2 * qq + p;

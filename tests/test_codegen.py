@@ -1,7 +1,7 @@
 """Generated-code checks for the prefill kernel's inline-asm MFMAs (CPU only).
 
-The score MFMAs of the prefill kernel are inline asm with VGPR accumulators,
-so the compiler inserts no wait states around them.  The hardware needs 2 wait
+The score MFMAs of the prefill kernel, and the two products of its head-mix
+epilogue, are inline asm, so the compiler inserts no wait states around them.  The hardware needs 2 wait
 states between a VALU write of an MFMA operand and the MFMA, and some more
 between the MFMA and a VALU read of its result.  The kernel source supplies the
 second (s_nop after the last MFMA of a chain) and arranges for the first (the
@@ -70,6 +70,28 @@ def test_score_mfmas_present(prefill_asm):
 def test_no_valu_write_of_an_operand_just_before_an_asm_mfma(prefill_asm):
     bad = []
     for i, l in _vgpr_mfmas(prefill_asm):
+        srcs = set().union(*[_regs(t) for t in _operands(l)[1:4]])
+        ws = 0
+        for j in range(i - 1, max(0, i - 8), -1):
+            p = prefill_asm[j]
+            if ws >= 2:
+                break
+            if p.startswith("v_") and not p.startswith("v_mfma"):
+                ops = _operands(p)
+                if ops and _regs(ops[0]) & srcs:
+                    bad.append((p, l))
+            ws += _wait_states(p)
+    assert not bad, bad[:5]
+
+
+def test_no_valu_write_of_any_operand_just_before_an_mfma(prefill_asm):
+    # every MFMA, also those accumulating into AGPRs (the head-mix product of the
+    # epilogue is inline asm of that kind): no VALU write, v_accvgpr_write
+    # included, of a source operand within 2 wait states
+    bad = []
+    for i, l in enumerate(prefill_asm):
+        if not l.startswith("v_mfma"):
+            continue
         srcs = set().union(*[_regs(t) for t in _operands(l)[1:4]])
         ws = 0
         for j in range(i - 1, max(0, i - 8), -1):
