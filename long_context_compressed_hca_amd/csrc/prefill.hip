@@ -818,17 +818,21 @@ __device__ __forceinline__ void vha_query(const Args& a, WaveState& st, const It
   load_vha_frags(a, f, lane);
   const bf16x8 (&dn)[4] = f.dn;
   const bf16x8 (&up)[2][2] = f.up;
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
-    __builtin_amdgcn_sched_barrier(0);  // one dim block at a time (register pressure)
-    // Z^T in VGPRs (with the builtin the allocator takes accumulator
-    // registers for it and moves O blocks out of them); the last MFMA carries
-    // the wait states of the VALU reads below.
-    f32x16 z;
+  // Z^T of one 32-dim block in VGPRs (with the builtin the allocator takes
+  // accumulator registers for it and moves O blocks out of them); the last
+  // MFMA carries the wait states of the VALU reads of the result.
+  auto down_product = [&](int bb, f32x16& z) {
     mfma_z_zero(z, dn[0], vha_x_frag(rlo, 0, bb, lane));
     mfma_z_acc(z, dn[1], vha_x_frag(rlo, 1, bb, lane));
     mfma_z_acc(z, dn[2], vha_x_frag(rhi, 2, bb, lane));
     mfma_z_last(z, dn[3], vha_x_frag(rhi, 3, bb, lane));
+  };
+  // Block bb's up product follows block bb+1's down product, so the MFMAs of
+  // one overlap the conversion of the other.
+  f32x16 z;
+  down_product(0, z);
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
     // z: lane (dim 32bb + l32, g), register i = r 8(i/4) + 4g + i%4, so
     // registers 8s2 .. 8s2+7 are the k-slots of K-step s2 in the order above.
     bf16x8 za[2];
@@ -836,6 +840,7 @@ __device__ __forceinline__ void vha_query(const Args& a, WaveState& st, const It
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int j = 0; j < 8; ++j) za[s2][j] = (__bf16)z[8 * s2 + j];
+    if (bb < 3) down_product(bb + 1, z);
     // Into the O^T block in its accumulator registers.  The s_nop gives the 2
     // wait states a VALU write of za (and of the block, in gate_rb_vha) needs
     // before an MFMA reads it.
