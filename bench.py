@@ -320,7 +320,7 @@ def main():
         write_counters(*args.write_counters)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this library runs on one GPU only (asked for --gpus {args.gpus}); "
               "sharding across GPUs is not built.", file=sys.stderr)
         sys.exit(2)
 

@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   HCA_OK = 0,
   HCA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, inconsistent ranges */
-  HCA_ERR_UNSUPPORTED = 2, /* a shape this build has no kernel for (D, block, window, H) */
+  HCA_ERR_UNSUPPORTED = 2, /* a shape the library has no kernel for (D, block, window, H) */
   HCA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
   HCA_ERR_HIP = 4          /* the HIP runtime refused a launch */
 } hca_status_t;
