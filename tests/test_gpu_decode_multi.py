@@ -110,3 +110,18 @@ def test_bf16_output_and_repeat_calls():
     first = d.run().clone()
     assert torch.equal(first, d.run())
     compare(host_f64(first), d.oracle(), "bf16 out")
+
+
+def test_largest_row_count_per_sequence():
+    # M * H = 1024 rows per sequence (16 tokens x 64 heads), positions around
+    # block ends and t = 0
+    d = DecodeMulti(seed=43, positions=[0, 112, 240, 5000], M=16, H=64, out_dtype="f32")
+    compare(host_f64(d.run()), d.oracle(), "decode_multi M=16 H=64")
+
+
+def test_empty_batch_is_noop():
+    d = DecodeMulti(seed=44, positions=[5], M=2, H=16)
+    e = lambda t: t[:0]
+    hca.hca_attn_decode_multi(e(d.q), e(d.g), e(d.ck), e(d.cv), e(d.wk), e(d.wv), e(d.nk),
+                              e(d.nv), e(d.pos), e(d.out))
+    torch.cuda.synchronize()

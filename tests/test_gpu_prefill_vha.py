@@ -92,3 +92,13 @@ def test_128k_tokens_sampled():
     pos = sample_positions(0, 131072, 73, n_blocks=16, n_random=48)
     want = oracle.vha(p.oracle(pos), host(up), host(down))
     compare(p.gpu_rows(pos), want, "prefill+VHA T=131072 sampled")
+
+
+@pytest.mark.parametrize("Tq,q_start", [(1, 0), (1, 4095), (2, 130), (3, 127)])
+def test_few_queries(Tq, q_start):
+    # one query (the item's second half empty), two (one full item), three
+    p = Prefill(seed=74 + Tq, Tq=Tq, H=H, q_start=q_start, out_dtype="f32")
+    up, down = _factors(74, 4)
+    got = host_f64(_run_vha(p, up, down))
+    want = oracle.vha(p.oracle(), host(up), host(down))
+    compare(got, want, f"prefill+VHA Tq={Tq} q_start={q_start}")
