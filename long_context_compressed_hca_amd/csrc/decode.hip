@@ -404,10 +404,13 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     for (int db = 0; db < 8; ++db)
       vf[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sVc + voff + 32 * db));
     __builtin_amdgcn_sched_barrier(0);
+    // The weights first: their chain (partial-score reads, exp2, the weight
+    // write) ends the step for the owner waves, and issuing the copies takes
+    // several hundred cycles.
+    if (owner) weights(s + 1, sp, sPn);  // tile s+1
     scores(kc, sQn);  // tile s+2
     load_k<MT>(ks, s + 6, w, l16, g4, kn);
     copy_rows<MT>(ks, s + 5, ks.ev, ks.wv, ks.nv, sVd, kVRow, w, lane16);
-    if (owner) weights(s + 1, sp, sPn);  // tile s+1
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
