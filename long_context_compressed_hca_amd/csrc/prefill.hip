@@ -806,16 +806,15 @@ __device__ __forceinline__ void load_vha_frags(const Args& a, VhaFrags& f, int l
 // gate_rb_vha into regions rlo, rhi).  The result replaces the gated output in
 // O^T; bf16 output is written back into the regions for store_rb, f32 output
 // is stored from registers.
-// The factor fragments are loaded here, per query: kept live across the
-// gating of the item's other query they take registers the allocator then
-// finds by moving O blocks to scratch.
+// The caller loads the factor fragments one row block's gating ahead: kept
+// live across the gating of the item's other query, they take registers the
+// allocator then finds by moving O blocks to scratch.
 template <bool kF32>
 __device__ __forceinline__ void vha_query(const Args& a, WaveState& st, const Item& it, int qq,
-                                          uint8_t* rlo, uint8_t* rhi, int lane, int wave) {
+                                          const VhaFrags& f, uint8_t* rlo, uint8_t* rhi, int lane,
+                                          int wave) {
   asm volatile("" : "+v"(lane));
   const int l32 = lane & 31, g = lane >> 5;
-  VhaFrags f;
-  load_vha_frags(a, f, lane);
   const bf16x8 (&dn)[4] = f.dn;
   const bf16x8 (&up)[2][2] = f.up;
   // Z^T of one 32-dim block in VGPRs (with the builtin the allocator takes
@@ -1090,13 +1089,16 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
     } else {
       // The item's second query (row blocks 2, 3) first: its logits are in.
       gate_rb_vha(st, 2, sV0 + greg, sL, lane);
+      VhaFrags vf;
+      load_vha_frags(a, vf, lane);  // in flight during the next gating
       gate_rb_vha(st, 3, sV1 + greg, sL, lane);
-      vha_query<kF32>(a, st, it, 1, sV0 + greg, sV1 + greg, lane, wave);
+      vha_query<kF32>(a, st, it, 1, vf, sV0 + greg, sV1 + greg, lane, wave);
       if (!kF32) store_rb(a, it, 2, sV0 + greg, lane, wave);
       if (!kF32) store_rb(a, it, 3, sV1 + greg, lane, wave);
       gate_rb_vha(st, 0, sK0 + greg, sL, lane);
+      load_vha_frags(a, vf, lane);
       gate_rb_vha(st, 1, sK1 + greg, sL, lane);
-      vha_query<kF32>(a, st, it, 0, sK0 + greg, sK1 + greg, lane, wave);
+      vha_query<kF32>(a, st, it, 0, vf, sK0 + greg, sK1 + greg, lane, wave);
       if (!kF32) store_rb(a, it, 0, sK0 + greg, lane, wave);
       if (!kF32) store_rb(a, it, 1, sK1 + greg, lane, wave);
     }
