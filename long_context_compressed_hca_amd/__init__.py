@@ -78,6 +78,18 @@ def _dev_ptr(t, name, dtype=None, optional=False):
     return t.data_ptr()
 
 
+def _expect(t, shape, name):
+    """Raise ValueError unless tensor t (or None) has exactly `shape`."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(map(str, devs))}")
+
+
 def _stream(device):
     import torch
     return torch.cuda.current_stream(device).cuda_stream
@@ -87,11 +99,46 @@ def hca_compress(k, v, ck, cv, *, block: int = BLOCK):
     """ck, cv [T // 128, 512] <- block means of k, v [T, 512] (bf16).  k/ck or v/cv may be None."""
     import torch
     ref = k if k is not None else v
+    if ref is None:
+        raise ValueError("k and v are both None")
+    if ref.dim() != 2:
+        raise ValueError("k and v must be [T, D]")
     T, Dd = ref.shape
+    for x, c, n in ((k, ck, "k"), (v, cv, "v")):
+        if (x is None) != (c is None):
+            raise ValueError(f"{n} and c{n} must be both given or both None")
+        _expect(x, (T, Dd), n)
+        _expect(c, (T // block, Dd), "c" + n)
+    _same_device(k, v, ck, cv)
     _check(lib().hca_compress(_dev_ptr(k, "k", torch.bfloat16, True),
                               _dev_ptr(v, "v", torch.bfloat16, True), T, Dd, Dd, block,
                               _dev_ptr(ck, "ck", torch.bfloat16, True),
                               _dev_ptr(cv, "cv", torch.bfloat16, True), _stream(ref.device)))
+
+
+def _check_prefill_shapes(q, g, k, v, ck, cv, out) -> int:
+    """Shape checks shared by the prefill entry points; returns Nc."""
+    import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [Tq, H, D]")
+    Dd = q.shape[2]
+    _expect(g, q.shape, "g")
+    _expect(out, q.shape, "out")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    if k.dim() != 2 or k.shape[1] != Dd:
+        raise ValueError(f"k must be [Tkv, {Dd}], got {tuple(k.shape)}")
+    _expect(v, k.shape, "v")
+    if (ck is None) != (cv is None):
+        raise ValueError("ck and cv must be both given or both None")
+    nc = 0
+    if ck is not None:
+        if ck.dim() != 2 or ck.shape[1] != Dd:
+            raise ValueError(f"ck must be [Nc, {Dd}], got {tuple(ck.shape)}")
+        _expect(cv, ck.shape, "cv")
+        nc = ck.shape[0]
+    _same_device(q, g, k, v, ck, cv, out)
+    return nc
 
 
 def hca_attn_prefill(q, g, k, v, ck, cv, out, *, q_start: int = 0, kv_start: int = 0,
@@ -100,11 +147,7 @@ def hca_attn_prefill(q, g, k, v, ck, cv, out, *, q_start: int = 0, kv_start: int
     rows k/v starting at position kv_start, gated by sigmoid(g)."""
     import torch
     Tq, H, Dd = q.shape
-    if g.shape != q.shape or out.shape != q.shape:
-        raise ValueError("q, g and out must have the same shape")
-    if out.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out must be bfloat16 or float32")
-    nc = 0 if ck is None else ck.shape[0]
+    nc = _check_prefill_shapes(q, g, k, v, ck, cv, out)
     if scale is None:
         scale = Dd ** -0.5
     _check(lib().hca_attn_prefill(
@@ -116,13 +159,35 @@ def hca_attn_prefill(q, g, k, v, ck, cv, out, *, q_start: int = 0, kv_start: int
         _stream(q.device)))
 
 
+def _check_cache_shapes(B, Dd, ck, cv, wk, wv, pos, window) -> int:
+    """Shape checks of a decode call's per-sequence cache; returns nc_cap."""
+    if (ck is None) != (cv is None):
+        raise ValueError("ck and cv must be both given or both None")
+    nc_cap = 0
+    if ck is not None:
+        if ck.dim() != 3 or ck.shape[0] != B or ck.shape[2] != Dd:
+            raise ValueError(f"ck must be [{B}, nc_cap, {Dd}], got {tuple(ck.shape)}")
+        _expect(cv, ck.shape, "cv")
+        nc_cap = ck.shape[1]
+    _expect(wk, (B, window, Dd), "wk")
+    _expect(wv, (B, window, Dd), "wv")
+    _expect(pos, (B,), "pos")
+    return nc_cap
+
+
 def hca_attn_decode(q, g, ck, cv, wk, wv, pos, out, *, scale: float | None = None,
                     block: int = BLOCK, window: int = WINDOW):
     """out [B, H, 512] <- HCA decode for one new token per sequence at positions pos [B]
     (int64, on the GPU), with per-sequence entries ck/cv [B, nc_cap, 512] and rings
     wk/wv [B, 128, 512] (position p in slot p % 128)."""
     import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, D]")
     B, H, Dd = q.shape
+    _expect(g, q.shape, "g")
+    _expect(out, q.shape, "out")
+    nc_cap = _check_cache_shapes(B, Dd, ck, cv, wk, wv, pos, window)
+    _same_device(q, g, ck, cv, wk, wv, pos, out)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
     if scale is None:
@@ -130,7 +195,7 @@ def hca_attn_decode(q, g, ck, cv, wk, wv, pos, out, *, scale: float | None = Non
     _check(lib().hca_attn_decode(
         _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
         _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
-        ck.shape[1], _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
+        nc_cap, _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
         _dev_ptr(pos, "pos", torch.int64), B, H, Dd, block, window, float(scale),
         _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
         _stream(q.device)))
@@ -143,11 +208,15 @@ def hca_attn_decode_multi(q, g, ck, cv, wk, wv, nk, nv, pos, out, *, scale: floa
     new tokens.  Entries ck/cv [B, nc_cap, 512]; rings wk/wv [B, 128, 512] of committed
     rows (position p < pos in slot p % 128); the new tokens' rows nk/nv [B, M, 512]."""
     import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, M, H, D]")
     B, M, H, Dd = q.shape
-    if g.shape != q.shape or out.shape != q.shape:
-        raise ValueError("q, g and out must have the same shape")
-    if nk.shape != (B, M, Dd) or nv.shape != (B, M, Dd):
-        raise ValueError("nk and nv must be [B, M, D]")
+    _expect(g, q.shape, "g")
+    _expect(out, q.shape, "out")
+    _expect(nk, (B, M, Dd), "nk")
+    _expect(nv, (B, M, Dd), "nv")
+    nc_cap = _check_cache_shapes(B, Dd, ck, cv, wk, wv, pos, window)
+    _same_device(q, g, ck, cv, wk, wv, nk, nv, pos, out)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
     if scale is None:
@@ -155,7 +224,7 @@ def hca_attn_decode_multi(q, g, ck, cv, wk, wv, nk, nv, pos, out, *, scale: floa
     _check(lib().hca_attn_decode_multi(
         _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
         _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
-        ck.shape[1], _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
+        nc_cap, _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
         _dev_ptr(nk, "nk", torch.bfloat16), _dev_ptr(nv, "nv", torch.bfloat16),
         _dev_ptr(pos, "pos", torch.int64), B, M, H, Dd, block, window, float(scale),
         _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
@@ -169,14 +238,13 @@ def hca_attn_prefill_vha(q, g, k, v, ck, cv, up, down, out, *, q_start: int = 0,
     heads of each query; up [64, r], down [r, 64] bf16 on the GPU, r in 4, 8, .., 32."""
     import torch
     Tq, H, Dd = q.shape
-    if g.shape != q.shape or out.shape != q.shape:
-        raise ValueError("q, g and out must have the same shape")
-    if out.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out must be bfloat16 or float32")
+    nc = _check_prefill_shapes(q, g, k, v, ck, cv, out)
+    if up.dim() != 2:
+        raise ValueError("up must be [H, r]")
     r = up.shape[1]
     if up.shape != (H, r) or down.shape != (r, H):
         raise ValueError("up must be [H, r] and down [r, H]")
-    nc = 0 if ck is None else ck.shape[0]
+    _same_device(q, up, down)
     if scale is None:
         scale = Dd ** -0.5
     _check(lib().hca_attn_prefill_vha(

@@ -254,9 +254,8 @@ hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck,
   TRY(check_shape(D, block, window));
   if (B < 0) return fail(HCA_ERR_INVALID_ARG, "B = %d < 0", B);
   if (M < 1 || M > 16) return fail(HCA_ERR_UNSUPPORTED, "M = %d (need 1 .. 16)", M);
-  if (H < 16 || H % 16 != 0 || M * H > 1024)
-    return fail(HCA_ERR_UNSUPPORTED, "H = %d, M = %d (need H a multiple of 16, M*H <= 1024)", H,
-                M);
+  if (H < 16 || H > 64 || H % 16 != 0)
+    return fail(HCA_ERR_UNSUPPORTED, "H = %d (need a multiple of 16, at most 64)", H);
   if (nc_cap < 0) return fail(HCA_ERR_INVALID_ARG, "nc_cap = %lld < 0", (long long)nc_cap);
   if (out_dtype != HCA_BF16 && out_dtype != HCA_F32)
     return fail(HCA_ERR_INVALID_ARG, "unknown out_dtype %d", (int)out_dtype);

@@ -152,6 +152,7 @@ def decode_multi(L, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(D=128), UNSUPPORTED), (dict(M=0), UNSUPPORTED), (dict(M=17), UNSUPPORTED),
     (dict(H=8), UNSUPPORTED), (dict(H=24), UNSUPPORTED), (dict(M=16, H=80), UNSUPPORTED),
+    (dict(M=1, H=128), UNSUPPORTED), (dict(M=8, H=128), UNSUPPORTED),
     (dict(B=-1), INVALID), (dict(nc_cap=-1), INVALID), (dict(pos=0), INVALID),
     (dict(pos=P + 4), INVALID), (dict(nk=0), INVALID), (dict(nv=MIS), INVALID),
     (dict(ck=0), INVALID), (dict(scale=0.0), INVALID), (dict(dtype=2), INVALID),

@@ -111,7 +111,7 @@ def test_8192_tokens_64_heads_sampled():
 
 
 def test_128k_tokens_64_heads_sampled():
-    _sampled(Prefill(seed=3, Tq=131072, H=64), 3, "T=131072 H=64", n_blocks=24, n_random=96)
+    _sampled(Prefill(seed=3, Tq=131072, H=64), 3, "T=131072 H=64")
 
 
 def test_1m_context_last_chunk_sampled():
@@ -119,4 +119,4 @@ def test_1m_context_last_chunk_sampled():
     T = 1 << 20
     p = Prefill(seed=5, Tq=65536, H=64, q_start=T - 65536, k_total=T)
     assert p.kv_start == T - 65536 - 127 and p.Nc == 8192
-    _sampled(p, 5, "1M chunk", n_blocks=8, n_random=24)
+    _sampled(p, 5, "1M chunk")

@@ -89,7 +89,7 @@ def test_128k_tokens_sampled():
     p = Prefill(seed=73, Tq=131072, H=H)
     up, down = _factors(73, 8)
     _run_vha(p, up, down)
-    pos = sample_positions(0, 131072, 73, n_blocks=16, n_random=48)
+    pos = sample_positions(0, 131072, 73)
     want = oracle.vha(p.oracle(pos), host(up), host(down))
     compare(p.gpu_rows(pos), want, "prefill+VHA T=131072 sampled")
 
