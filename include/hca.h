@@ -37,8 +37,7 @@
  *     next synchronization, as usual in HIP.
  *   - hca_last_error() gives a human-readable reason for the last non-OK
  *     status returned on the calling thread.
- *   - Supported shapes: D = 512, block = 128, window = 128, 1 <= H <= 64 for
- *     prefill and H a multiple of 16 up to 64 for decode.
+ *   - Supported shapes: D = 512, block = 128, window = 128, 1 <= H <= 64.
  */
 #ifndef HCA_H
 #define HCA_H
@@ -131,16 +130,32 @@ hca_status_t hca_attn_prefill_vha(const void* q, const void* g, const void* k, c
                                   hca_dtype_t out_dtype, void* stream);
 
 /*
+ * Bytes of device workspace hca_attn_decode needs for B sequences of H query heads
+ * with nc_cap cached entries each (0: none).  Batches too small to fill the GPU
+ * with one workgroup per 16 query heads split each sequence's keys across
+ * workgroups (split-K); their partial softmax states (row maximum, row sum and
+ * unnormalised output, fp32) go through the workspace and a second kernel merges
+ * them.  Returns 0 for an unsupported shape (hca_attn_decode then reports it).
+ */
+size_t hca_decode_workspace_size(int B, int H, int D, int64_t nc_cap);
+
+/*
  * Decode attention: one new query per sequence, for B sequences at once.
- *   q, g     device, bf16 [B, H, D]          the new token's queries and gate logits
- *   ck, cv   device, bf16 [B, nc_cap, D]     per-sequence entries (only the first
- *                                            floor((pos+1)/128) are read)
- *   wk, wv   device, bf16 [B, window, D]     per-sequence ring of raw rows; position p
- *                                            lives in slot p % window, and slots of
- *                                            positions max(0,pos-127)..pos must be valid
- *   pos      device, int64 [B]               position of the new token (already written
- *                                            into its ring slot)
- *   out      device, [B, H, D]               bf16 or f32
+ *   q, g       device, bf16 [B, H, D]          the new token's queries and gate logits
+ *   ck, cv     device, bf16 [B, nc_cap, D]     per-sequence entries (only the first
+ *                                              floor((pos+1)/128) are read); may be NULL
+ *                                              if nc_cap = 0
+ *   wk, wv     device, bf16 [B, window, D]     per-sequence ring of raw rows; position p
+ *                                              lives in slot p % window, and slots of
+ *                                              positions max(0,pos-127)..pos must be valid
+ *   pos        device, int64 [B]               position of the new token (already written
+ *                                              into its ring slot)
+ *   out        device, [B, H, D]               bf16 or f32
+ *   workspace  device, at least hca_decode_workspace_size(B, H, D, nc_cap) bytes,
+ *              16-byte aligned, owned by the caller; may be NULL when that size is 0
+ *              (else HCA_ERR_WORKSPACE).  Its contents on entry do not matter and are
+ *              undefined afterwards; calls that share a workspace must not overlap.
+ * Supported: 1 <= H <= 64, nc_cap <= 2^24.
  * Entry counts come from device memory, so the host cannot check them: a pos with
  * floor((pos+1)/128) > nc_cap or pos < 0 is clamped on the device (never read out
  * of bounds) and its output is then unspecified.
@@ -149,7 +164,8 @@ hca_status_t hca_attn_prefill_vha(const void* q, const void* g, const void* k, c
 hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const void* cv,
                              int64_t nc_cap, const void* wk, const void* wv, const int64_t* pos,
                              int B, int H, int D, int block, int window, float scale, void* out,
-                             hca_dtype_t out_dtype, void* stream);
+                             hca_dtype_t out_dtype, void* workspace, size_t ws_bytes,
+                             void* stream);
 
 /*
  * Multi-token decode: M new tokens per sequence at positions pos .. pos+M-1, for B
@@ -169,8 +185,9 @@ hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const
  *   nk, nv   device, bf16 [B, M, D]          raw rows of the new tokens
  *   pos      device, int64 [B]               position of the first new token
  *   out      device, [B, M, H, D]            bf16 or f32
- * 1 <= M <= 16 and M*H <= 1024 (else HCA_ERR_UNSUPPORTED).  With M = 1 this is
- * hca_attn_decode with the new row passed in nk, nv instead of its ring slot.
+ * 1 <= M <= 16 and 1 <= H <= 64 (else HCA_ERR_UNSUPPORTED).  With M = 1 this is
+ * hca_attn_decode with the new row passed in nk, nv instead of its ring slot.  No
+ * workspace: the M * H query rows of a batch fill the GPU without a key split.
  * As for hca_attn_decode, a pos with floor((pos+M)/128) > nc_cap or pos < 0 is
  * clamped on the device and its output is then unspecified.  B = 0 is a no-op.
  */

@@ -45,7 +45,10 @@ def lib():
         L.hca_attn_prefill.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I, F,
                                        P, I, P]
         L.hca_attn_prefill.restype = I
-        L.hca_attn_decode.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, F, P, I, P]
+        L.hca_decode_workspace_size.argtypes = [I, I, I, I64]
+        L.hca_decode_workspace_size.restype = ctypes.c_size_t
+        L.hca_attn_decode.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, F, P, I, P,
+                                      ctypes.c_size_t, P]
         L.hca_attn_decode.restype = I
         L.hca_attn_decode_multi.argtypes = [P, P, P, P, I64, P, P, P, P, P, I, I, I, I, I, I, F,
                                             P, I, P]
@@ -175,11 +178,18 @@ def _check_cache_shapes(B, Dd, ck, cv, wk, wv, pos, window) -> int:
     return nc_cap
 
 
+def decode_workspace_size(B: int, H: int, nc_cap: int, D: int = D) -> int:
+    """Bytes of device workspace hca_attn_decode needs (0: none)."""
+    return int(lib().hca_decode_workspace_size(B, H, D, nc_cap))
+
+
 def hca_attn_decode(q, g, ck, cv, wk, wv, pos, out, *, scale: float | None = None,
-                    block: int = BLOCK, window: int = WINDOW):
+                    workspace=None, block: int = BLOCK, window: int = WINDOW):
     """out [B, H, 512] <- HCA decode for one new token per sequence at positions pos [B]
     (int64, on the GPU), with per-sequence entries ck/cv [B, nc_cap, 512] and rings
-    wk/wv [B, 128, 512] (position p in slot p % 128)."""
+    wk/wv [B, 128, 512] (position p in slot p % 128).  workspace: a device uint8 tensor
+    of at least decode_workspace_size(B, H, nc_cap) bytes; allocated here (through
+    torch) when None and needed."""
     import torch
     if q.dim() != 3:
         raise ValueError("q must be [B, H, D]")
@@ -192,13 +202,17 @@ def hca_attn_decode(q, g, ck, cv, wk, wv, pos, out, *, scale: float | None = Non
         raise TypeError("out must be bfloat16 or float32")
     if scale is None:
         scale = Dd ** -0.5
+    need = decode_workspace_size(B, H, nc_cap, Dd) if B > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hca_attn_decode(
         _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
         _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
         nc_cap, _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
         _dev_ptr(pos, "pos", torch.int64), B, H, Dd, block, window, float(scale),
         _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
-        _stream(q.device)))
+        _dev_ptr(workspace, "workspace", optional=True), ws_bytes, _stream(q.device)))
 
 
 def hca_attn_decode_multi(q, g, ck, cv, wk, wv, nk, nv, pos, out, *, scale: float | None = None,

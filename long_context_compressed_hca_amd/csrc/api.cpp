@@ -203,19 +203,29 @@ hca_status_t hca_attn_prefill_vha(const void* q, const void* g, const void* k, c
                       "hca_attn_prefill_vha launch");
 }
 
-hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const void* cv,
-                             int64_t nc_cap, const void* wk, const void* wv, const int64_t* pos,
-                             int B, int H, int D, int block, int window, float scale, void* out,
-                             hca_dtype_t out_dtype, void* stream) {
+size_t hca_decode_workspace_size(int B, int H, int D, int64_t nc_cap) {
+  if (B <= 0 || H < 1 || H > 64 || D != hca::kD || nc_cap < 0) return 0;
+  return hca::decode_workspace_bytes(B, H, nc_cap);
+}
+
+// Checks shared by the decode entry points; fills p.
+static hca_status_t decode_check(const void* q, const void* g, const void* ck, const void* cv,
+                                 int64_t nc_cap, const void* wk, const void* wv,
+                                 const int64_t* pos, int B, int M, int H, int D, int block,
+                                 int window, float scale, void* out, hca_dtype_t out_dtype,
+                                 hca::DecodeProblem& p) {
   TRY(check_shape(D, block, window));
   if (B < 0) return fail(HCA_ERR_INVALID_ARG, "B = %d < 0", B);
-  if (H < 16 || H > 64 || H % 16 != 0)
-    return fail(HCA_ERR_UNSUPPORTED, "H = %d (need a multiple of 16, at most 64)", H);
+  if (M < 1 || M > 16) return fail(HCA_ERR_UNSUPPORTED, "M = %d (need 1 .. 16)", M);
+  if (H < 1 || H > 64) return fail(HCA_ERR_UNSUPPORTED, "H = %d (need 1 <= H <= 64)", H);
   if (nc_cap < 0) return fail(HCA_ERR_INVALID_ARG, "nc_cap = %lld < 0", (long long)nc_cap);
+  if (nc_cap > (int64_t)1 << 24)
+    return fail(HCA_ERR_UNSUPPORTED, "nc_cap = %lld (at most 2^24 entries per sequence)",
+                (long long)nc_cap);
   if (out_dtype != HCA_BF16 && out_dtype != HCA_F32)
     return fail(HCA_ERR_INVALID_ARG, "unknown out_dtype %d", (int)out_dtype);
   TRY(check_scale(scale));
-  if (B == 0) return ok();
+  if (B == 0) return HCA_OK;
   TRY(check_ptr(q, "q"));
   TRY(check_ptr(g, "g"));
   TRY(check_ptr(wk, "wk"));
@@ -228,7 +238,6 @@ hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const
     TRY(check_ptr(ck, "ck"));
     TRY(check_ptr(cv, "cv"));
   }
-  hca::DecodeProblem p;
   p.q = static_cast<const uint16_t*>(q);
   p.g = static_cast<const uint16_t*>(g);
   p.ck = static_cast<const uint16_t*>(ck);
@@ -242,7 +251,34 @@ hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const
   p.H = H;
   p.scale = scale;
   p.out_f32 = out_dtype == HCA_F32;
-  return hip_status(hca::launch_decode(p, static_cast<hipStream_t>(stream)),
+  return HCA_OK;
+}
+
+hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const void* cv,
+                             int64_t nc_cap, const void* wk, const void* wv, const int64_t* pos,
+                             int B, int H, int D, int block, int window, float scale, void* out,
+                             hca_dtype_t out_dtype, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  hca::DecodeProblem p;
+  TRY(decode_check(q, g, ck, cv, nc_cap, wk, wv, pos, B, 1, H, D, block, window, scale, out,
+                   out_dtype, p));
+  if (B == 0) return ok();
+  const size_t need = hca::decode_workspace_bytes(B, H, nc_cap);
+  if (need == 0 && H % 16 == 0)
+    // A batch that fills the GPU with one workgroup per 16 heads: the kernel
+    // whose four waves walk each tile together (decode.hip) streams the keys
+    // faster there.
+    return hip_status(hca::launch_decode(p, static_cast<hipStream_t>(stream)),
+                      "hca_attn_decode launch");
+  if (need > 0) {
+    if (workspace == nullptr || ws_bytes < need)
+      return fail(HCA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (%s)",
+                  workspace ? ws_bytes : (size_t)0, need, "hca_decode_workspace_size");
+    if (!aligned16(workspace))
+      return fail(HCA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  }
+  return hip_status(hca::launch_decode_sk(p, nullptr, nullptr, 1, workspace,
+                                          static_cast<hipStream_t>(stream)),
                     "hca_attn_decode launch");
 }
 
@@ -251,47 +287,22 @@ hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck,
                                    const void* nk, const void* nv, const int64_t* pos, int B,
                                    int M, int H, int D, int block, int window, float scale,
                                    void* out, hca_dtype_t out_dtype, void* stream) {
-  TRY(check_shape(D, block, window));
-  if (B < 0) return fail(HCA_ERR_INVALID_ARG, "B = %d < 0", B);
-  if (M < 1 || M > 16) return fail(HCA_ERR_UNSUPPORTED, "M = %d (need 1 .. 16)", M);
-  if (H < 16 || H > 64 || H % 16 != 0)
-    return fail(HCA_ERR_UNSUPPORTED, "H = %d (need a multiple of 16, at most 64)", H);
-  if (nc_cap < 0) return fail(HCA_ERR_INVALID_ARG, "nc_cap = %lld < 0", (long long)nc_cap);
-  if (out_dtype != HCA_BF16 && out_dtype != HCA_F32)
-    return fail(HCA_ERR_INVALID_ARG, "unknown out_dtype %d", (int)out_dtype);
-  TRY(check_scale(scale));
+  hca::DecodeProblem p;
+  TRY(decode_check(q, g, ck, cv, nc_cap, wk, wv, pos, B, M, H, D, block, window, scale, out,
+                   out_dtype, p));
   if (B == 0) return ok();
-  TRY(check_ptr(q, "q"));
-  TRY(check_ptr(g, "g"));
-  TRY(check_ptr(wk, "wk"));
-  TRY(check_ptr(wv, "wv"));
   TRY(check_ptr(nk, "nk"));
   TRY(check_ptr(nv, "nv"));
-  TRY(check_ptr(out, "out"));
-  if (pos == nullptr) return fail(HCA_ERR_INVALID_ARG, "pos is NULL");
-  if (reinterpret_cast<uintptr_t>(pos) % 8 != 0)
-    return fail(HCA_ERR_INVALID_ARG, "pos is not 8-byte aligned");
-  if (nc_cap > 0) {
-    TRY(check_ptr(ck, "ck"));
-    TRY(check_ptr(cv, "cv"));
-  }
-  hca::DecodeProblem p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.g = static_cast<const uint16_t*>(g);
-  p.ck = static_cast<const uint16_t*>(ck);
-  p.cv = static_cast<const uint16_t*>(cv);
-  p.wk = static_cast<const uint16_t*>(wk);
-  p.wv = static_cast<const uint16_t*>(wv);
-  p.pos = pos;
-  p.out = out;
-  p.nc_cap = nc_cap;
-  p.B = B;
-  p.H = H;
-  p.scale = scale;
-  p.out_f32 = out_dtype == HCA_F32;
-  return hip_status(hca::launch_decode_multi(p, static_cast<const uint16_t*>(nk),
-                                             static_cast<const uint16_t*>(nv), M,
-                                             static_cast<hipStream_t>(stream)),
+  if (H % 16 == 0)
+    // Head blocks of 16 rows: the kernel that gives one workgroup up to 4 blocks
+    // of a sequence (decode.hip) reads each sequence's keys into fewer CUs.
+    return hip_status(hca::launch_decode_multi(p, static_cast<const uint16_t*>(nk),
+                                               static_cast<const uint16_t*>(nv), M,
+                                               static_cast<hipStream_t>(stream)),
+                      "hca_attn_decode_multi launch");
+  return hip_status(hca::launch_decode_sk(p, static_cast<const uint16_t*>(nk),
+                                          static_cast<const uint16_t*>(nv), M, nullptr,
+                                          static_cast<hipStream_t>(stream)),
                     "hca_attn_decode_multi launch");
 }
 

@@ -56,4 +56,15 @@ hipError_t launch_decode(const DecodeProblem& p, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeProblem& p, const uint16_t* nk, const uint16_t* nv,
                                int M, hipStream_t stream);
 
+// Split-K decode: keys split across the four waves of a workgroup and, for
+// batches too small to fill the chip, across decode_splits() workgroups whose
+// partial results go through a workspace of decode_workspace_bytes() bytes.
+// nk == nullptr: one new token per sequence (its row in the ring slot).
+// Otherwise M new tokens whose rows are in nk, nv [B, M, 512], q, g and out
+// [B, M, H, 512], no split across workgroups and no workspace.
+int decode_splits(int B, int H, int64_t nc_cap);
+size_t decode_workspace_bytes(int B, int H, int64_t nc_cap);
+hipError_t launch_decode_sk(const DecodeProblem& p, const uint16_t* nk, const uint16_t* nv, int M,
+                            void* ws, hipStream_t stream);
+
 }  // namespace hca

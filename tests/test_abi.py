@@ -118,21 +118,47 @@ def test_prefill_vha_noop(L):
 
 def decode(L, **kw):
     a = dict(q=P, g=P, ck=P, cv=P, nc_cap=256, wk=P, wv=P, pos=P, B=64, H=64, D=512, block=128,
-             window=128, scale=512 ** -0.5, out=P, dtype=0, stream=None)
+             window=128, scale=512 ** -0.5, out=P, dtype=0, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.hca_attn_decode(a["q"], a["g"], a["ck"], a["cv"], a["nc_cap"], a["wk"], a["wv"],
                              a["pos"], a["B"], a["H"], a["D"], a["block"], a["window"],
-                             a["scale"], a["out"], a["dtype"], a["stream"])
+                             a["scale"], a["out"], a["dtype"], a["ws"], a["ws_bytes"],
+                             a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=128), UNSUPPORTED), (dict(H=8), UNSUPPORTED), (dict(H=80), UNSUPPORTED),
-    (dict(H=24), UNSUPPORTED), (dict(B=-1), INVALID), (dict(nc_cap=-1), INVALID),
+    (dict(D=128), UNSUPPORTED), (dict(H=0), UNSUPPORTED), (dict(H=80), UNSUPPORTED),
+    (dict(nc_cap=(1 << 24) + 1), UNSUPPORTED), (dict(B=-1), INVALID),
+    (dict(nc_cap=-1), INVALID),
     (dict(pos=0), INVALID), (dict(pos=P + 4), INVALID), (dict(wk=0), INVALID),
     (dict(ck=0), INVALID), (dict(scale=float("nan")), INVALID), (dict(dtype=3), INVALID),
 ])
 def test_decode_rejects(L, kw, status):
     assert decode(L, **kw) == status
+
+
+WORKSPACE = hca.HCA_ERR_WORKSPACE
+
+
+def test_decode_workspace_size(L):
+    # batches that fill the GPU need none; small ones split their keys across
+    # workgroups and need fp32 partials (32 + 16 * 512 floats per 16 heads and split)
+    assert L.hca_decode_workspace_size(64, 64, 512, 256) == 0
+    assert L.hca_decode_workspace_size(256, 16, 512, 4096) == 0
+    small = L.hca_decode_workspace_size(8, 64, 512, 256)
+    assert small > 0 and small % ((32 + 16 * 512) * 4 * 8 * 4) == 0
+    assert L.hca_decode_workspace_size(1, 8, 512, 1 << 20) > 0
+    assert L.hca_decode_workspace_size(1, 8, 512, 0) == 0   # 8 window tiles: no split
+    for bad in [(0, 64, 512, 256), (8, 65, 512, 256), (8, 64, 256, 256), (8, 64, 512, -1)]:
+        assert L.hca_decode_workspace_size(*bad) == 0
+
+
+def test_decode_workspace_errors(L):
+    need = L.hca_decode_workspace_size(8, 64, 512, 256)
+    assert decode(L, B=8, ws=None, ws_bytes=0) == WORKSPACE
+    assert decode(L, B=8, ws=P, ws_bytes=need - 1) == WORKSPACE
+    assert decode(L, B=8, ws=MIS, ws_bytes=need) == INVALID
+    assert "workspace" in L.hca_last_error().decode()
 
 
 def test_decode_noop(L):
@@ -151,7 +177,7 @@ def decode_multi(L, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(D=128), UNSUPPORTED), (dict(M=0), UNSUPPORTED), (dict(M=17), UNSUPPORTED),
-    (dict(H=8), UNSUPPORTED), (dict(H=24), UNSUPPORTED), (dict(M=16, H=80), UNSUPPORTED),
+    (dict(H=0), UNSUPPORTED), (dict(M=16, H=80), UNSUPPORTED),
     (dict(M=1, H=128), UNSUPPORTED), (dict(M=8, H=128), UNSUPPORTED),
     (dict(B=-1), INVALID), (dict(nc_cap=-1), INVALID), (dict(pos=0), INVALID),
     (dict(pos=P + 4), INVALID), (dict(nk=0), INVALID), (dict(nv=MIS), INVALID),

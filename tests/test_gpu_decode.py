@@ -45,7 +45,7 @@ def test_64_sequences_32k_history():
     print(compare(host_f64(d.run()), d.oracle(), "decode B=64"))
 
 
-@pytest.mark.parametrize("H", [16, 32, 48, 64])
+@pytest.mark.parametrize("H", [1, 8, 16, 24, 32, 48, 64])
 def test_mixed_positions(H):
     positions = [0, 1, 5, 126, 127, 128, 129, 255, 256, 383, 1000, 4095, 4096, 32767]
     d = Decode(seed=10 + H, positions=positions, H=H, out_dtype="f32")
@@ -60,6 +60,30 @@ def test_large_batches(B):
     positions[:4] = [0, 127, 128, 2999]
     d = Decode(seed=17 + B, positions=positions, H=64, out_dtype="f32")
     compare(host_f64(d.run()), d.oracle(), f"decode B={B}")
+
+
+@pytest.mark.parametrize("B,H,pos", [(1, 64, 20000), (2, 8, 70000), (8, 64, 32768),
+                                     (3, 40, 30000), (16, 16, 20000)])
+def test_small_batches_split_keys(B, H, pos):
+    # batches too small to fill the GPU split each sequence's keys across
+    # workgroups and merge the partial states through the workspace
+    import long_context_compressed_hca_amd as h
+    rng = np.random.default_rng(B * 1000 + H)
+    positions = rng.integers(0, pos + 1, size=B)
+    positions[0] = pos
+    if B > 1:
+        positions[-1] = min(positions[-1], 5)  # a sequence with fewer tiles than streams
+    d = Decode(seed=18 + B + H, positions=positions, H=H, out_dtype="f32")
+    need = h.decode_workspace_size(B, H, d.nc_cap)
+    assert need > 0
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=dev())  # stale contents
+    hca.hca_attn_decode(d.q, d.g, d.ck, d.cv, d.wk, d.wv, d.pos, d.out, workspace=ws)
+    torch.cuda.synchronize()
+    first = d.out.clone()
+    compare(host_f64(first), d.oracle(), f"split decode B={B} H={H}")
+    hca.hca_attn_decode(d.q, d.g, d.ck, d.cv, d.wk, d.wv, d.pos, d.out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first, d.out)  # same workspace again: same bits
 
 
 def test_cache_larger_than_needed():

@@ -52,7 +52,8 @@ def test_verify_64_sequences_32k_history():
 POSITIONS = [0, 1, 5, 124, 125, 126, 127, 128, 129, 253, 254, 255, 256, 383, 1000, 4093]
 
 
-@pytest.mark.parametrize("M,H", [(1, 64), (2, 16), (3, 64), (4, 32), (8, 64), (16, 16)])
+@pytest.mark.parametrize("M,H", [(1, 64), (2, 16), (3, 64), (4, 32), (8, 64), (16, 16), (3, 8),
+                                 (2, 24), (5, 1)])
 def test_mixed_positions(M, H):
     d = DecodeMulti(seed=20 + M + H, positions=POSITIONS, M=M, H=H, out_dtype="f32")
     compare(host_f64(d.run()), d.oracle(), f"decode_multi M={M} H={H}")

@@ -128,17 +128,21 @@ def _ring_slot(t):
     return t % 128
 
 
-@pytest.mark.parametrize("H,out_dtype", [(64, "bf16"), (16, "f32")])
-def test_decode_peaked_rows(H, out_dtype):
-    positions = np.array([5, 130, 300, 1000, 4095, 32768, 200, 2500], dtype=np.int64)
-    B = len(positions)
+@pytest.mark.parametrize("H,out_dtype,B", [(64, "bf16", 8), (16, "f32", 8), (8, "f32", 8),
+                                          (64, "f32", 64), (16, "bf16", 256)])
+def test_decode_peaked_rows(H, out_dtype, B):
+    # positions from 131072 on have at least 64 entry tiles, so every stream of
+    # keys (at most 16 splits x 4 waves) starts with an entry tile: the aimed
+    # window keys lie more than 2^64 above each stream's first reference
+    positions = np.array([5, 130, 300, 140000, 4095, 32768, 150001, 2500], dtype=np.int64)
+    positions = np.resize(positions, B)  # larger batches repeat the pattern
     nc_cap = int(max((positions + 1) // 128))
     seed = 92 + H
     q, g = gen(seed, synth.Q, (B, H, D)), gen(seed, synth.G, (B, H, D))
     ck, cv = gen(seed, synth.CK, (B, nc_cap, D)), gen(seed, synth.CV, (B, nc_cap, D))
     wk, wv = gen(seed, synth.WK, (B, 128, D)), gen(seed, synth.WV, (B, 128, D))
     qh, wkh, ckh = host(q), host(wk), host(ck)
-    n_over = 0
+    n_over = n_late = 0
     for b, t in enumerate(positions):
         nc = (t + 1) // 128
         if nc == 0:
@@ -146,8 +150,11 @@ def test_decode_peaked_rows(H, out_dtype):
         for h in range(0, H, 2):
             ka, kb = wkh[b, _ring_slot(t)], wkh[b, _ring_slot(t - 5)]
             qh[b, h] = _aim(qh[b, h], ka, kb)
-            n_over += _gap(qh[b, h], (ka, kb), ckh[b, :nc]) > GAP
-    assert n_over >= 0.9 * 7 * (H // 2), n_over
+            over = _gap(qh[b, h], (ka, kb), ckh[b, :nc]) > GAP
+            n_over += over
+            n_late += over and nc >= 1024
+    assert n_over >= 0.9 * (B * 7 // 8) * max(1, H // 2), n_over
+    assert n_late >= 2 * max(1, H // 2), n_late
     q = _to_dev(qh)
     pos = torch.as_tensor(positions, device=dev())
     out = torch.empty((B, H, D), device=dev(),
@@ -158,7 +165,7 @@ def test_decode_peaked_rows(H, out_dtype):
     compare(host_f64(out), ref, f"peaked decode H={H}")
 
 
-@pytest.mark.parametrize("M,H", [(3, 64), (2, 16)])
+@pytest.mark.parametrize("M,H", [(3, 64), (2, 16), (3, 8), (2, 24)])
 def test_decode_multi_peaked_rows(M, H):
     positions = np.array([3, 129, 700, 32765, 5000], dtype=np.int64)
     B = len(positions)
@@ -169,7 +176,7 @@ def test_decode_multi_peaked_rows(M, H):
     wk, wv = gen(seed, synth.WK, (B, 128, D)), gen(seed, synth.WV, (B, 128, D))
     nk, nv = gen(seed, synth.NK, (B, M, D)), gen(seed, synth.NV, (B, M, D))
     qh, wkh, ckh, nkh = host(q), host(wk), host(ck), host(nk)
-    n_over = 0
+    n_over = n_late = 0
     for b, t in enumerate(positions):
         for j in range(M):
             nc = (t + j + 1) // 128
@@ -179,8 +186,12 @@ def test_decode_multi_peaked_rows(M, H):
                 # the token's own new row and a committed ring row of its window
                 ka, kb = nkh[b, j], wkh[b, _ring_slot(t - 2)]
                 qh[b, j, h] = _aim(qh[b, j, h], ka, kb)
-                n_over += _gap(qh[b, j, h], (ka, kb), ckh[b, :nc]) > GAP
+                over = _gap(qh[b, j, h], (ka, kb), ckh[b, :nc]) > GAP
+                n_over += over
+                # 64 entries or more: each of the 4 key streams starts with an entry tile
+                n_late += over and nc >= 64
     assert n_over >= 0.9 * 4 * M * (H // 2), n_over
+    assert n_late >= M * (H // 2), n_late
     q = _to_dev(qh)
     pos = torch.as_tensor(positions, device=dev())
     out = torch.empty((B, M, H, D), device=dev(), dtype=torch.float32)
