@@ -168,6 +168,24 @@ hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const
                              void* stream);
 
 /*
+ * hca_attn_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without the workspace, which comes from a scratch array built into the
+ * library instead, one per GPU (8,421,376 bytes: the largest workspace
+ * hca_decode_workspace_size returns), held until the process ends.  The call
+ * allocates and frees nothing; a shape needing more scratch than that returns
+ * HCA_ERR_WORKSPACE.  Every call on a GPU shares that GPU's scratch, so calls that
+ * overlap on one GPU (concurrent streams, other threads) race and must be
+ * serialised by the caller.  The first call on each device looks up the scratch's
+ * device address (hipGetSymbolAddress); the stream must belong to the current device.
+ */
+hca_status_t hca_attn_decode_noalloc(const void* q, const void* g, const void* ck, const void* cv,
+                                     int64_t nc_cap, const void* wk, const void* wv,
+                                     const int64_t* pos, int B, int H, int D, int block,
+                                     int window, float scale, void* out, hca_dtype_t out_dtype,
+                                     void* stream);
+
+/*
  * Multi-token decode: M new tokens per sequence at positions pos .. pos+M-1, for B
  * sequences at once, as when the tokens of a drafter are verified in one pass (the
  * ECHO layer doubles as a speculative-decoding drafter: blog.derekhsu.net, section

@@ -50,6 +50,8 @@ def lib():
         L.hca_attn_decode.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, F, P, I, P,
                                       ctypes.c_size_t, P]
         L.hca_attn_decode.restype = I
+        L.hca_attn_decode_noalloc.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, F, P, I, P]
+        L.hca_attn_decode_noalloc.restype = I
         L.hca_attn_decode_multi.argtypes = [P, P, P, P, I64, P, P, P, P, P, I, I, I, I, I, I, F,
                                             P, I, P]
         L.hca_attn_decode_multi.restype = I
@@ -213,6 +215,32 @@ def hca_attn_decode(q, g, ck, cv, wk, wv, pos, out, *, scale: float | None = Non
         _dev_ptr(pos, "pos", torch.int64), B, H, Dd, block, window, float(scale),
         _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
         _dev_ptr(workspace, "workspace", optional=True), ws_bytes, _stream(q.device)))
+
+
+def hca_attn_decode_noalloc(q, g, ck, cv, wk, wv, pos, out, *, scale: float | None = None,
+                            block: int = BLOCK, window: int = WINDOW):
+    """hca_attn_decode without a workspace argument: split batches use the library's
+    built-in per-GPU scratch, so the call allocates nothing.  Calls overlapping on one
+    GPU race on that scratch."""
+    import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, D]")
+    B, H, Dd = q.shape
+    _expect(g, q.shape, "g")
+    _expect(out, q.shape, "out")
+    nc_cap = _check_cache_shapes(B, Dd, ck, cv, wk, wv, pos, window)
+    _same_device(q, g, ck, cv, wk, wv, pos, out)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    if scale is None:
+        scale = Dd ** -0.5
+    _check(lib().hca_attn_decode_noalloc(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
+        _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
+        nc_cap, _dev_ptr(wk, "wk", torch.bfloat16), _dev_ptr(wv, "wv", torch.bfloat16),
+        _dev_ptr(pos, "pos", torch.int64), B, H, Dd, block, window, float(scale),
+        _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
+        _stream(q.device)))
 
 
 def hca_attn_decode_multi(q, g, ck, cv, wk, wv, nk, nv, pos, out, *, scale: float | None = None,

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "hca_kernels.h"
 
@@ -58,11 +59,42 @@ hca_status_t hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Device scratch of hca_attn_decode_noalloc: room for the largest decode
+// workspace, one copy per GPU, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host it is only a stand-in for
+// the symbol): it uses the device address looked up once per device.
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[hca::kDecodeWorkspaceMax];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 #define TRY(expr)                          \
   do {                                     \
     const hca_status_t st_ = (expr);       \
     if (st_ != HCA_OK) return st_;         \
   } while (0)
+
+// Device address of this GPU's scratch (the current device), looked up on the
+// first call for that device.
+hca_status_t scratch_address(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(HCA_ERR_HIP, "hipGetDevice: %s (%d)", hipGetErrorString(e), (int)e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HCA_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess || p == nullptr)
+      return fail(HCA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s (%d)", dev,
+                  hipGetErrorString(es), (int)es);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HCA_OK;
+}
 
 }  // namespace
 
@@ -280,6 +312,29 @@ hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const
   return hip_status(hca::launch_decode_sk(p, nullptr, nullptr, 1, workspace,
                                           static_cast<hipStream_t>(stream)),
                     "hca_attn_decode launch");
+}
+
+hca_status_t hca_attn_decode_noalloc(const void* q, const void* g, const void* ck, const void* cv,
+                                     int64_t nc_cap, const void* wk, const void* wv,
+                                     const int64_t* pos, int B, int H, int D, int block,
+                                     int window, float scale, void* out, hca_dtype_t out_dtype,
+                                     void* stream) {
+  hca::DecodeProblem p;
+  TRY(decode_check(q, g, ck, cv, nc_cap, wk, wv, pos, B, 1, H, D, block, window, scale, out,
+                   out_dtype, p));
+  if (B == 0) return ok();
+  const size_t need = hca::decode_workspace_bytes(B, H, nc_cap);
+  if (need > hca::kDecodeWorkspaceMax)
+    return fail(HCA_ERR_WORKSPACE, "needs %zu bytes of workspace, the built-in scratch holds %zu",
+                need, hca::kDecodeWorkspaceMax);
+  if (need == 0 && H % 16 == 0)
+    return hip_status(hca::launch_decode(p, static_cast<hipStream_t>(stream)),
+                      "hca_attn_decode_noalloc launch");
+  void* ws = nullptr;
+  if (need > 0) TRY(scratch_address(&ws));
+  return hip_status(hca::launch_decode_sk(p, nullptr, nullptr, 1, ws,
+                                          static_cast<hipStream_t>(stream)),
+                    "hca_attn_decode_noalloc launch");
 }
 
 hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck, const void* cv,

@@ -64,6 +64,9 @@ hipError_t launch_decode_multi(const DecodeProblem& p, const uint16_t* nk, const
 // [B, M, H, 512], no split across workgroups and no workspace.
 int decode_splits(int B, int H, int64_t nc_cap);
 size_t decode_workspace_bytes(int B, int H, int64_t nc_cap);
+// Largest workspace decode_workspace_bytes() returns: a split batch has at most
+// 256 partials (B * head blocks * splits <= 256) of (32 + 16 * 512) floats.
+constexpr size_t kDecodeWorkspaceMax = (size_t)256 * (32 + 16 * kD) * sizeof(float);
 hipError_t launch_decode_sk(const DecodeProblem& p, const uint16_t* nk, const uint16_t* nv, int M,
                             void* ws, hipStream_t stream);
 

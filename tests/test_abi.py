@@ -153,6 +153,24 @@ def test_decode_workspace_size(L):
         assert L.hca_decode_workspace_size(*bad) == 0
 
 
+def decode_noalloc(L, **kw):
+    a = dict(q=P, g=P, ck=P, cv=P, nc_cap=256, wk=P, wv=P, pos=P, B=64, H=64, D=512, block=128,
+             window=128, scale=512 ** -0.5, out=P, dtype=0, stream=None)
+    a.update(kw)
+    return L.hca_attn_decode_noalloc(a["q"], a["g"], a["ck"], a["cv"], a["nc_cap"], a["wk"],
+                                     a["wv"], a["pos"], a["B"], a["H"], a["D"], a["block"],
+                                     a["window"], a["scale"], a["out"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=128), UNSUPPORTED), (dict(H=0), UNSUPPORTED), (dict(B=-1), INVALID),
+    (dict(pos=0), INVALID), (dict(q=MIS), INVALID), (dict(scale=-1.0), INVALID),
+])
+def test_decode_noalloc_rejects(L, kw, status):
+    assert decode_noalloc(L, **kw) == status
+    assert decode_noalloc(L, B=0) == OK
+
+
 def test_decode_workspace_errors(L):
     need = L.hca_decode_workspace_size(8, 64, 512, 256)
     assert decode(L, B=8, ws=None, ws_bytes=0) == WORKSPACE
