@@ -49,6 +49,8 @@ def bind(lib):
     lib.hca_oracle_compress.argtypes = [P, I64, I64, I, I, P]
     lib.hca_oracle_attn.argtypes = [P, P, P, I64, P, P, I64, I64, P, P, I64, I, I, I, I, D, P, I]
     lib.hca_oracle_decode.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, D, P, I]
+    lib.hca_oracle_attn_backward.argtypes = [P, P, P, I64, P, P, P, P, I64, I, I, I, I, D, P, P,
+                                             P, P, P, P, I]
     lib.hca_oracle_round_bf16.argtypes = [D]
     lib.hca_oracle_round_bf16.restype = ctypes.c_uint16
     lib.hca_oracle_widen_bf16.argtypes = [ctypes.c_uint16]
@@ -203,3 +205,60 @@ def _widen_array(bits) -> np.ndarray:
 def attn_vha(q, g, tpos, k, v, kv_start, ck, cv, up, down, **kw) -> np.ndarray:
     """HCA attention rows (``attn``), gated, then the VHA head mix (``vha``)."""
     return vha(attn(q, g, tpos, k, v, kv_start, ck, cv, **kw), up, down)
+
+
+def gate_logits(latent, w_g) -> np.ndarray:
+    """Gate logits of the low-rank gate: the gate is computed from the query's
+    low-rank latent, several times narrower than the hidden state
+    (blog.derekhsu.net, section 潛在閘控稀疏注意力, the 低秩閘控注意力 item;
+    yilup.net, section 架構設計: far fewer gate weights than a full-width gate).
+        G[t, n] = sum_r latent[t, r] * W_g[n, r]
+    with n = h * D + d indexing (head, dim) of the gate, i.e. G = latent @ W_g^T.
+      latent  [T, R]   bfloat16 bits (R = 1024: 4096 hidden / 4)
+      w_g     [N, R]   bfloat16 bits, out x in like a linear layer's weight (N = H * D)
+    Returns float64 [T, N] (no rounding)."""
+    return _widen_array(latent) @ _widen_array(w_g).T
+
+
+def attn_lowrank_gate(q, latent, w_g, tpos, k, v, kv_start, ck, cv, **kw) -> np.ndarray:
+    """HCA attention rows gated by sigmoid of the low-rank gate logits: the
+    ungated attention (``attn`` with G = +inf, whose sigmoid is exactly 1) times
+    1 / (1 + exp(-G)), G = ``gate_logits(latent, w_g)`` reshaped to [n, H, D]
+    (unrounded).  Returns float64 [n, H, D]."""
+    q = _u16(q)
+    n, H, D = q.shape
+    ungated = attn(q, np.full(q.shape, 0x7F80, np.uint16), tpos, k, v, kv_start, ck, cv, **kw)
+    G = gate_logits(latent, w_g).reshape(n, H, D)
+    return ungated / (1.0 + np.exp(-G))
+
+
+def attn_backward(q, g, dout, k, v, *, block=128, window=128, scale=None, nthreads=0):
+    """Gradients of a whole-sequence prefill (queries and raw rows at positions
+    0 .. T-1, entries = ``compress`` of k and v) for the upstream gradient dout
+    of the gated output (the training pass; blog.derekhsu.net, section 訓練基礎設施).
+    The attention part follows the chain rule row by row (C routine
+    ``hca_oracle_attn_backward``); then each entry's gradient reaches every raw row
+    of its block divided by the block size, the derivative of the mean (the
+    bfloat16 rounding of an entry is passed through as the identity).
+      q, g, dout [T, H, D], k, v [T, D]: bfloat16 bits
+    Returns float64 (dq [T, H, D], dk [T, D], dv [T, D], dg [T, H, D])."""
+    q, g, dout, k, v = _u16(q), _u16(g), _u16(dout), _u16(k), _u16(v)
+    T, H, D = q.shape
+    assert g.shape == q.shape and dout.shape == q.shape and k.shape == (T, D) == v.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    ck, cv = compress(k, block), compress(v, block)
+    Nc = ck.shape[0]
+    dq = np.empty((T, H, D)); dg = np.empty((T, H, D))
+    dk = np.empty((T, D)); dv = np.empty((T, D))
+    dck = np.zeros((max(Nc, 1), D)); dcv = np.zeros((max(Nc, 1), D))
+    rc = _load().hca_oracle_attn_backward(
+        _ptr(q), _ptr(g), _ptr(dout), T, _ptr(k), _ptr(v), _ptr(ck) if Nc else None,
+        _ptr(cv) if Nc else None, Nc, H, D, block, window, float(scale), _ptr(dq), _ptr(dg),
+        _ptr(dk), _ptr(dv), _ptr(dck), _ptr(dcv), int(nthreads))
+    if rc:
+        raise OracleError(f"hca_oracle_attn_backward: {rc}")
+    if Nc:
+        dk[:Nc * block] += np.repeat(dck[:Nc] / block, block, axis=0)
+        dv[:Nc * block] += np.repeat(dcv[:Nc] / block, block, axis=0)
+    return dq, dk, dv, dg

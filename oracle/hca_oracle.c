@@ -276,3 +276,161 @@ int hca_oracle_decode(const uint16_t *q, const uint16_t *g, const uint16_t *ck,
     }
     return failed ? ORACLE_ENOMEM : 0;
 }
+
+/*
+ * Backward pass of prefill attention over a whole sequence (queries at
+ * positions 0 .. T-1, raw rows 0 .. T-1, entries of blocks 0 .. Nc-1), for the
+ * training step of the layer (blog.derekhsu.net, section 訓練基礎設施: the
+ * pages' attention kernel runs both passes).  With, for one (t, h) row,
+ *   s_j = scale <q, k_j>,  p = softmax(s),  a = sum_j p_j v_j,
+ *   sig = 1 / (1 + exp(-g)),  o = a * sig,
+ * and the upstream gradient dO of o, the chain rule gives
+ *   dg   = dO * a * sig * (1 - sig)          da  = dO * sig
+ *   dp_j = <da, v_j>                         ds_j = p_j (dp_j - sum_i p_i dp_i)
+ *   dq   = scale * sum_j ds_j k_j
+ *   dk_j += scale * ds_j * q                 dv_j += p_j * da
+ * where key j is an entry (into dck, dcv) or a raw row (into dk, dv).  The
+ * gradients of the raw rows through the entries (every row of block b gets
+ * dck[b] / block, the mean's derivative) are added by the caller, so that this
+ * routine only follows the attention itself.
+ *   q, g, dout  [T, H, D]   bfloat16 bits
+ *   k, v        [T, D]      ck, cv [Nc, D]   bfloat16 bits
+ *   dq, dg      [T, H, D]   dk, dv [T, D]    dck, dcv [Nc, D]   double (overwritten)
+ * Each thread accumulates its own copy of dk, dv, dck, dcv; the copies are
+ * added in thread order at the end.
+ */
+int hca_oracle_attn_backward(const uint16_t *q, const uint16_t *g, const uint16_t *dout,
+                             int64_t T, const uint16_t *k, const uint16_t *v,
+                             const uint16_t *ck, const uint16_t *cv, int64_t Nc, int H, int D,
+                             int block, int window, double scale, double *dq, double *dg,
+                             double *dk, double *dv, double *dck, double *dcv, int nthreads)
+{
+    if (!q || !g || !dout || !k || !v || !dq || !dg || !dk || !dv || T < 0 || H <= 0 ||
+        D <= 0 || block <= 0 || window <= 0 || Nc < 0 || Nc > T / block)
+        return ORACLE_EBADARG;
+    if (Nc > 0 && (!ck || !cv || !dck || !dcv)) return ORACLE_EBADARG;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    if (nthreads > 8) nthreads = 8;
+    const int64_t maxkeys = Nc + window;
+    const size_t acc_n = (size_t)(T + Nc) * D;  /* rows 0..T-1 raw, T..T+Nc-1 entries */
+    double *acc_k = calloc((size_t)nthreads * acc_n, sizeof(double));
+    double *acc_v = calloc((size_t)nthreads * acc_n, sizeof(double));
+    if (!acc_k || !acc_v) {
+        free(acc_k);
+        free(acc_v);
+        return ORACLE_ENOMEM;
+    }
+    int failed = 0;
+
+#pragma omp parallel num_threads(nthreads)
+    {
+        const int tid = omp_get_thread_num();
+        double *ak = acc_k + (size_t)tid * acc_n, *av = acc_v + (size_t)tid * acc_n;
+        int64_t *kid = malloc(sizeof(*kid) * (size_t)maxkeys);   /* accumulator row of key j */
+        const uint16_t **keys = malloc(sizeof(*keys) * (size_t)maxkeys);
+        const uint16_t **vals = malloc(sizeof(*vals) * (size_t)maxkeys);
+        double *p = malloc(sizeof(*p) * (size_t)maxkeys);
+        double *dp = malloc(sizeof(*dp) * (size_t)maxkeys);
+        double *a = malloc(sizeof(*a) * (size_t)D);
+        double *da = malloc(sizeof(*da) * (size_t)D);
+        if (!kid || !keys || !vals || !p || !dp || !a || !da) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp barrier
+        if (!failed) {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < T * H; ++r) {
+                const int64_t t = r / H;
+                const size_t off = (size_t)r * D;
+                int64_t nk = 0;
+                for (int64_t b = 0; b < Nc; ++b) {
+                    if (b * block + block - 1 <= t) {
+                        keys[nk] = ck + b * D;
+                        vals[nk] = cv + b * D;
+                        kid[nk] = T + b;
+                        ++nk;
+                    }
+                }
+                const int64_t lo = t - window + 1 < 0 ? 0 : t - window + 1;
+                for (int64_t s = lo; s <= t; ++s) {
+                    keys[nk] = k + s * D;
+                    vals[nk] = v + s * D;
+                    kid[nk] = s;
+                    ++nk;
+                }
+                /* forward: weights and the ungated output */
+                double m = -INFINITY;
+                for (int64_t j = 0; j < nk; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += widen_bf16(q[off + d]) * widen_bf16(keys[j][d]);
+                    p[j] = scale * dot;
+                    if (p[j] > m) m = p[j];
+                }
+                double z = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    p[j] = exp(p[j] - m);
+                    z += p[j];
+                }
+                for (int64_t j = 0; j < nk; ++j) p[j] /= z;
+                for (int d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < nk; ++j) acc += p[j] * widen_bf16(vals[j][d]);
+                    a[d] = acc;
+                }
+                /* gate and its gradient */
+                for (int d = 0; d < D; ++d) {
+                    const double sig = 1.0 / (1.0 + exp(-widen_bf16(g[off + d])));
+                    const double go = widen_bf16(dout[off + d]);
+                    dg[off + d] = go * a[d] * sig * (1.0 - sig);
+                    da[d] = go * sig;
+                }
+                /* softmax backward */
+                double dsum = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += da[d] * widen_bf16(vals[j][d]);
+                    dp[j] = dot;
+                    dsum += p[j] * dot;
+                }
+                for (int d = 0; d < D; ++d) dq[off + d] = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    const double ds = p[j] * (dp[j] - dsum);
+                    double *akj = ak + (size_t)kid[j] * D, *avj = av + (size_t)kid[j] * D;
+                    for (int d = 0; d < D; ++d) {
+                        dq[off + d] += scale * ds * widen_bf16(keys[j][d]);
+                        akj[d] += scale * ds * widen_bf16(q[off + d]);
+                        avj[d] += p[j] * da[d];
+                    }
+                }
+            }
+        }
+        free(kid);
+        free(keys);
+        free(vals);
+        free(p);
+        free(dp);
+        free(a);
+        free(da);
+    }
+    if (!failed) {
+        for (size_t i = 0; i < acc_n; ++i) {
+            double sk = 0.0, sv = 0.0;
+            for (int th = 0; th < nthreads; ++th) {
+                sk += acc_k[(size_t)th * acc_n + i];
+                sv += acc_v[(size_t)th * acc_n + i];
+            }
+            const size_t row = i / (size_t)D;
+            if (row < (size_t)T) {
+                dk[i] = sk;
+                dv[i] = sv;
+            } else {
+                dck[i - (size_t)T * D] = sk;
+                dcv[i - (size_t)T * D] = sv;
+            }
+        }
+    }
+    free(acc_k);
+    free(acc_v);
+    return failed ? ORACLE_ENOMEM : 0;
+}

@@ -84,3 +84,27 @@ def sdpa_causal(q, g, k, v, scale):
     o = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, is_causal=True, scale=scale)
     gate = torch.sigmoid(torch.from_numpy(widen(g)).permute(1, 0, 2))
     return (o * gate).permute(1, 0, 2).numpy()
+
+
+def dense_attention_f64(qf, gf, kf, vf, block, window, scale):
+    """The layer's forward pass from float64 arrays with no rounding anywhere
+    (entries are the exact block means of kf, vf): a dense key matrix, a boolean
+    visibility matrix, softmax, values, sigmoid gate.  Used for finite
+    differences and as the autograd graph for the backward pins."""
+    T, H, D = qf.shape
+    nc = T // block
+    ckf = kf[:nc * block].reshape(nc, block, D).mean(axis=1)
+    cvf = vf[:nc * block].reshape(nc, block, D).mean(axis=1)
+    kaug = np.concatenate([kf, ckf], axis=0)
+    vaug = np.concatenate([vf, cvf], axis=0)
+    pos = np.arange(T)
+    block_last = np.arange(nc) * block + (block - 1)
+    t = pos[:, None]
+    visible = np.concatenate([(pos[None, :] <= t) & (pos[None, :] > t - window),
+                              block_last[None, :] <= t], axis=1)
+    s = scale * np.einsum("thd,jd->thj", qf, kaug)
+    s = np.where(visible[:, None, :], s, -np.inf)
+    s = s - s.max(axis=2, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=2, keepdims=True)
+    return np.einsum("thj,jd->thd", p, vaug) / (1.0 + np.exp(-gf))

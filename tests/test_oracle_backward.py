@@ -1,0 +1,183 @@
+"""Pins of the oracle's backward pass (``oracle.attn_backward``), independent of
+it: central finite differences of an fp64 forward written separately
+(tests/_independent.py), torch autograd on an fp64 dense masked attention,
+closed forms of the gate, and planted mistakes that the battery must catch.
+CPU only."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._independent import dense_attention_f64, widen
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _dyadic(seed, shape, lo=-16, hi=16):
+    """bf16 bits of multiples of 1/8 in [lo/8, hi/8]: block means of four such rows
+    are exact in bf16, so the oracle's rounded entries equal the exact means."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(lo, hi + 1, size=shape).astype(np.float32) / 8
+    return synth.f32_to_bf16_bits(x)
+
+
+def _inputs(seed, T, H, D):
+    q = synth.normal_bf16(seed, synth.Q, (T, H, D))
+    g = synth.normal_bf16(seed, synth.G, (T, H, D))
+    do = synth.normal_bf16(seed, 12, (T, H, D))
+    k, v = _dyadic(seed, (T, D)), _dyadic(seed + 1, (T, D))
+    return q, g, do, k, v
+
+
+def _fd_check(q, g, do, k, v, block, window, scale, n_coords=24, seed=0):
+    """Central differences of L = sum(dO * out) at random coordinates of q, g, k,
+    v against the oracle's gradients.  Returns the worst relative error."""
+    dq, dk, dv, dg = oracle.attn_backward(q, g, do, k, v, block=block, window=window,
+                                          scale=scale)
+    base = dict(q=widen(q), g=widen(g), k=widen(k), v=widen(v))
+    dof = widen(do)
+    grads = dict(q=dq, g=dg, k=dk, v=dv)
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    h = 1e-6
+
+    def loss(x):
+        out = dense_attention_f64(x["q"], x["g"], x["k"], x["v"], block, window, scale)
+        return float((dof * out).sum())
+
+    for name, arr in base.items():
+        for _ in range(n_coords):
+            idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            xp = {kk: vv.copy() for kk, vv in base.items()}
+            xm = {kk: vv.copy() for kk, vv in base.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd = (loss(xp) - loss(xm)) / (2 * h)
+            an = grads[name][idx]
+            worst = max(worst, abs(fd - an) / max(1e-3, abs(fd)))
+    return worst
+
+
+def test_finite_differences_small_blocks():
+    # block = window = 4, D = 8: entries, window edges and ragged tails all occur
+    q, g, do, k, v = _inputs(1, 23, 2, 8)
+    assert _fd_check(q, g, do, k, v, 4, 4, 0.35) < 1e-6
+
+
+def test_finite_differences_window_longer_than_block():
+    q, g, do, k, v = _inputs(2, 30, 3, 8)
+    assert _fd_check(q, g, do, k, v, 4, 7, 0.3, seed=1) < 1e-6
+
+
+def _torch_reference(q, g, do, k, v, block, window, scale):
+    """fp64 autograd through a dense masked attention whose entries are the block
+    means of k and v (in the graph, so their gradients reach every row)."""
+    qf, gf, kf, vf = (torch.tensor(widen(x), requires_grad=True) for x in (q, g, k, v))
+    T, H, D = qf.shape
+    nc = T // block
+    ck = kf[:nc * block].reshape(nc, block, D).mean(1)
+    cv = vf[:nc * block].reshape(nc, block, D).mean(1)
+    kaug, vaug = torch.cat([kf, ck]), torch.cat([vf, cv])
+    pos = torch.arange(T)
+    t = pos[:, None]
+    vis = torch.cat([(pos[None] <= t) & (pos[None] > t - window),
+                     (torch.arange(nc) * block + block - 1)[None] <= t], dim=1)
+    s = scale * torch.einsum("thd,jd->thj", qf, kaug)
+    s = s.masked_fill(~vis[:, None, :], float("-inf"))
+    out = torch.einsum("thj,jd->thd", torch.softmax(s, dim=2), vaug) * torch.sigmoid(gf)
+    out.backward(torch.tensor(widen(do)))
+    return qf.grad.numpy(), kf.grad.numpy(), vf.grad.numpy(), gf.grad.numpy()
+
+
+def test_torch_autograd_real_constants():
+    # block = window = 128, T = 300: two entries; K and V constant within each
+    # 128-row block, so the oracle's bf16 entries are the exact means
+    T, H, D = 300, 2, 32
+    q = synth.normal_bf16(3, synth.Q, (T, H, D))
+    g = synth.normal_bf16(3, synth.G, (T, H, D))
+    do = synth.normal_bf16(3, 12, (T, H, D))
+    kb = synth.normal_bf16(3, synth.K, (3, D))
+    vb = synth.normal_bf16(3, synth.V, (3, D))
+    k = np.repeat(kb, 128, axis=0)[:T].copy()
+    v = np.repeat(vb, 128, axis=0)[:T].copy()
+    got = oracle.attn_backward(q, g, do, k, v, scale=D ** -0.5)
+    want = _torch_reference(q, g, do, k, v, 128, 128, D ** -0.5)
+    for a, b, name in zip(got, want, ["dq", "dk", "dv", "dg"]):
+        np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+def test_torch_autograd_causal_only():
+    # T <= 127 with window 128: plain causal attention, no entries
+    T, H, D = 100, 3, 16
+    q, g, do = (synth.normal_bf16(4, i, (T, H, D)) for i in (synth.Q, synth.G, 12))
+    k, v = synth.normal_bf16(4, synth.K, (T, D)), synth.normal_bf16(4, synth.V, (T, D))
+    got = oracle.attn_backward(q, g, do, k, v, scale=0.25)
+    want = _torch_reference(q, g, do, k, v, 128, 128, 0.25)
+    for a, b, name in zip(got, want, ["dq", "dk", "dv", "dg"]):
+        np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+def test_gate_closed_forms():
+    T, H, D = 40, 2, 8
+    q, g, do, k, v = _inputs(5, T, H, D)
+    # sigmoid(+inf) = 1: the gate's own gradient sig (1 - sig) is exactly 0
+    dq, dk, dv, dg = oracle.attn_backward(q, np.full(q.shape, 0x7F80, np.uint16), do, k, v,
+                                          block=4, window=4)
+    assert np.all(dg == 0)
+    # sigmoid(-inf) = 0: nothing reaches the attention and the gate's gradient is 0
+    grads = oracle.attn_backward(q, np.full(q.shape, 0xFF80, np.uint16), do, k, v, block=4,
+                                 window=4)
+    assert all(np.all(x == 0) for x in grads)
+    # no upstream gradient: every gradient is 0
+    grads = oracle.attn_backward(q, g, np.zeros_like(do), k, v, block=4, window=4)
+    assert all(np.all(x == 0) for x in grads)
+
+
+def test_values_gradient_sums_to_upstream():
+    # each row's weights sum to 1, so the value gradients (raw rows plus entries,
+    # before pooling) add up to the sum over rows of dO * sigmoid(g)
+    T, H, D = 37, 2, 8
+    q, g, do, k, v = _inputs(6, T, H, D)
+    _, _, dv, _ = oracle.attn_backward(q, g, do, k, v, block=4, window=4)
+    want = (widen(do) / (1 + np.exp(-widen(g)))).sum(axis=(0, 1))
+    np.testing.assert_allclose(dv.sum(axis=0), want, rtol=1e-12, atol=1e-12)
+
+
+MUTANTS = {
+    "no_softmax_centering": ("const double ds = p[j] * (dp[j] - dsum);",
+                             "const double ds = p[j] * dp[j];"),
+    "ds_without_weight": ("const double ds = p[j] * (dp[j] - dsum);",
+                          "const double ds = (dp[j] - dsum);"),
+    "dk_without_scale": ("akj[d] += scale * ds * widen_bf16(q[off + d]);",
+                         "akj[d] += ds * widen_bf16(q[off + d]);"),
+    "dv_from_scores": ("avj[d] += p[j] * da[d];", "avj[d] += ds * da[d];"),
+    "gate_grad_sign": ("dg[off + d] = go * a[d] * sig * (1.0 - sig);",
+                       "dg[off + d] = go * a[d] * sig * (1.0 + sig);"),
+    "ungated_upstream": ("da[d] = go * sig;", "da[d] = go;"),
+    "entries_not_seen": ("kid[nk] = T + b;", "kid[nk] = b;"),
+}
+
+
+@pytest.fixture()
+def mutant(tmp_path, request, monkeypatch):
+    name = request.param
+    src = open(oracle.SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path_c = tmp_path / f"{name}.c"
+    path_c.write_text(src.replace(old, new))
+    path_so = tmp_path / f"{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared",
+                           "-ffp-contract=off", str(path_c), "-o", str(path_so), "-lm"])
+    monkeypatch.setattr(oracle, "_lib", oracle.bind(ctypes.CDLL(str(path_so))))
+    return name
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), indirect=True)
+def test_backward_mutant_is_caught(mutant):
+    q, g, do, k, v = _inputs(1, 23, 2, 8)
+    assert _fd_check(q, g, do, k, v, 4, 4, 0.35, n_coords=12) > 1e-4, mutant
