@@ -215,6 +215,23 @@ hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck,
                                    int M, int H, int D, int block, int window, float scale,
                                    void* out, hca_dtype_t out_dtype, void* stream);
 
+/*
+ * Gate logits of the low-rank gate (blog.derekhsu.net, section 潛在閘控稀疏注意力, the
+ * 低秩閘控注意力 item: the gate comes from the query's low-rank latent, several times
+ * narrower than the hidden state; yilup.net, section 架構設計):
+ *   g[t, n] = sum_r latent[t, r] * w_g[n, r]      (g = latent w_g^T)
+ * accumulated in fp32 and rounded to nearest-even bf16.  With n = h * D + d, g is the
+ * [T, H, D] gate-logit tensor hca_attn_prefill takes, so the low-rank gated prefill is
+ * this call followed by hca_attn_prefill on g.
+ *   latent  device, bf16 [T, R]
+ *   w_g     device, bf16 [N, R]    (out x in, like a linear layer's weight)
+ *   g       device, bf16 [T, N]    (overwritten)
+ * R a multiple of 32 from 32 to 16384, N a multiple of 2048 up to 65536 (H * 512 with
+ * H a multiple of 4), else HCA_ERR_UNSUPPORTED.  T = 0 is a no-op.
+ */
+hca_status_t hca_gate_logits(const void* latent, const void* w_g, int64_t T, int R, int N,
+                             void* g, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,8 @@ def lib():
         L.hca_attn_decode.restype = I
         L.hca_attn_decode_noalloc.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, F, P, I, P]
         L.hca_attn_decode_noalloc.restype = I
+        L.hca_gate_logits.argtypes = [P, P, I64, I, I, P, P]
+        L.hca_gate_logits.restype = I
         L.hca_attn_decode_multi.argtypes = [P, P, P, P, I64, P, P, P, P, P, I, I, I, I, I, I, F,
                                             P, I, P]
         L.hca_attn_decode_multi.restype = I
@@ -297,3 +299,32 @@ def hca_attn_prefill_vha(q, g, k, v, ck, cv, up, down, out, *, q_start: int = 0,
         _dev_ptr(up, "up", torch.bfloat16), _dev_ptr(down, "down", torch.bfloat16), r,
         _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
         _stream(q.device)))
+
+
+def hca_gate_logits(latent, w_g, g):
+    """g [T, N] (or [T, H, 512] with N = H * 512) <- bf16(latent [T, R] @ w_g [N, R]^T):
+    the logits of the low-rank gate."""
+    import torch
+    if latent.dim() != 2 or w_g.dim() != 2 or w_g.shape[1] != latent.shape[1]:
+        raise ValueError("latent must be [T, R] and w_g [N, R]")
+    T, R = latent.shape
+    N = w_g.shape[0]
+    if g.numel() != T * N or g.shape[0] != T:
+        raise ValueError(f"g must hold [{T}, {N}]")
+    _same_device(latent, w_g, g)
+    _check(lib().hca_gate_logits(_dev_ptr(latent, "latent", torch.bfloat16),
+                                 _dev_ptr(w_g, "w_g", torch.bfloat16), T, R, N,
+                                 _dev_ptr(g, "g", torch.bfloat16), _stream(latent.device)))
+
+
+def hca_attn_prefill_lowrank_gate(q, latent, w_g, k, v, ck, cv, out, *, g=None, q_start: int = 0,
+                                  kv_start: int = 0, scale: float | None = None):
+    """HCA prefill gated by the low-rank gate: g = latent @ w_g^T (hca_gate_logits, into
+    ``g`` or a buffer allocated here) followed by hca_attn_prefill on it."""
+    import torch
+    Tq, H, Dd = q.shape
+    if g is None:
+        g = torch.empty((Tq, H, Dd), dtype=torch.bfloat16, device=q.device)
+    hca_gate_logits(latent, w_g, g)
+    hca_attn_prefill(q, g, k, v, ck, cv, out, q_start=q_start, kv_start=kv_start, scale=scale)
+    return g

@@ -337,6 +337,24 @@ hca_status_t hca_attn_decode_noalloc(const void* q, const void* g, const void* c
                     "hca_attn_decode_noalloc launch");
 }
 
+hca_status_t hca_gate_logits(const void* latent, const void* w_g, int64_t T, int R, int N,
+                             void* g, void* stream) {
+  if (T < 0) return fail(HCA_ERR_INVALID_ARG, "T = %lld < 0", (long long)T);
+  if (R < 32 || R > 16384 || R % 32 != 0)
+    return fail(HCA_ERR_UNSUPPORTED, "R = %d (need a multiple of 32, 32 .. 16384)", R);
+  if (N < 2048 || N > 65536 || N % 2048 != 0)
+    return fail(HCA_ERR_UNSUPPORTED, "N = %d (need a multiple of 2048, at most 65536)", N);
+  if (T > ((int64_t)1 << 40)) return fail(HCA_ERR_UNSUPPORTED, "T beyond 2^40");
+  if (T == 0) return ok();
+  TRY(check_ptr(latent, "latent"));
+  TRY(check_ptr(w_g, "w_g"));
+  TRY(check_ptr(g, "g"));
+  return hip_status(hca::launch_gate(static_cast<const uint16_t*>(latent),
+                                     static_cast<const uint16_t*>(w_g), static_cast<uint16_t*>(g),
+                                     T, R, N, static_cast<hipStream_t>(stream)),
+                    "hca_gate_logits launch");
+}
+
 hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck, const void* cv,
                                    int64_t nc_cap, const void* wk, const void* wv,
                                    const void* nk, const void* nv, const int64_t* pos, int B,

@@ -1,0 +1,199 @@
+// gate.hip - gate logits of the low-rank gate on gfx950: G = latent * W_g^T.
+//
+// The gate that multiplies the attention output is computed from the query's
+// low-rank latent, several times narrower than the hidden state
+// (blog.derekhsu.net, section 潛在閘控稀疏注意力, the 低秩閘控注意力 item;
+// yilup.net, section 架構設計): G[t, n] = sum_r latent[t, r] * W_g[n, r], with
+// n = h * 512 + d indexing the (head, dim) of the gate.  The prefill kernel
+// applies sigmoid(G) in its epilogue.
+//
+// A plain bf16 GEMM with fp32 accumulation, both operands K-contiguous
+// (latent [T, R] row major, W_g [N, R] like a linear layer's weight):
+//   * a workgroup computes a 256 (n) x 256 (t) tile of G^T, four waves of
+//     128 x 128, each 4 x 4 MFMA 32x32x16 blocks with the accumulators in
+//     AGPRs; computing G^T puts four consecutive n of one t in each lane, so
+//     the epilogue stores 8 contiguous bytes per lane;
+//   * K advances 32 at a time through four LDS stages (32 KiB each), filled by
+//     DMA three steps ahead; 64-byte rows are stored with their 16-byte chunks
+//     permuted (chunk c of row i at c ^ ((i >> 2) & 3)), so the fragment reads
+//     of 8 lanes hit 8 different bank groups; the permutation is applied on
+//     the global side of the copy (each lane fetches the chunk that belongs at
+//     its LDS position);
+//   * tiles are dealt in groups of 4 (t) x 8 (n) per XCD, so the 32
+//     workgroups of a group read their latent and W_g slices from that XCD's
+//     L2 (12 slices instead of 64 per step).
+// Bound: MFMA (arithmetic intensity about 128 flop per byte per tile, more
+// with the L2 sharing).
+#include "hca_common.h"
+#include "hca_kernels.h"
+
+namespace hca {
+namespace {
+
+constexpr int kBT = 256, kBN = 256, kBK = 32;
+constexpr int kRowB = kBK * 2;              // 64 bytes per row per stage
+constexpr int kOpBytes = 256 * kRowB;       // one operand of one stage: 16 KiB
+constexpr int kStageB = 2 * kOpBytes;       // W_g then latent
+constexpr int kStages = 4;
+
+struct GateArgs {
+  const uint16_t* lat;  // [T, R]
+  const uint16_t* w;    // [N, R]
+  uint16_t* g;          // [T, N]
+  int64_t T;
+  int R, N;
+  int n_tiles_t, n_tiles_n;
+};
+
+// Position of 16-byte chunk c of row i inside its 64-byte LDS row.
+__device__ __forceinline__ int chunk_pos(int i, int c) { return c ^ ((i >> 2) & 3); }
+
+// DMA of one operand's 256 x 32 slice (columns k0 .. k0+31) into an LDS
+// stage: wave `wave` copies rows 64 wave .. 64 wave + 63, 16 rows (1 KiB) per
+// instruction; lane L writes LDS row r0 + L / 4, position L % 4, and fetches
+// the chunk stored there.
+__device__ __forceinline__ void dma_slice(__amdgpu_buffer_rsrc_t src, int ld_bytes, int k0,
+                                          uint8_t* dst, int wave, int lane) {
+  const int rr = lane >> 2, pos = lane & 3;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 64 * wave + 16 * u + rr;
+    const int c = pos ^ ((row >> 2) & 3);
+    dma16_buf(src, row * ld_bytes + 2 * k0 + 16 * c, (lds_void*)(dst + (64 * wave + 16 * u) * kRowB));
+  }
+}
+
+// MFMA with the accumulator pinned to AGPRs (inline asm: the builtin lets the
+// register allocator move accumulators between register files around the
+// loop).  The operands come from LDS reads, whose waits the compiler inserts;
+// no VALU instruction writes them.  The accumulators are zeroed long before
+// the first MFMA and read after mfma_drain().
+__device__ __forceinline__ void mfma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__global__ void __launch_bounds__(256, 1) gate_kernel(GateArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageB];
+
+  // blockIdx -> (t tile, n tile): consecutive workgroups of one XCD (blockIdx
+  // % 8) fill a group of 4 t tiles x 8 n tiles.
+  const int L = blockIdx.x;
+  const int x = L & 7, li = L >> 3;
+  const int grp = (li >> 5) * 8 + x, w32 = li & 31;
+  const int groups_n = a.n_tiles_n / 8;
+  const int tt = (grp / groups_n) * 4 + (w32 >> 3);
+  const int nt = (grp % groups_n) * 8 + (w32 & 7);
+  if (tt >= a.n_tiles_t) return;
+  const int64_t t0 = (int64_t)tt * kBT;
+  const int n0 = nt * kBN;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wa = wave >> 1, wb = wave & 1;  // n half, t half
+  const int ld = a.R * 2;
+  const int64_t t_rows = a.T - t0 < kBT ? a.T - t0 : kBT;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w + (int64_t)n0 * a.R, kBN * ld);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lat + t0 * a.R, (int)t_rows * ld);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int nk = a.R / kBK;
+  // Prologue: steps 0, 1, 2.
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (s < nk) {
+      dma_slice(rw, ld, s * kBK, lds + s * kStageB, wave, lane);
+      dma_slice(rl, ld, s * kBK, lds + s * kStageB + kOpBytes, wave, lane);
+    }
+  }
+  // Fragment offsets: lane (i = lane % 32, k half = lane / 32) of 32-row block
+  // bi reads row 32 bi + i, logical chunk 2 kk + lane / 32.
+  const int fi = lane & 31, fh = lane >> 5;
+
+  for (int s = 0; s < nk; ++s) {
+    // This wave's copies of step s have landed (steps s+1, s+2 may be in
+    // flight: 8 copies each), then every wave's, and every wave is done with
+    // step s-1, whose stage step s+3 reuses.
+    if (s + 2 < nk)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 16);  // vmcnt(16)
+    else if (s + 1 < nk)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 8);   // vmcnt(8)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+    barrier_no_fence();
+    if (s + 3 < nk) {
+      uint8_t* st = lds + ((s + 3) % kStages) * kStageB;
+      dma_slice(rw, ld, (s + 3) * kBK, st, wave, lane);
+      dma_slice(rl, ld, (s + 3) * kBK, st + kOpBytes, wave, lane);
+    }
+    const uint8_t* sw = lds + (s % kStages) * kStageB;
+    const uint8_t* sl = sw + kOpBytes;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const int r = 128 * wa + 32 * bi + fi;
+        af[bi] = *reinterpret_cast<const bf16x8*>(sw + r * kRowB + 16 * chunk_pos(r, 2 * kk + fh));
+      }
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) {
+        const int r = 128 * wb + 32 * bj + fi;
+        bfr[bj] = *reinterpret_cast<const bf16x8*>(sl + r * kRowB + 16 * chunk_pos(r, 2 * kk + fh));
+      }
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+          mfma32(acc[bi][bj], af[bi], bfr[bj]);
+    }
+  }
+
+  asm volatile("s_nop 15\n\ts_nop 15");  // wait states before VALU reads of the accumulators
+  // Epilogue: D[n][t] block (bi, bj): lane (t = lane % 32, half h), register r
+  // -> n = 8 (r / 4) + 4 h + r % 4.  Four consecutive n of one t: 8 bytes of a
+  // row of G, range checked against the last row.
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + t0 * a.N, (int)t_rows * a.N * 2);
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int t = 128 * wb + 32 * bj + fi;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int n = n0 + 128 * wa + 32 * bi + 8 * qq + 4 * fh;
+        const f32x16& c = acc[bi][bj];
+        typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+        const u32x2 v = {pack_bf16x2(c[4 * qq], c[4 * qq + 1]), pack_bf16x2(c[4 * qq + 2], c[4 * qq + 3])};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rg, (t * a.N + n) * 2, 0, 0);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gate(const uint16_t* latent, const uint16_t* w, uint16_t* g, int64_t T, int R,
+                       int N, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  GateArgs a;
+  a.lat = latent;
+  a.w = w;
+  a.g = g;
+  a.T = T;
+  a.R = R;
+  a.N = N;
+  a.n_tiles_t = (int)((T + kBT - 1) / kBT);
+  a.n_tiles_n = N / kBN;
+  // groups of 4 x 8 tiles; t tiles rounded up to a multiple of 4 (the extra
+  // workgroups exit at once), n tiles are a multiple of 8 (N % 2048 == 0)
+  const int64_t groups = (int64_t)((a.n_tiles_t + 3) / 4) * (a.n_tiles_n / 8);
+  const int64_t wgs = ((groups + 7) / 8) * 8 * 32;
+  hipLaunchKernelGGL(gate_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace hca
