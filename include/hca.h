@@ -232,6 +232,45 @@ hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck,
 hca_status_t hca_gate_logits(const void* latent, const void* w_g, int64_t T, int R, int N,
                              void* g, void* stream);
 
+/*
+ * Bytes of device workspace hca_attn_backward needs for T positions and H query heads:
+ * per query row its log-sum-exp and <dA, A> (fp32) and dA = dout * sigmoid(g) (bf16),
+ * plus the fp32 gradients of the floor(T/128) entries.  0 for T <= 0 or an unsupported
+ * shape.
+ */
+size_t hca_backward_workspace_size(int64_t T, int H, int D);
+
+/*
+ * Backward pass of a whole-sequence prefill (the training pass; the pages measure
+ * the attention kernel on both passes: blog.derekhsu.net, section 訓練基礎設施):
+ * queries and raw rows at positions 0 .. T-1, entries ck, cv of the Nc = floor(T/128)
+ * completed blocks as hca_compress writes them, output o = softmax-attention(q) *
+ * sigmoid(g) as hca_attn_prefill computes it (q_start = kv_start = 0).  For the
+ * upstream gradient dout = dL/do:
+ *   dg = dout * a * s * (1 - s),   a = ungated attention output, s = sigmoid(g)
+ *   dq = scale * sum_j p_j (<da, v_j> - <da, a>) k_j,   da = dout * s
+ *   dk[j], dv[j]: the same terms gathered per key; an entry's gradient is then
+ *   added to each raw row of its block divided by 128 (the derivative of the mean;
+ *   the bf16 rounding of the entry is passed through as the identity).
+ *   q, g, dout  device, bf16 [T, H, D]
+ *   k, v        device, bf16 [T, D]
+ *   ck, cv      device, bf16 [floor(T/128), D] (may be NULL if T < 128)
+ *   dq, dg      device, f32 [T, H, D]   (overwritten)
+ *   dk, dv      device, f32 [T, D]      (overwritten)
+ *   workspace   device, at least hca_backward_workspace_size(T, H, D) bytes, owned by
+ *               the caller (else HCA_ERR_WORKSPACE); contents on entry do not matter.
+ * 1 <= H <= 64 and T * H < 2^31 (else HCA_ERR_UNSUPPORTED).  The kernels recompute
+ * the forward's softmax with its rounding (weights rounded to bf16 for the value
+ * product); products take bf16 operands (weights, dA and the score gradients rounded
+ * to nearest even) with fp32 accumulation.  Entry gradients are summed with fp32
+ * atomics, so dk and dv are not bitwise reproducible from run to run.  T = 0 is a no-op.
+ */
+hca_status_t hca_attn_backward(const void* q, const void* g, const void* k, const void* v,
+                               const void* ck, const void* cv, const void* dout, int64_t T, int H,
+                               int D, int block, int window, float scale, void* dq, void* dk,
+                               void* dv, void* dg, void* workspace, size_t ws_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,11 @@ def lib():
         L.hca_attn_prefill_vha.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I,
                                            F, P, P, I, P, I, P]
         L.hca_attn_prefill_vha.restype = I
+        L.hca_backward_workspace_size.argtypes = [I64, I, I]
+        L.hca_backward_workspace_size.restype = ctypes.c_size_t
+        L.hca_attn_backward.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I, F, P, P, P, P, P,
+                                        ctypes.c_size_t, P]
+        L.hca_attn_backward.restype = I
         _lib = L
     return _lib
 
@@ -328,3 +333,55 @@ def hca_attn_prefill_lowrank_gate(q, latent, w_g, k, v, ck, cv, out, *, g=None, 
     hca_gate_logits(latent, w_g, g)
     hca_attn_prefill(q, g, k, v, ck, cv, out, q_start=q_start, kv_start=kv_start, scale=scale)
     return g
+
+
+def backward_workspace_size(T: int, H: int, D: int = D) -> int:
+    """Bytes of device workspace hca_attn_backward needs (0 for T = 0 or an
+    unsupported shape)."""
+    return int(lib().hca_backward_workspace_size(T, H, D))
+
+
+def hca_attn_backward(q, g, k, v, ck, cv, dout, dq, dk, dv, dg, *, scale: float | None = None,
+                      workspace=None, block: int = BLOCK, window: int = WINDOW):
+    """Gradients of a whole-sequence HCA prefill (queries and raw rows at positions
+    0 .. T-1, ck/cv the floor(T/128) entries of k/v) for the upstream gradient dout of
+    the gated output: dq, dg [T, H, 512] and dk, dv [T, 512], float32, overwritten.
+    An entry's gradient reaches each raw row of its block divided by 128.  workspace:
+    a device uint8 tensor of at least backward_workspace_size(T, H) bytes; allocated
+    here (through torch) when None."""
+    import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, D]")
+    T, H, Dd = q.shape
+    for t, name in ((g, "g"), (dout, "dout")):
+        _expect(t, q.shape, name)
+    for t, name in ((dq, "dq"), (dg, "dg")):
+        _expect(t, q.shape, name)
+    for t, name in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _expect(t, (T, Dd), name)
+    Nc = T // block
+    for t, name in ((ck, "ck"), (cv, "cv")):
+        if t is not None:
+            _expect(t, (t.shape[0], Dd), name)
+            if t.shape[0] < Nc:
+                raise ValueError(f"{name} holds {t.shape[0]} entries, {Nc} needed")
+        elif Nc > 0:
+            raise ValueError(f"{name} is needed for T >= {block}")
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (dg, "dg")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    _same_device(*(t for t in (q, g, k, v, ck, cv, dout, dq, dk, dv, dg) if t is not None))
+    if scale is None:
+        scale = Dd ** -0.5
+    need = backward_workspace_size(T, H, Dd) if T > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hca_attn_backward(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
+        _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+        _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
+        _dev_ptr(dout, "dout", torch.bfloat16), T, H, Dd, block, window, float(scale),
+        _dev_ptr(dq, "dq", torch.float32), _dev_ptr(dk, "dk", torch.float32),
+        _dev_ptr(dv, "dv", torch.float32), _dev_ptr(dg, "dg", torch.float32),
+        _dev_ptr(workspace, "workspace", optional=True), ws_bytes, _stream(q.device)))

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhca.so")
-SOURCES = ["api.cpp", "compress.hip", "prefill.hip", "decode.hip", "decode_sk.hip", "gate.hip"]
+SOURCES = ["api.cpp", "compress.hip", "prefill.hip", "decode.hip", "decode_sk.hip", "gate.hip",
+           "backward.hip"]
 HEADERS = ["hca_common.h", "hca_kernels.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

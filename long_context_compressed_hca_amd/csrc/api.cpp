@@ -38,6 +38,9 @@ hca_status_t check_ptr(const void* p, const char* name) {
   return HCA_OK;
 }
 
+// Query rows (T * H) and positions stay below 2^31: the kernels index them in 32 bits.
+constexpr int64_t kMaxRows = 0x7FFFFFFF;
+
 hca_status_t check_shape(int D, int block, int window) {
   if (D != hca::kD) return fail(HCA_ERR_UNSUPPORTED, "D = %d (only 512 is supported)", D);
   if (block != hca::kBlock)
@@ -377,6 +380,60 @@ hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck,
                                           static_cast<const uint16_t*>(nv), M, nullptr,
                                           static_cast<hipStream_t>(stream)),
                     "hca_attn_decode_multi launch");
+}
+
+size_t hca_backward_workspace_size(int64_t T, int H, int D) {
+  if (T <= 0 || H < 1 || H > 64 || D != hca::kD || T * H > kMaxRows) return 0;
+  return hca::backward_workspace_bytes(T, H);
+}
+
+hca_status_t hca_attn_backward(const void* q, const void* g, const void* k, const void* v,
+                               const void* ck, const void* cv, const void* dout, int64_t T, int H,
+                               int D, int block, int window, float scale, void* dq, void* dk,
+                               void* dv, void* dg, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  TRY(check_shape(D, block, window));
+  if (T < 0) return fail(HCA_ERR_INVALID_ARG, "T = %lld < 0", (long long)T);
+  if (H < 1 || H > 64) return fail(HCA_ERR_UNSUPPORTED, "H = %d (need 1 <= H <= 64)", H);
+  if (T * H > kMaxRows)
+    return fail(HCA_ERR_UNSUPPORTED, "T * H = %lld query rows (at most 2^31 - 1)",
+                (long long)(T * H));
+  TRY(check_scale(scale));
+  if (T == 0) return ok();
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(g, "g"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(v, "v"));
+  TRY(check_ptr(dout, "dout"));
+  TRY(check_ptr(dq, "dq"));
+  TRY(check_ptr(dk, "dk"));
+  TRY(check_ptr(dv, "dv"));
+  TRY(check_ptr(dg, "dg"));
+  if (T >= hca::kBlock) {
+    TRY(check_ptr(ck, "ck"));
+    TRY(check_ptr(cv, "cv"));
+  }
+  const size_t need = hca::backward_workspace_bytes(T, H);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(HCA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+  TRY(check_ptr(workspace, "workspace"));
+  hca::BackwardProblem p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.g = static_cast<const uint16_t*>(g);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.ck = static_cast<const uint16_t*>(ck);
+  p.cv = static_cast<const uint16_t*>(cv);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.dq = static_cast<float*>(dq);
+  p.dk = static_cast<float*>(dk);
+  p.dv = static_cast<float*>(dv);
+  p.dg = static_cast<float*>(dg);
+  p.T = T;
+  p.H = H;
+  p.scale = scale;
+  return hip_status(hca::launch_backward(p, workspace, static_cast<hipStream_t>(stream)),
+                    "hca_attn_backward launch");
 }
 
 }  // extern "C"

@@ -75,4 +75,18 @@ hipError_t launch_decode_sk(const DecodeProblem& p, const uint16_t* nk, const ui
 hipError_t launch_gate(const uint16_t* latent, const uint16_t* w, uint16_t* g, int64_t T, int R,
                        int N, hipStream_t stream);
 
+// Backward pass of a whole-sequence prefill (queries and raw rows at positions
+// 0 .. T-1, Nc = floor(T / 128) entries): fp32 gradients of q, g, k, v for the
+// upstream gradient dout of the gated output; an entry's gradient reaches the
+// raw rows of its block divided by 128.  Workspace: backward_workspace_bytes().
+struct BackwardProblem {
+  const uint16_t *q, *g, *k, *v, *ck, *cv, *dout;  // q, g, dout [T, H, 512]; k, v [T, 512]
+  float *dq, *dk, *dv, *dg;                         // dq, dg [T, H, 512]; dk, dv [T, 512]
+  int64_t T;
+  int H;
+  float scale;
+};
+size_t backward_workspace_bytes(int64_t T, int H);
+hipError_t launch_backward(const BackwardProblem& p, void* ws, hipStream_t stream);
+
 }  // namespace hca

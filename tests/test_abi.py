@@ -209,6 +209,46 @@ def test_decode_multi_noop(L):
     assert decode_multi(L, B=0) == OK
 
 
+def backward(L, **kw):
+    a = dict(q=P, g=P, k=P, v=P, ck=P, cv=P, dout=P, T=1000, H=64, D=512, block=128, window=128,
+             scale=512 ** -0.5, dq=P, dk=P, dv=P, dg=P, ws=P, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.hca_attn_backward(a["q"], a["g"], a["k"], a["v"], a["ck"], a["cv"], a["dout"],
+                               a["T"], a["H"], a["D"], a["block"], a["window"], a["scale"],
+                               a["dq"], a["dk"], a["dv"], a["dg"], a["ws"], a["ws_bytes"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=256), UNSUPPORTED), (dict(block=64), UNSUPPORTED), (dict(window=256), UNSUPPORTED),
+    (dict(H=0), UNSUPPORTED), (dict(H=65), UNSUPPORTED), (dict(T=1 << 26), UNSUPPORTED),
+    (dict(T=-1), INVALID), (dict(scale=float("inf")), INVALID), (dict(q=0), INVALID),
+    (dict(dout=MIS), INVALID), (dict(dg=0), INVALID), (dict(ck=0), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1000), WORKSPACE), (dict(ws=MIS), INVALID),
+])
+def test_backward_rejects(L, kw, status):
+    assert backward(L, **kw) == status
+
+
+def test_backward_noop_and_optional_entries(L):
+    assert backward(L, T=0, q=0, ws=None, ws_bytes=0) == OK
+    # below one block there are no entries: ck, cv may be NULL (rejected later for
+    # the missing workspace, so nothing is launched)
+    assert backward(L, T=100, ck=0, cv=0, ws=None, ws_bytes=0) == WORKSPACE
+
+
+def test_backward_workspace_size(L):
+    # per query row 2 floats + 512 bf16 of dA, per entry 2 x 512 floats, each
+    # array 256-byte aligned, plus 256 bytes of alignment slack
+    up = lambda x: (x + 255) // 256 * 256
+    for T, H in [(1, 1), (1000, 64), (131072, 64), (257, 3)]:
+        rows, nc = T * H, T // 128
+        want = 2 * up(4 * rows) + up(1024 * rows) + 2 * up(2048 * nc) + 256
+        assert L.hca_backward_workspace_size(T, H, 512) == want
+    for bad in [(0, 64, 512), (100, 0, 512), (100, 65, 512), (100, 8, 256), (1 << 26, 64, 512)]:
+        assert L.hca_backward_workspace_size(*bad) == 0
+
+
 def compress(L, k=P, v=P, T=256, ld=512, D=512, block=128, ck=P, cv=P):
     return L.hca_compress(k, v, T, ld, D, block, ck, cv, None)
 
