@@ -243,6 +243,13 @@ size_t hca_decode_workspace_size(int B, int H, int D, int64_t nc_cap) {
   return hca::decode_workspace_bytes(B, H, nc_cap);
 }
 
+// decode.hip's kernels take whole head blocks of 16 and address a sequence's
+// entries through one buffer descriptor, whose 32-bit size holds fewer than 2^21
+// entries of 1 KiB; decode_sk.hip's (per-tile descriptors) take the rest.
+static bool whole_tile_kernel(int H, int64_t nc_cap) {
+  return H % 16 == 0 && nc_cap < ((int64_t)1 << 21);
+}
+
 // Checks shared by the decode entry points; fills p.
 static hca_status_t decode_check(const void* q, const void* g, const void* ck, const void* cv,
                                  int64_t nc_cap, const void* wk, const void* wv,
@@ -299,7 +306,7 @@ hca_status_t hca_attn_decode(const void* q, const void* g, const void* ck, const
                    out_dtype, p));
   if (B == 0) return ok();
   const size_t need = hca::decode_workspace_bytes(B, H, nc_cap);
-  if (need == 0 && H % 16 == 0)
+  if (need == 0 && whole_tile_kernel(H, nc_cap))
     // A batch that fills the GPU with one workgroup per 16 heads: the kernel
     // whose four waves walk each tile together (decode.hip) streams the keys
     // faster there.
@@ -330,7 +337,7 @@ hca_status_t hca_attn_decode_noalloc(const void* q, const void* g, const void* c
   if (need > hca::kDecodeWorkspaceMax)
     return fail(HCA_ERR_WORKSPACE, "needs %zu bytes of workspace, the built-in scratch holds %zu",
                 need, hca::kDecodeWorkspaceMax);
-  if (need == 0 && H % 16 == 0)
+  if (need == 0 && whole_tile_kernel(H, nc_cap))
     return hip_status(hca::launch_decode(p, static_cast<hipStream_t>(stream)),
                       "hca_attn_decode_noalloc launch");
   void* ws = nullptr;
@@ -369,7 +376,7 @@ hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck,
   if (B == 0) return ok();
   TRY(check_ptr(nk, "nk"));
   TRY(check_ptr(nv, "nv"));
-  if (H % 16 == 0)
+  if (whole_tile_kernel(H, nc_cap))
     // Head blocks of 16 rows: the kernel that gives one workgroup up to 4 blocks
     // of a sequence (decode.hip) reads each sequence's keys into fewer CUs.
     return hip_status(hca::launch_decode_multi(p, static_cast<const uint16_t*>(nk),
