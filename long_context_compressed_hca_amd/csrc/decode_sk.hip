@@ -298,15 +298,17 @@ template <bool MT>
 __global__ void __launch_bounds__(256, 1) decode_sk_kernel(SkArgs a) {
   __shared__ __attribute__((aligned(256))) uint8_t lds[kLdsBytes];
 
-  // blockIdx -> (sequence, head block, split): XCD x = blockIdx % 8 takes
-  // sequences x, x + 8, ... with all their workgroups.
+  // blockIdx -> (sequence, key split, head block): XCD x = blockIdx % 8 takes
+  // the (sequence, split) pairs x, x + 8, ... with all their head blocks, which
+  // walk the same tiles at the same time and share them through that XCD's
+  // L2.  The splits of one sequence go to different XCDs, so a small batch
+  // still spreads over the whole GPU.
   const int L = blockIdx.x;
-  const int per = a.n_hb * a.n_ks;
   const int k8 = L >> 3;
-  const int inner = k8 % per;
-  const int b = (k8 / per) * 8 + (L & 7);
+  const int pair = (k8 / a.n_hb) * 8 + (L & 7);
+  const int hb = k8 % a.n_hb;
+  const int b = pair / a.n_ks, ks = pair % a.n_ks;
   if (b >= a.B) return;
-  const int hb = inner / a.n_ks, ks = inner % a.n_ks;
   const int W = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4, lane16 = lane * 16;
   uint8_t* const st0 = lds + (2 * W) * kStage;
@@ -561,46 +563,48 @@ __global__ void __launch_bounds__(256, 1) decode_sk_kernel(SkArgs a) {
   }
 }
 
-// Merge of the n_ks partials of each (sequence, head block): thread (row
-// t / 16, dims 32 (t % 16) .. +31).
+// Merge of the n_ks partials of each (sequence, head block): workgroup
+// (b, hb, 64-dim chunk dc), thread (row t / 16, dims 64 dc + 4 (t % 16) .. +3).
+// The splits' loads are independent, so they are in flight together.
 __global__ void __launch_bounds__(256) combine_kernel(SkArgs a) {
-  const int b = blockIdx.x / a.n_hb, hb = blockIdx.x % a.n_hb;
-  const int rr = threadIdx.x >> 4, d0 = 32 * (threadIdx.x & 15);
+  const int dc = blockIdx.x & 7, bh = blockIdx.x >> 3;
+  const int b = bh / a.n_hb, hb = bh % a.n_hb;
+  const int rr = threadIdx.x >> 4, d = 64 * dc + 4 * (threadIdx.x & 15);
   const int row = 16 * hb + rr;
   if (row >= a.R) return;
   const float* part = a.ws + (int64_t)(b * a.n_hb + hb) * a.n_ks * kPart;
+  constexpr int kMaxSplits = 16;
+  float mk[kMaxSplits];
   float mstar = -INFINITY;
-  for (int k = 0; k < a.n_ks; ++k) mstar = fmaxf(mstar, part[k * kPart + rr]);
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k) {
+    mk[k] = k < a.n_ks ? part[k * kPart + rr] : -INFINITY;
+    mstar = fmaxf(mstar, mk[k]);
+  }
   float lstar = 0.0f;
-  for (int k = 0; k < a.n_ks; ++k) {
-    const float mk = part[k * kPart + rr];
-    lstar += mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - mstar) * part[k * kPart + 16 + rr];
+  f32x4 acc = {};
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k) {
+    if (k < a.n_ks) {
+      const float f = mk[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk[k] - mstar);
+      lstar += f * part[k * kPart + 16 + rr];
+      acc += f * *reinterpret_cast<const f32x4*>(part + k * kPart + 32 + rr * kD + d);
+    }
   }
   const float inv = 1.0f / lstar;
   const int64_t orow = (int64_t)b * a.R + row;
-  const uint16_t* grow = a.g + orow * kD;
-#pragma unroll 2
-  for (int v = 0; v < 8; ++v) {
-    const int d = d0 + 4 * v;
-    f32x4 acc = {};
-    for (int k = 0; k < a.n_ks; ++k) {
-      const float mk = part[k * kPart + rr];
-      const float f = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - mstar);
-      acc += f * *reinterpret_cast<const f32x4*>(part + k * kPart + 32 + rr * kD + d);
-    }
-    const uint2 g2 = *reinterpret_cast<const uint2*>(grow + d);
-    const float gv[4] = {bf16_bits_to_f32(g2.x & 0xFFFFu), bf16_bits_to_f32(g2.x >> 16),
-                         bf16_bits_to_f32(g2.y & 0xFFFFu), bf16_bits_to_f32(g2.y >> 16)};
-    float r[4];
+  const uint2 g2 = *reinterpret_cast<const uint2*>(a.g + orow * kD + d);
+  const float gv[4] = {bf16_bits_to_f32(g2.x & 0xFFFFu), bf16_bits_to_f32(g2.x >> 16),
+                       bf16_bits_to_f32(g2.y & 0xFFFFu), bf16_bits_to_f32(g2.y >> 16)};
+  float r[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = acc[e] * inv * sigmoid(gv[e]);
-    if (a.out_f32)
-      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * kD + d) =
-          make_float4(r[0], r[1], r[2], r[3]);
-    else
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * kD + d) =
-          make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
-  }
+  for (int e = 0; e < 4; ++e) r[e] = acc[e] * inv * sigmoid(gv[e]);
+  if (a.out_f32)
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * kD + d) =
+        make_float4(r[0], r[1], r[2], r[3]);
+  else
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * kD + d) =
+        make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
 }
 
 }  // namespace
@@ -614,7 +618,7 @@ int decode_splits(int B, int H, int64_t nc_cap) {
   const int64_t tiles = (nc_cap + kTile - 1) / kTile + kWindow / kTile;
   const int64_t cap = tiles / 8 > 1 ? tiles / 8 : 1;
   if (n > cap) n = (int)cap;
-  if (n > 16) n = 16;
+  if (n > 16) n = 16;  // combine_kernel merges at most 16 splits
   return n < 1 ? 1 : n;
 }
 
@@ -649,14 +653,15 @@ hipError_t launch_decode_sk(const DecodeProblem& p, const uint16_t* nk, const ui
   a.n_ks = multi ? 1 : decode_splits(p.B, p.H, p.nc_cap);
   a.c = p.scale * 1.4426950408889634f;
   a.out_f32 = p.out_f32 ? 1 : 0;
-  const dim3 grid((unsigned)(((p.B + 7) / 8) * 8 * a.n_hb * a.n_ks)), block(256);
+  const int64_t pairs = (int64_t)p.B * a.n_ks;
+  const dim3 grid((unsigned)(((pairs + 7) / 8) * 8 * a.n_hb)), block(256);
   if (multi)
     hipLaunchKernelGGL((decode_sk_kernel<true>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((decode_sk_kernel<false>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_ks == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.B * a.n_hb)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.B * a.n_hb * 8)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
