@@ -40,7 +40,13 @@ def build(verbose: bool = False) -> str:
                                                  stderr=subprocess.PIPE, text=True)))
     failed = []
     for src, cmd, p in procs:
-        out, err = p.communicate()
+        try:
+            out, err = p.communicate(timeout=900)
+        except subprocess.TimeoutExpired:
+            p.kill()
+            out, err = p.communicate()
+            failed.append((src, " ".join(cmd), "compiler did not finish within 900 s"))
+            continue
         err = _quiet(err)
         if verbose and (out.strip() or err.strip()):
             print(f"[{src}]\n{out}{err}", file=sys.stderr)

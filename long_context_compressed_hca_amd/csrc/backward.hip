@@ -13,36 +13,47 @@
 // and an entry's gradient reaches each row of its block divided by 128 (the
 // derivative of the mean).
 //
-// Kernels (one wave = 16 query rows, or 16 keys; four waves per workgroup,
-// each on its own work with its own LDS):
-//   rows_kernel   per 16 flat rows (t, h): dA = dO * sig rounded to bf16 (kept
-//                 in the workspace for the key kernel); pass A walks the keys
-//                 with the decode kernel's fixed-reference softmax for the row
-//                 sum, a (for dg) and Dt = sum_j p_j <dA, v_j> from the same dA
-//                 and p the score gradients use, so that they sum to zero to fp32
-//                 rounding; then dg, the row statistics lse and Dt; pass B walks
-//                 the keys again for dq: S^T = K Q^T, P = 2^(x - lse),
-//                 dP^T = V dA^T, dS^T = P (dP^T - Dt), dQ^T += K^T dS^T (K^T by
-//                 transposing LDS reads);
-//   keys_kernel   per 16 keys (raw rows, or entries with a chunk of queries):
-//                 over the row blocks that see them, S = Q K^T, dP = dA V^T,
-//                 dS, then dV^T += dA^T P and dK^T += Q^T dS with Q and dA rows
-//                 copied into LDS and read transposed; raw keys are stored,
-//                 entries are added atomically (several chunks per entry);
+// Kernels (four waves per workgroup; one wave = 16 query rows, or 16 keys):
+//   rows_kernel   per 64 flat rows (t, h) (wave w: rows 16w .. 16w+15): dA =
+//                 dO * sig rounded to bf16 (kept in the workspace for the key
+//                 kernel); pass A walks the 32-key tiles of the keys any of the
+//                 64 rows sees, with the decode kernel's fixed-reference
+//                 softmax, for the row sum, a (for dg) and Dt = sum_j p_j
+//                 <dA, v_j> from the same dA and p the score gradients use, so
+//                 that they sum to zero to fp32 rounding; then dg, the row
+//                 statistics lse and Dt; pass B walks the tiles again for dq:
+//                 S^T = K Q^T, P = 2^(x - lse), dP^T = V dA^T,
+//                 dS^T = P (dP^T - Dt), dQ^T += K^T dS^T.
+//   keys_kernel   per 64 keys (wave w: keys 16w .. 16w+15, K and V fragments
+//                 in registers): over the 32-row blocks of queries that see
+//                 them, S = Q K^T, dP = dA V^T, dS, then dV^T += dA^T P and
+//                 dK^T += Q^T dS.  Raw keys are stored; entries are split into
+//                 tasks of 512 row blocks whose sums are added atomically.
 //   pool_kernel   dk, dv of raw rows += entry gradients / 128.
-// fp32 accumulation throughout; MFMA operands are bf16 (P, dS and dA rounded
-// to nearest even; P as in the forward).
+// Both main kernels stream their tiles (K and V; Q, dA and the row statistics)
+// global -> LDS by DMA through two stages, each wave copying a quarter of
+// every tile one tile ahead, and all four waves read every tile: as MFMA
+// fragments (16x16x32 score-shaped chains) and, for the products that contract
+// over keys or rows, with transposing reads (16x16x32 over the tile's 32 rows).
+// One barrier per tile.  fp32 accumulation throughout; MFMA operands are bf16
+// (P, dS and dA rounded to nearest even; P as in the forward).
 #include "hca_common.h"
 #include "hca_kernels.h"
 
 namespace hca {
 namespace {
 
-constexpr int kTile = 16;
-constexpr int kRow = 1024 + 64;          // LDS rows read transposed (conflict free)
-constexpr int kStage = kTile * kRow;     // 17408 bytes
+constexpr int kTile = 32;                // keys per tile (rows kernel), rows per block (keys kernel)
+// LDS row strides: rows that are also read with transposing reads sit 1024 +
+// 64 bytes apart (4 consecutive rows cover the banks once), rows read only as
+// b128 fragments 1024 + 16 apart (8 consecutive rows cover them once).
+constexpr int kRowT = 1024 + 64;
+constexpr int kRowF = 1024 + 16;
+constexpr int kStage = kTile * kRowT;    // one 32-row tile at either stride: 34816 bytes
 constexpr float kHeadroom = 64.0f;
-constexpr int kChunk = 4096;             // queries per entry task
+constexpr int kRowsPerWg = 64;
+constexpr int kKeysPerWg = 64;
+constexpr int kChunkRb = 512;            // row blocks per entry task
 
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -54,8 +65,8 @@ struct BwArgs {
   float *lse, *dt, *dck, *dcv;  // workspace: row statistics, entry gradients
   uint16_t* da;                 // workspace: dA rows, bf16 [T * H, 512]
   int64_t T;
-  int H, Nc, n_rb;              // rows blocks of 16 flat rows
-  int n_raw_tiles, n_ent_tasks, ent_chunks;
+  int H, Nc, n_rb;              // n_rb: blocks of kTile flat rows
+  int n_ent_tasks, n_chunks;    // entry tasks = entry groups x chunks of kChunkRb row blocks
   float c, scale;               // c = scale * log2(e)
 };
 
@@ -78,65 +89,136 @@ __device__ __forceinline__ float xsum32(float x) {
 __device__ __forceinline__ float sigmoid(float g) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
 }
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-// s_waitcnt vmcnt(0) / vmcnt(16) (vmcnt in bits 3:0 and 15:14), then a compiler
-// barrier so that no memory access moves across the wait.
-__device__ __forceinline__ void wait_vm0() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_vm16() {
-  __builtin_amdgcn_s_waitcnt(0x4F70);
+// s_waitcnt vmcnt(N) (vmcnt in bits 3:0 and 15:14), then a compiler barrier so
+// that no memory access moves across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
   asm volatile("" ::: "memory");
 }
 
 // The MFMAs are inline asm, so that accumulators and operands keep their
-// register files (see decode_sk.hip): each carries the 2 wait states a VALU
-// write of an operand needs, and the last of a chain the 16 a VALU read of its
-// result needs.
-//   score chain: d (VGPR) = A (VGPR) * B (AGPR)
-__device__ __forceinline__ void mfma_va_first(f32x4& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_va(f32x4& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_va_last(f32x4& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 15" : "+v"(d) : "v"(a), "a"(b));
-}
-//   same with both operands in VGPRs
-__device__ __forceinline__ void mfma_vv_first(f32x4& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_vv(f32x4& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_vv_last(f32x4& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 15" : "+v"(d) : "v"(a), "v"(b));
-}
+// register files (the builtins let the register allocator move accumulators
+// between AGPRs and VGPRs around loops).  mfma_drain gives the wait states a
+// VALU read of accumulators written by the last MFMAs needs.
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15"); }
 
-// O^T[512 dims x 16] += M^T P for a 16-row LDS tile M (rows kRow apart) read
-// with transposing reads, P (B operand, keys x columns) in registers; the
-// accumulators stay in AGPRs.  One asm block orders the 32 reads, their waits
-// and the 32 MFMAs (8 reads in flight while the previous 8 MFMAs issue).
-__device__ __forceinline__ void tr_tile(f32x4 (&o)[32], uint32_t ad, const i16x4& p) {
-  i16x4 t[32];
-#define HCA_RD(i) "ds_read_b64_tr_b16 %[t" #i "], %[ad] offset:" #i "*32\n\t"
-#define HCA_MF(i) "v_mfma_f32_16x16x16_bf16 %[o" #i "], %[t" #i "], %[p], %[o" #i "]\n\t"
+// O^T[512 dims x 16] += M^T P over a 32-row LDS tile M (rows kRowT apart),
+// with 16x16x32 MFMAs (full rate; the 16x16x16 form costs about as many cycles
+// for half the work).  The contraction index of lane group g4 is the 8 rows
+// {4 g4 .. 4 g4 + 3, 16 + 4 g4 .. 16 + 4 g4 + 3}: the A operand M^T comes from
+// two transposing reads, at ad (rows 4 g4 ..) and ad2 = ad + 16 rows, into the
+// two halves of one 4-register group, and P (B operand, 8 bf16 per lane) holds
+// the same rows in that order.  The groups are fixed registers v192 .. v255
+// (clobbered: inline asm cannot name the halves of an operand), a ring of 16:
+// the reads of 8 dim blocks are in flight while the previous 8 blocks' MFMAs
+// issue, and a group is refilled only after the MFMA reading it has issued and
+// the reads in between have been waited for.  Accumulators in AGPRs.
+__device__ __forceinline__ void tr_tile32(f32x4 (&o)[32], uint32_t ad, uint32_t ad2, const bf16x8& p) {
   asm volatile(
-      HCA_RD(0) HCA_RD(1) HCA_RD(2) HCA_RD(3) HCA_RD(4) HCA_RD(5) HCA_RD(6) HCA_RD(7)
-      HCA_RD(8) HCA_RD(9) HCA_RD(10) HCA_RD(11) HCA_RD(12) HCA_RD(13) HCA_RD(14) HCA_RD(15)
-      "s_waitcnt lgkmcnt(8)\n\t"
-      HCA_MF(0) HCA_MF(1) HCA_MF(2) HCA_MF(3) HCA_MF(4) HCA_MF(5) HCA_MF(6) HCA_MF(7)
-      HCA_RD(16) HCA_RD(17) HCA_RD(18) HCA_RD(19) HCA_RD(20) HCA_RD(21) HCA_RD(22) HCA_RD(23)
-      "s_waitcnt lgkmcnt(8)\n\t"
-      HCA_MF(8) HCA_MF(9) HCA_MF(10) HCA_MF(11) HCA_MF(12) HCA_MF(13) HCA_MF(14) HCA_MF(15)
-      HCA_RD(24) HCA_RD(25) HCA_RD(26) HCA_RD(27) HCA_RD(28) HCA_RD(29) HCA_RD(30) HCA_RD(31)
-      "s_waitcnt lgkmcnt(8)\n\t"
-      HCA_MF(16) HCA_MF(17) HCA_MF(18) HCA_MF(19) HCA_MF(20) HCA_MF(21) HCA_MF(22) HCA_MF(23)
+      "ds_read_b64_tr_b16 v[192:193], %[ad] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[194:195], %[ad2] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[196:197], %[ad] offset:32\n\t"
+      "ds_read_b64_tr_b16 v[198:199], %[ad2] offset:32\n\t"
+      "ds_read_b64_tr_b16 v[200:201], %[ad] offset:64\n\t"
+      "ds_read_b64_tr_b16 v[202:203], %[ad2] offset:64\n\t"
+      "ds_read_b64_tr_b16 v[204:205], %[ad] offset:96\n\t"
+      "ds_read_b64_tr_b16 v[206:207], %[ad2] offset:96\n\t"
+      "ds_read_b64_tr_b16 v[208:209], %[ad] offset:128\n\t"
+      "ds_read_b64_tr_b16 v[210:211], %[ad2] offset:128\n\t"
+      "ds_read_b64_tr_b16 v[212:213], %[ad] offset:160\n\t"
+      "ds_read_b64_tr_b16 v[214:215], %[ad2] offset:160\n\t"
+      "ds_read_b64_tr_b16 v[216:217], %[ad] offset:192\n\t"
+      "ds_read_b64_tr_b16 v[218:219], %[ad2] offset:192\n\t"
+      "ds_read_b64_tr_b16 v[220:221], %[ad] offset:224\n\t"
+      "ds_read_b64_tr_b16 v[222:223], %[ad2] offset:224\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:288\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:288\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:320\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:320\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:352\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:352\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:384\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:384\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:416\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:416\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:448\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:448\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:480\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:480\n\t"
+      "s_waitcnt lgkmcnt(15)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o0], v[192:195], %[p], %[o0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o1], v[196:199], %[p], %[o1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o2], v[200:203], %[p], %[o2]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o3], v[204:207], %[p], %[o3]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o4], v[208:211], %[p], %[o4]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o5], v[212:215], %[p], %[o5]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o6], v[216:219], %[p], %[o6]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o7], v[220:223], %[p], %[o7]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      HCA_MF(24) HCA_MF(25) HCA_MF(26) HCA_MF(27) HCA_MF(28) HCA_MF(29) HCA_MF(30) HCA_MF(31)
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[192:193], %[ad] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[194:195], %[ad2] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[196:197], %[ad] offset:544\n\t"
+      "ds_read_b64_tr_b16 v[198:199], %[ad2] offset:544\n\t"
+      "ds_read_b64_tr_b16 v[200:201], %[ad] offset:576\n\t"
+      "ds_read_b64_tr_b16 v[202:203], %[ad2] offset:576\n\t"
+      "ds_read_b64_tr_b16 v[204:205], %[ad] offset:608\n\t"
+      "ds_read_b64_tr_b16 v[206:207], %[ad2] offset:608\n\t"
+      "ds_read_b64_tr_b16 v[208:209], %[ad] offset:640\n\t"
+      "ds_read_b64_tr_b16 v[210:211], %[ad2] offset:640\n\t"
+      "ds_read_b64_tr_b16 v[212:213], %[ad] offset:672\n\t"
+      "ds_read_b64_tr_b16 v[214:215], %[ad2] offset:672\n\t"
+      "ds_read_b64_tr_b16 v[216:217], %[ad] offset:704\n\t"
+      "ds_read_b64_tr_b16 v[218:219], %[ad2] offset:704\n\t"
+      "ds_read_b64_tr_b16 v[220:221], %[ad] offset:736\n\t"
+      "ds_read_b64_tr_b16 v[222:223], %[ad2] offset:736\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o8], v[224:227], %[p], %[o8]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o9], v[228:231], %[p], %[o9]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o10], v[232:235], %[p], %[o10]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o11], v[236:239], %[p], %[o11]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o12], v[240:243], %[p], %[o12]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o13], v[244:247], %[p], %[o13]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o14], v[248:251], %[p], %[o14]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o15], v[252:255], %[p], %[o15]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:800\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:800\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:832\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:832\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:864\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:864\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:896\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:896\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:928\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:928\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:960\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:960\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:992\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:992\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o16], v[192:195], %[p], %[o16]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o17], v[196:199], %[p], %[o17]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o18], v[200:203], %[p], %[o18]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o19], v[204:207], %[p], %[o19]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o20], v[208:211], %[p], %[o20]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o21], v[212:215], %[p], %[o21]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o22], v[216:219], %[p], %[o22]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o23], v[220:223], %[p], %[o23]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o24], v[224:227], %[p], %[o24]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o25], v[228:231], %[p], %[o25]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o26], v[232:235], %[p], %[o26]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o27], v[236:239], %[p], %[o27]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o28], v[240:243], %[p], %[o28]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o29], v[244:247], %[p], %[o29]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o30], v[248:251], %[p], %[o30]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o31], v[252:255], %[p], %[o31]"
       : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]),
         [o4] "+a"(o[4]), [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]),
         [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]), [o11] "+a"(o[11]),
@@ -144,23 +226,13 @@ __device__ __forceinline__ void tr_tile(f32x4 (&o)[32], uint32_t ad, const i16x4
         [o16] "+a"(o[16]), [o17] "+a"(o[17]), [o18] "+a"(o[18]), [o19] "+a"(o[19]),
         [o20] "+a"(o[20]), [o21] "+a"(o[21]), [o22] "+a"(o[22]), [o23] "+a"(o[23]),
         [o24] "+a"(o[24]), [o25] "+a"(o[25]), [o26] "+a"(o[26]), [o27] "+a"(o[27]),
-        [o28] "+a"(o[28]), [o29] "+a"(o[29]), [o30] "+a"(o[30]), [o31] "+a"(o[31]),
-        [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]),
-        [t4] "=&v"(t[4]), [t5] "=&v"(t[5]), [t6] "=&v"(t[6]), [t7] "=&v"(t[7]),
-        [t8] "=&v"(t[8]), [t9] "=&v"(t[9]), [t10] "=&v"(t[10]), [t11] "=&v"(t[11]),
-        [t12] "=&v"(t[12]), [t13] "=&v"(t[13]), [t14] "=&v"(t[14]), [t15] "=&v"(t[15]),
-        [t16] "=&v"(t[16]), [t17] "=&v"(t[17]), [t18] "=&v"(t[18]), [t19] "=&v"(t[19]),
-        [t20] "=&v"(t[20]), [t21] "=&v"(t[21]), [t22] "=&v"(t[22]), [t23] "=&v"(t[23]),
-        [t24] "=&v"(t[24]), [t25] "=&v"(t[25]), [t26] "=&v"(t[26]), [t27] "=&v"(t[27]),
-        [t28] "=&v"(t[28]), [t29] "=&v"(t[29]), [t30] "=&v"(t[30]), [t31] "=&v"(t[31])
-      : [ad] "v"(ad), [p] "v"(p)
-      : "memory");
-#undef HCA_RD
-#undef HCA_MF
+        [o28] "+a"(o[28]), [o29] "+a"(o[29]), [o30] "+a"(o[30]), [o31] "+a"(o[31])
+      : [ad] "v"(ad), [ad2] "v"(ad2), [p] "v"(p)
+      : "memory", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
 }
 
 // ---------------------------------------------------------------- key lists
-// The keys of a block of 16 flat rows whose queries run from t_lo to t_hi:
+// The keys of the rows whose queries run from t_lo to t_hi, in tiles of 32:
 // entry tiles (entries 0 .. nc-1, nc = (t_hi + 1) / 128), then raw tiles
 // (positions lo .. t_hi, lo = max(0, t_lo - 127)).
 struct Keys {
@@ -198,37 +270,202 @@ __device__ __forceinline__ TileSrc tile_src(const Keys& s, int j, const uint16_t
   }
   return t;
 }
-// 16 fragments of key row l16 (dims 32 ss + 8 g4 .. +7) into registers.
-__device__ __forceinline__ void load_frags(__amdgpu_buffer_rsrc_t r, int l16, int g4,
-                                           bf16x8 (&f)[16]) {
+// Rows 8w .. 8w+7 of a 32-row tile (buffer r of 1 KiB rows; rows past its end
+// arrive as zeros) into LDS rows `stride` bytes apart: 8 DMA instructions.
+__device__ __forceinline__ void copy8(__amdgpu_buffer_rsrc_t r, int w, int lane16, uint8_t* st,
+                                      int stride) {
 #pragma unroll
-  for (int ss = 0; ss < 16; ++ss)
-    f[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, l16 * 1024 + 64 * ss + 16 * g4, 0, 0));
+  for (int u = 0; u < 8; ++u) {
+    const int rr = 8 * w + u;
+    dma16_buf(r, rr * 1024 + lane16, (lds_void*)(st + rr * stride));
+  }
 }
-// The 16 rows of a buffer into an LDS tile (rows kRow apart).
-__device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t r, int lane16, uint8_t* st) {
-#pragma unroll
-  for (int rr = 0; rr < kTile; ++rr)
-    dma16_buf(r, rr * 1024 + lane16, (lds_void*)(st + rr * kRow));
+
+// One score-shaped chain over 16 rows of an LDS tile:
+//   s = sum_ss X[ss] B[ss]   (16 MFMA 16x16x32)
+// with the A operand X read from LDS (lane (l16, g4): 16 bytes at xad + 64 ss)
+// and B in registers.  One asm block issues the 16 reads, starts the MFMAs once
+// the first 8 have landed, and waits for everything it reads (the compiler
+// does not see these LDS reads, so it inserts no wait for DMA copies in flight
+// into other stages).  It ends with the wait states a VALU read of s needs.
+__device__ __forceinline__ void chain_a(f32x4& s, uint32_t xad, const bf16x8 (&b)[16]) {
+  bf16x8 x[16];
+  asm volatile(
+      "ds_read_b128 %[x0], %[xa] offset:0\n\t"
+      "ds_read_b128 %[x1], %[xa] offset:64\n\t"
+      "ds_read_b128 %[x2], %[xa] offset:128\n\t"
+      "ds_read_b128 %[x3], %[xa] offset:192\n\t"
+      "ds_read_b128 %[x4], %[xa] offset:256\n\t"
+      "ds_read_b128 %[x5], %[xa] offset:320\n\t"
+      "ds_read_b128 %[x6], %[xa] offset:384\n\t"
+      "ds_read_b128 %[x7], %[xa] offset:448\n\t"
+      "ds_read_b128 %[x8], %[xa] offset:512\n\t"
+      "ds_read_b128 %[x9], %[xa] offset:576\n\t"
+      "ds_read_b128 %[x10], %[xa] offset:640\n\t"
+      "ds_read_b128 %[x11], %[xa] offset:704\n\t"
+      "ds_read_b128 %[x12], %[xa] offset:768\n\t"
+      "ds_read_b128 %[x13], %[xa] offset:832\n\t"
+      "ds_read_b128 %[x14], %[xa] offset:896\n\t"
+      "ds_read_b128 %[x15], %[xa] offset:960\n\t"
+      "s_waitcnt lgkmcnt(8)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x0], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x1], %[b1], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x2], %[b2], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x3], %[b3], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x4], %[b4], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x5], %[b5], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x6], %[b6], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x7], %[b7], %[s]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x8], %[b8], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x9], %[b9], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x10], %[b10], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x11], %[b11], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x12], %[b12], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x13], %[b13], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x14], %[b14], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x15], %[b15], %[s]\n\t"
+      "s_nop 15\n\ts_nop 3"
+      : [s] "=&v"(s), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]),
+        [x3] "=&v"(x[3]), [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]),
+        [x7] "=&v"(x[7]), [x8] "=&v"(x[8]), [x9] "=&v"(x[9]), [x10] "=&v"(x[10]),
+        [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]), [x14] "=&v"(x[14]),
+        [x15] "=&v"(x[15])
+      : [xa] "v"(xad), [b0] "a"(b[0]), [b1] "a"(b[1]), [b2] "a"(b[2]),
+        [b3] "a"(b[3]), [b4] "a"(b[4]), [b5] "a"(b[5]), [b6] "a"(b[6]),
+        [b7] "a"(b[7]), [b8] "a"(b[8]), [b9] "a"(b[9]), [b10] "a"(b[10]),
+        [b11] "a"(b[11]), [b12] "a"(b[12]), [b13] "a"(b[13]), [b14] "a"(b[14]),
+        [b15] "a"(b[15])
+      : "memory");
+}
+// The same with B in VGPRs, after four 16-byte reads (row statistics).
+__device__ __forceinline__ void chain_vs(f32x4& s, uint32_t xad, const bf16x8 (&b)[16], uint32_t sad, f32x4 (&st)[4]) {
+  bf16x8 x[16];
+  asm volatile(
+      "ds_read_b128 %[st0], %[sa] offset:0\n\t"
+      "ds_read_b128 %[st1], %[sa] offset:64\n\t"
+      "ds_read_b128 %[st2], %[sa] offset:128\n\t"
+      "ds_read_b128 %[st3], %[sa] offset:192\n\t"
+      "ds_read_b128 %[x0], %[xa] offset:0\n\t"
+      "ds_read_b128 %[x1], %[xa] offset:64\n\t"
+      "ds_read_b128 %[x2], %[xa] offset:128\n\t"
+      "ds_read_b128 %[x3], %[xa] offset:192\n\t"
+      "ds_read_b128 %[x4], %[xa] offset:256\n\t"
+      "ds_read_b128 %[x5], %[xa] offset:320\n\t"
+      "ds_read_b128 %[x6], %[xa] offset:384\n\t"
+      "ds_read_b128 %[x7], %[xa] offset:448\n\t"
+      "ds_read_b128 %[x8], %[xa] offset:512\n\t"
+      "ds_read_b128 %[x9], %[xa] offset:576\n\t"
+      "ds_read_b128 %[x10], %[xa] offset:640\n\t"
+      "ds_read_b128 %[x11], %[xa] offset:704\n\t"
+      "ds_read_b128 %[x12], %[xa] offset:768\n\t"
+      "ds_read_b128 %[x13], %[xa] offset:832\n\t"
+      "ds_read_b128 %[x14], %[xa] offset:896\n\t"
+      "ds_read_b128 %[x15], %[xa] offset:960\n\t"
+      "s_waitcnt lgkmcnt(8)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x0], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x1], %[b1], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x2], %[b2], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x3], %[b3], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x4], %[b4], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x5], %[b5], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x6], %[b6], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x7], %[b7], %[s]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x8], %[b8], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x9], %[b9], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x10], %[b10], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x11], %[b11], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x12], %[b12], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x13], %[b13], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x14], %[b14], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x15], %[b15], %[s]\n\t"
+      "s_nop 15\n\ts_nop 3"
+      : [s] "=&v"(s), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]),
+        [x3] "=&v"(x[3]), [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]),
+        [x7] "=&v"(x[7]), [x8] "=&v"(x[8]), [x9] "=&v"(x[9]), [x10] "=&v"(x[10]),
+        [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]), [x14] "=&v"(x[14]),
+        [x15] "=&v"(x[15]), [st0] "=&v"(st[0]), [st1] "=&v"(st[1]), [st2] "=&v"(st[2]),
+        [st3] "=&v"(st[3])
+      : [xa] "v"(xad), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]),
+        [b3] "v"(b[3]), [b4] "v"(b[4]), [b5] "v"(b[5]), [b6] "v"(b[6]),
+        [b7] "v"(b[7]), [b8] "v"(b[8]), [b9] "v"(b[9]), [b10] "v"(b[10]),
+        [b11] "v"(b[11]), [b12] "v"(b[12]), [b13] "v"(b[13]), [b14] "v"(b[14]),
+        [b15] "v"(b[15]), [sa] "v"(sad)
+      : "memory");
+}
+__device__ __forceinline__ void chain_v(f32x4& s, uint32_t xad, const bf16x8 (&b)[16]) {
+  bf16x8 x[16];
+  asm volatile(
+      "ds_read_b128 %[x0], %[xa] offset:0\n\t"
+      "ds_read_b128 %[x1], %[xa] offset:64\n\t"
+      "ds_read_b128 %[x2], %[xa] offset:128\n\t"
+      "ds_read_b128 %[x3], %[xa] offset:192\n\t"
+      "ds_read_b128 %[x4], %[xa] offset:256\n\t"
+      "ds_read_b128 %[x5], %[xa] offset:320\n\t"
+      "ds_read_b128 %[x6], %[xa] offset:384\n\t"
+      "ds_read_b128 %[x7], %[xa] offset:448\n\t"
+      "ds_read_b128 %[x8], %[xa] offset:512\n\t"
+      "ds_read_b128 %[x9], %[xa] offset:576\n\t"
+      "ds_read_b128 %[x10], %[xa] offset:640\n\t"
+      "ds_read_b128 %[x11], %[xa] offset:704\n\t"
+      "ds_read_b128 %[x12], %[xa] offset:768\n\t"
+      "ds_read_b128 %[x13], %[xa] offset:832\n\t"
+      "ds_read_b128 %[x14], %[xa] offset:896\n\t"
+      "ds_read_b128 %[x15], %[xa] offset:960\n\t"
+      "s_waitcnt lgkmcnt(8)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x0], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x1], %[b1], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x2], %[b2], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x3], %[b3], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x4], %[b4], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x5], %[b5], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x6], %[b6], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x7], %[b7], %[s]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x8], %[b8], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x9], %[b9], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x10], %[b10], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x11], %[b11], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x12], %[b12], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x13], %[b13], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x14], %[b14], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s], %[x15], %[b15], %[s]\n\t"
+      "s_nop 15\n\ts_nop 3"
+      : [s] "=&v"(s), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]),
+        [x3] "=&v"(x[3]), [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]),
+        [x7] "=&v"(x[7]), [x8] "=&v"(x[8]), [x9] "=&v"(x[9]), [x10] "=&v"(x[10]),
+        [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]), [x14] "=&v"(x[14]),
+        [x15] "=&v"(x[15])
+      : [xa] "v"(xad), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]),
+        [b3] "v"(b[3]), [b4] "v"(b[4]), [b5] "v"(b[5]), [b6] "v"(b[6]),
+        [b7] "v"(b[7]), [b8] "v"(b[8]), [b9] "v"(b[9]), [b10] "v"(b[10]),
+        [b11] "v"(b[11]), [b12] "v"(b[12]), [b13] "v"(b[13]), [b14] "v"(b[14]),
+        [b15] "v"(b[15])
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)p;
 }
 
 // ----------------------------------------------------------------- rows pass
 __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
-  __shared__ __attribute__((aligned(256))) uint8_t lds[8 * kStage];
+  // stage s (0, 1): the K rows of a 32-key tile at lds + 2 s kStage, its V rows after them
+  __shared__ __attribute__((aligned(256))) uint8_t lds[4 * kStage];
   const int W = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rb = 4 * blockIdx.x + W;
-  if (rb >= a.n_rb) return;
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4, lane16 = lane * 16;
-  uint8_t* const st[2] = {lds + (2 * W) * kStage, lds + (2 * W + 1) * kStage};
   const int64_t nrows = a.T * a.H;
-  const int64_t r0 = (int64_t)rb * 16;
-  const int nr = nrows - r0 < 16 ? (int)(nrows - r0) : 16;   // rows of the block
+  const int64_t g0 = (int64_t)blockIdx.x * kRowsPerWg;  // the workgroup's rows g0 .. glast
+  const int64_t glast = g0 + kRowsPerWg - 1 < nrows ? g0 + kRowsPerWg - 1 : nrows - 1;
+  const int64_t r0 = g0 + 16 * W;                       // this wave's rows (none past nrows)
+  const int nr = r0 >= nrows ? 0 : (nrows - r0 < 16 ? (int)(nrows - r0) : 16);
   const int64_t rmy = r0 + l16 < nrows ? r0 + l16 : nrows - 1;  // this lane's row (clamped)
   const bool valid = l16 < nr;
   const int t_my = (int)(rmy / a.H);
-  const int t_lo = __builtin_amdgcn_readfirstlane((int)(r0 / a.H));
-  const int t_hi = __builtin_amdgcn_readfirstlane((int)((r0 + nr - 1) / a.H));
-  const Keys s = keys_of(t_lo, t_hi, a.Nc);
+  const Keys s = keys_of(__builtin_amdgcn_readfirstlane((int)(g0 / a.H)),
+                         __builtin_amdgcn_readfirstlane((int)(glast / a.H)), a.Nc);
+  const int nt = s.n_tiles;
   const int nc_my = (t_my + 1) / kBlock < s.nc ? (t_my + 1) / kBlock : s.nc;
   const int lo_my = t_my - (kWindow - 1) > 0 ? t_my - (kWindow - 1) : 0;
   const int64_t ro = rmy * kD;
@@ -249,16 +486,16 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
                     bf16_bits_to_f32(o2.y >> 16) * sigmoid(bf16_bits_to_f32(g2.y >> 16)))};
     __builtin_amdgcn_raw_buffer_store_b64(w2, rda, l16 * 1024 + 2 * d0, 0, 0);
   }
-  wait_vm0();  // the stores have reached L2 (loads below bypass L1)
+  wait_vm<0>();  // the stores have reached L2 (the loads below bypass L1)
   bf16x8 daf[16], qf[16];
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + r0 * kD, nr * 1024);
 #pragma unroll
-  for (int ss = 0; ss < 16; ++ss)
+  for (int ss = 0; ss < 16; ++ss) {
     daf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rda, l16 * 1024 + 64 * ss + 16 * g4, 0, 1));
-  // Q^T fragments (B operand of the scores)
-  load_frags(make_rsrc(a.q + r0 * kD, nr * 1024), l16, g4, qf);
-  const int voff = (4 * g4 + (l16 >> 2)) * kRow + 8 * (l16 & 3);
+    qf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, l16 * 1024 + 64 * ss + 16 * g4, 0, 0));
+  }
 
-  // visible range of key kk = 4 g4 + r of tile j: lo_v <= kk < hi_v
+  // visible range of key kk (0 .. 31) of tile j for this lane's row: lo_v <= kk < hi_v
   auto vis = [&](int j, int& lo_v, int& hi_v) {
     if (j < s.n_et) {
       lo_v = 0;
@@ -269,6 +506,21 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
       hi_v = t_my + 1 - p0;
     }
   };
+  // Tile j's stage; this wave's quarter of its K and V rows into it.
+  auto kst = [&](int j) { return lds + (j & 1) * (2 * kStage); };
+  auto issue_k = [&](int j, int stride) { copy8(tile_src(s, j, a.ck, a.k).r, W, lane16, kst(j), stride); };
+  auto issue_v = [&](int j, int stride) {
+    copy8(tile_src(s, j, a.cv, a.v).r, W, lane16, kst(j) + kStage, stride);
+  };
+  // Top of tile j: this wave's copies of it (issued during tile j-1) have
+  // landed, then every wave's; every wave is also done with tile j-1, whose
+  // stage tile j+1 takes.
+  auto arrive = [&]() {
+    wait_vm<0>();
+    barrier_no_fence();
+  };
+  const int voff = (4 * g4 + (l16 >> 2)) * kRowT + 8 * (l16 & 3);  // transposing reads
+  const int foffF = l16 * kRowF + 16 * g4, foffT = l16 * kRowT + 16 * g4;
 
   // ---- pass A: per row the maximum (fixed reference m), the weights
   // e_j = 2^(x_j - m) and, with them,
@@ -276,65 +528,60 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   //   the forward's ungated output a = (sum bf16(e_j) v_j) / (sum bf16(e_j)),
   // whence lse = m + log2 l and Dt = ldp / l = sum p_j dp_j: the same p and dp
   // the score gradients use, so that sum_j p_j (dp_j - Dt) = 0 holds to fp32
-  // rounding (an exact-zero gradient stays zero).
+  // rounding (an exact-zero gradient stays zero).  K is read as fragments
+  // only (rows kRowF apart), V also transposed (kRowT).  Keys 16h + 4 g4 + r
+  // of a tile are in sc[h][r] (h = 0, 1).
   f32x4 o[32];
   float m = -INFINITY, mseen = -INFINITY, l = 0.0f, lb = 0.0f, ldp = 0.0f;
-  bool fixed_m = false, over = false;
+  bool fixed_m = false;
   for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int db = 0; db < 32; ++db) o[db] = f32x4{};
     l = lb = ldp = 0.0f;
-    over = false;
-    copy_rows(tile_src(s, 0, a.cv, a.v).r, lane16, st[0]);
-    for (int j = 0; j < s.n_tiles; ++j) {
-      bf16x8 kf[16], vf[16];
-      sched_fence();
-      load_frags(tile_src(s, j, a.ck, a.k).r, l16, g4, kf);
-      load_frags(tile_src(s, j, a.cv, a.v).r, l16, g4, vf);
-      if (j + 1 < s.n_tiles) copy_rows(tile_src(s, j + 1, a.cv, a.v).r, lane16, st[(j + 1) & 1]);
-      sched_fence();
-      f32x4 sc, dp;
-      mfma_va_first(sc, kf[0], qf[0]);
-#pragma unroll
-      for (int ss = 1; ss < 15; ++ss) mfma_va(sc, kf[ss], qf[ss]);
-      mfma_va_last(sc, kf[15], qf[15]);
-      mfma_va_first(dp, vf[0], daf[0]);
-#pragma unroll
-      for (int ss = 1; ss < 15; ++ss) mfma_va(dp, vf[ss], daf[ss]);
-      mfma_va_last(dp, vf[15], daf[15]);
+    bool over = false;
+    barrier_no_fence();  // every wave is done with the stages
+    issue_k(0, kRowF);
+    issue_v(0, kRowT);
+    for (int j = 0; j < nt; ++j) {
+      arrive();
+      uint8_t* const sk = kst(j);
+      f32x4 sc[2], dp[2];  // S^T = K Q^T, dP^T = V dA^T
+      chain_a(sc[0], lds_addr(sk + foffF), qf);
+      chain_a(sc[1], lds_addr(sk + 16 * kRowF + foffF), qf);
+      if (j + 1 < nt) issue_k(j + 1, kRowF);
+      chain_a(dp[0], lds_addr(sk + kStage + foffT), daf);
+      chain_a(dp[1], lds_addr(sk + kStage + 16 * kRowT + foffT), daf);
+      if (j + 1 < nt) issue_v(j + 1, kRowT);
       int lo_v, hi_v;
       vis(j, lo_v, hi_v);
-      float x[4], mt = -INFINITY;
+      float x[8], mt = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = 4 * g4 + r;
-        x[r] = kk >= lo_v && kk < hi_v ? sc[r] * a.c : -INFINITY;
-        mt = fmaxf(mt, x[r]);
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = 16 * h + 4 * g4 + r;
+          x[4 * h + r] = kk >= lo_v && kk < hi_v ? sc[h][r] * a.c : -INFINITY;
+          mt = fmaxf(mt, x[4 * h + r]);
+        }
       mt = xmax32(xmax16(mt));
       if (!fixed_m && m == -INFINITY) m = mt;
       mseen = fmaxf(mseen, mt);
       over |= mt > m + kHeadroom;
       const float mx = m == -INFINITY ? 0.0f : m;
-      f32x4 e;
+      bf16x8 pb;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(x[r] - mx);
-        l += e[r];
-        ldp += e[r] * dp[r];
+      for (int i = 0; i < 8; ++i) {
+        const float e = __builtin_amdgcn_exp2f(x[i] - mx);
+        l += e;
+        ldp += e * dp[i >> 2][i & 3];
+        pb[i] = (__bf16)e;
+        lb += (float)pb[i];
       }
-      const bf16x4 pb = __builtin_convertvector(e, bf16x4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lb += (float)pb[r];
-      // V(j) rows have landed once at most the 16 copies of V(j+1) (or the V(j)
-      // fragment loads, on the last tile) are in flight.
-      sched_fence();
-      wait_vm16();
-      sched_fence();
-      tr_tile(o, (uint32_t)(uintptr_t)(st[j & 1] + voff), __builtin_bit_cast(i16x4, pb));
+      tr_tile32(o, lds_addr(sk + kStage + voff), lds_addr(sk + kStage + 16 * kRowT + voff), pb);
     }
-    wait_vm0();
-    if (pass == 1 || __builtin_amdgcn_ballot_w64(over) == 0) break;
+    // the workgroup walks the tiles again (all waves, barriers in step) if a
+    // score of any row rose more than 2^64 above its reference
+    if (pass == 1 || !__syncthreads_or(over)) break;
     m = mseen;
     fixed_m = true;
   }
@@ -349,8 +596,8 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     a.lse[rmy] = lse;
     a.dt[rmy] = dt;
   }
-#pragma unroll 4
-  for (int db = 0; db < 32; ++db) {
+#pragma unroll
+  for (int db = 0; db < 32; ++db) {  // fully unrolled: o[db] stays in registers
     const int d0 = 16 * db + 4 * g4;
     const uint2 g2 = *reinterpret_cast<const uint2*>(a.g + ro + d0);
     const uint2 o2 = *reinterpret_cast<const uint2*>(a.dout + ro + d0);
@@ -367,42 +614,33 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     if (valid) *reinterpret_cast<float4*>(a.dg + ro + d0) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
   }
 
-  // ---- pass B: dq
+  // ---- pass B: dq.  K is also read transposed (kRowT), V as fragments only.
 #pragma unroll
   for (int db = 0; db < 32; ++db) o[db] = f32x4{};
-  copy_rows(tile_src(s, 0, a.ck, a.k).r, lane16, st[0]);
-  for (int j = 0; j < s.n_tiles; ++j) {
-    bf16x8 kf[16], vf[16];
-    sched_fence();
-    load_frags(tile_src(s, j, a.ck, a.k).r, l16, g4, kf);
-    load_frags(tile_src(s, j, a.cv, a.v).r, l16, g4, vf);
-    if (j + 1 < s.n_tiles) copy_rows(tile_src(s, j + 1, a.ck, a.k).r, lane16, st[(j + 1) & 1]);
-    sched_fence();
-    f32x4 sc, dp;
-    mfma_va_first(sc, kf[0], qf[0]);
-#pragma unroll
-    for (int ss = 1; ss < 15; ++ss) mfma_va(sc, kf[ss], qf[ss]);
-    mfma_va_last(sc, kf[15], qf[15]);
-    mfma_va_first(dp, vf[0], daf[0]);
-#pragma unroll
-    for (int ss = 1; ss < 15; ++ss) mfma_va(dp, vf[ss], daf[ss]);
-    mfma_va_last(dp, vf[15], daf[15]);
+  barrier_no_fence();  // every wave is done with the stages
+  issue_k(0, kRowT);
+  issue_v(0, kRowF);
+  for (int j = 0; j < nt; ++j) {
+    arrive();
+    uint8_t* const sk = kst(j);
+    f32x4 sc[2], dp[2];
+    chain_a(sc[0], lds_addr(sk + foffT), qf);
+    chain_a(sc[1], lds_addr(sk + 16 * kRowT + foffT), qf);
+    if (j + 1 < nt) issue_k(j + 1, kRowT);
+    chain_a(dp[0], lds_addr(sk + kStage + foffF), daf);
+    chain_a(dp[1], lds_addr(sk + kStage + 16 * kRowF + foffF), daf);
+    if (j + 1 < nt) issue_v(j + 1, kRowF);
     int lo_v, hi_v;
     vis(j, lo_v, hi_v);
-    f32x4 ds;
+    bf16x8 dsb;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = 4 * g4 + r;
-      const float p = kk >= lo_v && kk < hi_v ? __builtin_amdgcn_exp2f(sc[r] * a.c - lse) : 0.0f;
-      ds[r] = p * (dp[r] - dt);
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 16 * (i >> 2) + 4 * g4 + (i & 3);
+      const float p = kk >= lo_v && kk < hi_v ? __builtin_amdgcn_exp2f(sc[i >> 2][i & 3] * a.c - lse) : 0.0f;
+      dsb[i] = (__bf16)(p * (dp[i >> 2][i & 3] - dt));
     }
-    const bf16x4 db4 = __builtin_convertvector(ds, bf16x4);
-    sched_fence();
-    wait_vm16();  // K(j) rows in LDS: only K(j+1) (or this tile's V) may be in flight
-    sched_fence();
-    tr_tile(o, (uint32_t)(uintptr_t)(st[j & 1] + voff), __builtin_bit_cast(i16x4, db4));
+    tr_tile32(o, lds_addr(sk + voff), lds_addr(sk + 16 * kRowT + voff), dsb);
   }
-  wait_vm0();
   mfma_drain();
   if (valid) {
 #pragma unroll
@@ -416,45 +654,53 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
 
 // ----------------------------------------------------------------- keys pass
 __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
-  __shared__ __attribute__((aligned(256))) uint8_t lds[8 * kStage];
+  // stage s (0, 1): Q rows of a 32-row block, its dA rows, then lse[32], Dt[32]
+  constexpr int kKStage = 2 * kStage + 256;
+  __shared__ __attribute__((aligned(256))) uint8_t lds[2 * kKStage];
   const int W = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int task = 4 * blockIdx.x + W;
-  if (task >= a.n_raw_tiles + a.n_ent_tasks) return;
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4, lane16 = lane * 16;
-  uint8_t* const sq = lds + (2 * W) * kStage;   // Q rows of the current row block
-  uint8_t* const sa = lds + (2 * W + 1) * kStage;  // dA rows
   const int64_t nrows = a.T * a.H;
 
-  // This task's 16 keys and the queries that can see them.
-  const bool ent = task >= a.n_raw_tiles;
-  int first, nkeys, t_from, t_to;
-  if (!ent) {
-    first = kTile * task;
-    nkeys = a.T - first < kTile ? (int)(a.T - first) : kTile;
-    t_from = first;
-    t_to = first + nkeys - 1 + (kWindow - 1);
+  // Task -> 64 keys and the row blocks rb0 .. rb1 of queries that can see
+  // them (the entry tasks first: they are the long ones).
+  const int task = blockIdx.x;
+  const bool ent = task < a.n_ent_tasks;
+  int first, nkeys;
+  int64_t rb0, rb1;
+  if (ent) {
+    const int grp = task / a.n_chunks, ch = task % a.n_chunks;
+    first = kKeysPerWg * grp;
+    nkeys = a.Nc - first < kKeysPerWg ? a.Nc - first : kKeysPerWg;
+    const int64_t t0 = (int64_t)kBlock * first + kBlock - 1;  // first query seeing entry `first`
+    const int64_t c0 = (int64_t)ch * kChunkRb, c1 = c0 + kChunkRb - 1;
+    rb0 = t0 * a.H / kTile;
+    rb0 = rb0 > c0 ? rb0 : c0;
+    rb1 = c1 < a.n_rb - 1 ? c1 : a.n_rb - 1;
   } else {
-    const int et = (task - a.n_raw_tiles) / a.ent_chunks, ch = (task - a.n_raw_tiles) % a.ent_chunks;
-    first = kTile * et;
-    nkeys = a.Nc - first < kTile ? a.Nc - first : kTile;
-    t_from = kBlock * first + kBlock - 1;
-    const int c0 = ch * kChunk;
-    t_to = c0 + kChunk - 1;
-    t_from = t_from > c0 ? t_from : c0;
+    first = kKeysPerWg * (task - a.n_ent_tasks);
+    nkeys = a.T - first < kKeysPerWg ? (int)(a.T - first) : kKeysPerWg;
+    int64_t t1 = (int64_t)first + kKeysPerWg - 1 + (kWindow - 1);
+    t1 = t1 < a.T - 1 ? t1 : a.T - 1;
+    rb0 = (int64_t)first * a.H / kTile;
+    rb1 = (t1 * a.H + a.H - 1) / kTile;
   }
-  t_to = t_to < a.T - 1 ? t_to : (int)(a.T - 1);
-  if (t_from > t_to) return;  // an entry chunk before the entries' first query
-  first = __builtin_amdgcn_readfirstlane(first);
-  // K and V rows of the keys (B operands: lane (key l16, g4), dims 32 ss + 8 g4)
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((ent ? a.ck : a.k) + (int64_t)first * kD, nkeys * 1024);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((ent ? a.cv : a.v) + (int64_t)first * kD, nkeys * 1024);
+  if (rb0 > rb1) return;  // the whole workgroup: an entry chunk before the entries' first query
+
+  // This wave's 16 keys (none past the last): K and V rows as the B operands
+  // of S = Q K^T and dP = dA V^T, lane (key l16, g4) dims 32 ss + 8 g4 .. +7.
+  const int wfirst = first + 16 * W;
+  const int wkeys = nkeys - 16 * W < 0 ? 0 : (nkeys - 16 * W < 16 ? nkeys - 16 * W : 16);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((ent ? a.ck : a.k) + (int64_t)wfirst * kD, wkeys * 1024);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((ent ? a.cv : a.v) + (int64_t)wfirst * kD, wkeys * 1024);
   bf16x8 kf[16], vf[16];
-  load_frags(rk, l16, g4, kf);
-  load_frags(rv, l16, g4, vf);
-  // this lane's key (column l16 of S): first visible query
-  const int key = first + l16;
-  const int key_t0 = ent ? kBlock * key + kBlock - 1 : key;
-  const bool key_ok = l16 < nkeys;
+#pragma unroll
+  for (int ss = 0; ss < 16; ++ss) {
+    kf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, l16 * 1024 + 64 * ss + 16 * g4, 0, 0));
+    vf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, l16 * 1024 + 64 * ss + 16 * g4, 0, 0));
+  }
+  const int key = wfirst + l16;  // this lane's key (column l16 of S)
+  const int key_t0 = ent ? kBlock * key + kBlock - 1 : key;  // its first query
+  const bool key_ok = l16 < wkeys;
 
   f32x4 dk[32], dv[32];
 #pragma unroll
@@ -462,69 +708,58 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
     dk[db] = f32x4{};
     dv[db] = f32x4{};
   }
-  const int voff = (4 * g4 + (l16 >> 2)) * kRow + 8 * (l16 & 3);
-  {
-    const int64_t rb0 = (int64_t)t_from * a.H / 16, rb1 = ((int64_t)t_to * a.H + a.H - 1) / 16;
-    for (int64_t rb = rb0; rb <= rb1; ++rb) {
-      const int64_t r0 = rb * 16;
-      const int nr = nrows - r0 < 16 ? (int)(nrows - r0) : 16;
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + r0 * kD, nr * 1024);
-      const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.da + r0 * kD, nr * 1024);
-      sched_fence();
-      copy_rows(rq, lane16, sq);
-      copy_rows(rd, lane16, sa);
-      // rows 4 g4 + r of the block: statistics (S layout: lane holds rows 4 g4 .. +3)
-      float lse4[4], dt4[4];
-      int t4[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = r0 + 4 * g4 + r;
-        const int64_t rr = row < nrows ? row : nrows - 1;
-        lse4[r] = a.lse[rr];
-        dt4[r] = a.dt[rr];
-        t4[r] = row < nrows ? (int)(row / a.H) : -1;
-      }
-      wait_vm0();
-      sched_fence();
-      // S = Q K^T and dP = dA V^T, A operands (rows l16, dims 32 ss + 8 g4) from LDS
-      f32x4 sc, dp;
-      {
-        bf16x8 qa[16];
-#pragma unroll
-        for (int ss = 0; ss < 16; ++ss)
-          qa[ss] = *reinterpret_cast<const bf16x8*>(sq + l16 * kRow + 64 * ss + 16 * g4);
-        mfma_vv_first(sc, qa[0], kf[0]);
-#pragma unroll
-        for (int ss = 1; ss < 15; ++ss) mfma_vv(sc, qa[ss], kf[ss]);
-        mfma_vv_last(sc, qa[15], kf[15]);
-      }
-      {
-        bf16x8 da[16];
-#pragma unroll
-        for (int ss = 0; ss < 16; ++ss)
-          da[ss] = *reinterpret_cast<const bf16x8*>(sa + l16 * kRow + 64 * ss + 16 * g4);
-        mfma_vv_first(dp, da[0], vf[0]);
-#pragma unroll
-        for (int ss = 1; ss < 15; ++ss) mfma_vv(dp, da[ss], vf[ss]);
-        mfma_vv_last(dp, da[15], vf[15]);
-      }
-      // lane (key l16, g4) holds S[rows 4 g4 + r][key l16]
-      f32x4 pp, ds;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t4[r];
-        const bool v = key_ok && t >= 0 && t >= key_t0 && (ent || t - (kWindow - 1) <= key);
-        const float p = v ? __builtin_amdgcn_exp2f(sc[r] * a.c - lse4[r]) : 0.0f;
-        pp[r] = p;
-        ds[r] = p * (dp[r] - dt4[r]);
-      }
-      const bf16x4 pb = __builtin_convertvector(pp, bf16x4);
-      const bf16x4 dsb = __builtin_convertvector(ds, bf16x4);
-      // dV^T += dA^T P, dK^T += Q^T dS (transposed LDS reads of the row tiles)
-      tr_tile(dv, (uint32_t)(uintptr_t)(sa + voff), __builtin_bit_cast(i16x4, pb));
-      tr_tile(dk, (uint32_t)(uintptr_t)(sq + voff), __builtin_bit_cast(i16x4, dsb));
-      sched_fence();
+  // Row block i's stage; this wave's quarter of its Q and dA rows, and of its
+  // statistics (lanes 0, 1: 8 rows' lse, then their Dt): 18 DMA instructions.
+  const int nb = (int)(rb1 - rb0 + 1);
+  auto st = [&](int i) { return lds + (i & 1) * kKStage; };
+  auto issue_q = [&](int i) {
+    const int64_t r0 = (rb0 + i) * kTile;
+    const int nr = nrows - r0 < kTile ? (int)(nrows - r0) : kTile;
+    uint8_t* sp = st(i);
+    copy8(make_rsrc(a.q + r0 * kD, nr * 1024), W, lane16, sp, kRowT);
+    if (lane < 2) {
+      dma16_buf(make_rsrc(a.lse + r0, nr * 4), 32 * W + lane16, (lds_void*)(sp + 2 * kStage + 32 * W));
+      dma16_buf(make_rsrc(a.dt + r0, nr * 4), 32 * W + lane16,
+                (lds_void*)(sp + 2 * kStage + 128 + 32 * W));
     }
+  };
+  auto issue_a = [&](int i) {
+    const int64_t r0 = (rb0 + i) * kTile;
+    const int nr = nrows - r0 < kTile ? (int)(nrows - r0) : kTile;
+    copy8(make_rsrc(a.da + r0 * kD, nr * 1024), W, lane16, st(i) + kStage, kRowT);
+  };
+  const int voff = (4 * g4 + (l16 >> 2)) * kRowT + 8 * (l16 & 3);
+  const int foff = l16 * kRowT + 16 * g4;
+  issue_q(0);
+  issue_a(0);
+  for (int i = 0; i < nb; ++i) {
+    wait_vm<0>();        // this wave's copies of block i (issued during block i-1)
+    barrier_no_fence();  // every wave's; every wave is done with block i-1
+    uint8_t* const sp = st(i);
+    const int64_t r0 = (rb0 + i) * kTile;
+    // S = Q K^T and dP = dA V^T: lane (key l16, g4) gets rows 16h + 4 g4 + r in
+    // sc[h][r]; the statistics of rows 4 g4 .. and 16 + 4 g4 .. (lse, then Dt)
+    f32x4 sc[2], dp[2], stt[4];
+    chain_vs(sc[0], lds_addr(sp + foff), kf, lds_addr(sp + 2 * kStage + 16 * g4), stt);
+    chain_v(sc[1], lds_addr(sp + 16 * kRowT + foff), kf);
+    if (i + 1 < nb) issue_q(i + 1);
+    chain_v(dp[0], lds_addr(sp + kStage + foff), vf);
+    chain_v(dp[1], lds_addr(sp + kStage + 16 * kRowT + foff), vf);
+    if (i + 1 < nb) issue_a(i + 1);
+    bf16x8 pb, dsb;
+#pragma unroll
+    for (int i8 = 0; i8 < 8; ++i8) {
+      const int h = i8 >> 2, r = i8 & 3;
+      const int64_t row = r0 + 16 * h + 4 * g4 + r;
+      const int t = row < nrows ? (int)(row / a.H) : -1;
+      const bool v = key_ok && t >= key_t0 && (ent || t - (kWindow - 1) <= key);
+      const float p = v ? __builtin_amdgcn_exp2f(sc[h][r] * a.c - stt[h][r]) : 0.0f;
+      pb[i8] = (__bf16)p;
+      dsb[i8] = (__bf16)(p * (dp[h][r] - stt[2 + h][r]));
+    }
+    // dV^T += dA^T P, dK^T += Q^T dS (transposing reads of the row tiles)
+    tr_tile32(dv, lds_addr(sp + kStage + voff), lds_addr(sp + kStage + 16 * kRowT + voff), pb);
+    tr_tile32(dk, lds_addr(sp + voff), lds_addr(sp + 16 * kRowT + voff), dsb);
   }
   mfma_drain();
   // lane (key l16, g4) holds dims 16 db + 4 g4 .. +3 of key l16
@@ -608,10 +843,9 @@ hipError_t launch_backward(const BackwardProblem& p, void* ws, hipStream_t strea
   a.dck = reinterpret_cast<float*>(w);
   w += up((size_t)a.Nc * kD * 4);
   a.dcv = reinterpret_cast<float*>(w);
-  a.n_rb = (int)((rows + 15) / 16);
-  a.n_raw_tiles = (int)((p.T + kTile - 1) / kTile);
-  a.ent_chunks = (int)((p.T + kChunk - 1) / kChunk);
-  a.n_ent_tasks = ((a.Nc + kTile - 1) / kTile) * a.ent_chunks;
+  a.n_rb = (int)((rows + kTile - 1) / kTile);
+  a.n_chunks = (a.n_rb + kChunkRb - 1) / kChunkRb;
+  a.n_ent_tasks = ((a.Nc + kKeysPerWg - 1) / kKeysPerWg) * a.n_chunks;
   a.scale = p.scale;
   a.c = p.scale * 1.4426950408889634f;
   if (a.Nc > 0) {
@@ -619,9 +853,11 @@ hipError_t launch_backward(const BackwardProblem& p, void* ws, hipStream_t strea
     hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, a.dck, (int64_t)a.Nc * kD);
     hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, a.dcv, (int64_t)a.Nc * kD);
   }
-  hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((a.n_rb + 3) / 4)), dim3(256), 0, stream, a);
-  const int tasks = a.n_raw_tiles + a.n_ent_tasks;
-  hipLaunchKernelGGL(keys_kernel, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((rows + kRowsPerWg - 1) / kRowsPerWg)), dim3(256),
+                     0, stream, a);
+  const int64_t raw_tasks = (p.T + kKeysPerWg - 1) / kKeysPerWg;
+  hipLaunchKernelGGL(keys_kernel, dim3((unsigned)(a.n_ent_tasks + raw_tasks)), dim3(256), 0, stream,
+                     a);
   if (a.Nc > 0) {
     const int64_t n = (int64_t)a.Nc * kBlock * (kD / 4);
     hipLaunchKernelGGL(pool_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
