@@ -110,12 +110,14 @@ __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 1
 // {4 g4 .. 4 g4 + 3, 16 + 4 g4 .. 16 + 4 g4 + 3}: the A operand M^T comes from
 // two transposing reads, at ad (rows 4 g4 ..) and ad2 = ad + 16 rows, into the
 // two halves of one 4-register group, and P (B operand, 8 bf16 per lane) holds
-// the same rows in that order.  The groups are fixed registers v192 .. v255
-// (clobbered: inline asm cannot name the halves of an operand), a ring of 16:
-// the reads of 8 dim blocks are in flight while the previous 8 blocks' MFMAs
-// issue, and a group is refilled only after the MFMA reading it has issued and
-// the reads in between have been waited for.  Accumulators in AGPRs.
-__device__ __forceinline__ void tr_tile32(f32x4 (&o)[32], uint32_t ad, uint32_t ad2, const bf16x8& p) {
+// the same rows in that order.  The groups are fixed registers (clobbered:
+// inline asm cannot name the halves of an operand) used as a ring: the reads of
+// one half of the ring are in flight while the other half's MFMAs issue, and a
+// group is refilled only after the MFMA reading it has issued and the reads in
+// between have been waited for.  Accumulators in AGPRs.  tr_rows: a ring of 16
+// groups in v192 .. v255; tr_keys: 8 groups in v224 .. v255 (the key kernel
+// keeps its K and V fragments in VGPRs).
+__device__ __forceinline__ void tr_rows(f32x4 (&o)[32], uint32_t ad, uint32_t ad2, const bf16x8& p) {
   asm volatile(
       "ds_read_b64_tr_b16 v[192:193], %[ad] offset:0\n\t"
       "ds_read_b64_tr_b16 v[194:195], %[ad2] offset:0\n\t"
@@ -230,6 +232,129 @@ __device__ __forceinline__ void tr_tile32(f32x4 (&o)[32], uint32_t ad, uint32_t 
       : [ad] "v"(ad), [ad2] "v"(ad2), [p] "v"(p)
       : "memory", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
 }
+__device__ __forceinline__ void tr_keys(f32x4 (&o)[32], uint32_t ad, uint32_t ad2, const bf16x8& p) {
+  asm volatile(
+      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:32\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:32\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:64\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:64\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:96\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:96\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:128\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:128\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:160\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:160\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:192\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:192\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:224\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:224\n\t"
+      "s_waitcnt lgkmcnt(8)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o0], v[224:227], %[p], %[o0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o1], v[228:231], %[p], %[o1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o2], v[232:235], %[p], %[o2]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o3], v[236:239], %[p], %[o3]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:288\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:288\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:320\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:320\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:352\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:352\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o4], v[240:243], %[p], %[o4]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o5], v[244:247], %[p], %[o5]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o6], v[248:251], %[p], %[o6]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o7], v[252:255], %[p], %[o7]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:384\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:384\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:416\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:416\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:448\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:448\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:480\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:480\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o8], v[224:227], %[p], %[o8]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o9], v[228:231], %[p], %[o9]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o10], v[232:235], %[p], %[o10]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o11], v[236:239], %[p], %[o11]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:544\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:544\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:576\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:576\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:608\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:608\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o12], v[240:243], %[p], %[o12]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o13], v[244:247], %[p], %[o13]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o14], v[248:251], %[p], %[o14]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o15], v[252:255], %[p], %[o15]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:640\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:640\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:672\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:672\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:704\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:704\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:736\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:736\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o16], v[224:227], %[p], %[o16]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o17], v[228:231], %[p], %[o17]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o18], v[232:235], %[p], %[o18]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o19], v[236:239], %[p], %[o19]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:800\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:800\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:832\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:832\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:864\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:864\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o20], v[240:243], %[p], %[o20]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o21], v[244:247], %[p], %[o21]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o22], v[248:251], %[p], %[o22]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o23], v[252:255], %[p], %[o23]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:896\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:896\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:928\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:928\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:960\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:960\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:992\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:992\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o24], v[224:227], %[p], %[o24]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o25], v[228:231], %[p], %[o25]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o26], v[232:235], %[p], %[o26]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o27], v[236:239], %[p], %[o27]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o28], v[240:243], %[p], %[o28]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o29], v[244:247], %[p], %[o29]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o30], v[248:251], %[p], %[o30]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o31], v[252:255], %[p], %[o31]"
+      : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]),
+        [o4] "+a"(o[4]), [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]),
+        [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]), [o11] "+a"(o[11]),
+        [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]), [o15] "+a"(o[15]),
+        [o16] "+a"(o[16]), [o17] "+a"(o[17]), [o18] "+a"(o[18]), [o19] "+a"(o[19]),
+        [o20] "+a"(o[20]), [o21] "+a"(o[21]), [o22] "+a"(o[22]), [o23] "+a"(o[23]),
+        [o24] "+a"(o[24]), [o25] "+a"(o[25]), [o26] "+a"(o[26]), [o27] "+a"(o[27]),
+        [o28] "+a"(o[28]), [o29] "+a"(o[29]), [o30] "+a"(o[30]), [o31] "+a"(o[31])
+      : [ad] "v"(ad), [ad2] "v"(ad2), [p] "v"(p)
+      : "memory", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
+}
 
 // ---------------------------------------------------------------- key lists
 // The keys of the rows whose queries run from t_lo to t_hi, in tiles of 32:
@@ -281,168 +406,352 @@ __device__ __forceinline__ void copy8(__amdgpu_buffer_rsrc_t r, int w, int lane1
   }
 }
 
-// One score-shaped chain over 16 rows of an LDS tile:
-//   s = sum_ss X[ss] B[ss]   (16 MFMA 16x16x32)
-// with the A operand X read from LDS (lane (l16, g4): 16 bytes at xad + 64 ss)
-// and B in registers.  One asm block issues the 16 reads, starts the MFMAs once
-// the first 8 have landed, and waits for everything it reads (the compiler
-// does not see these LDS reads, so it inserts no wait for DMA copies in flight
-// into other stages).  It ends with the wait states a VALU read of s needs.
-__device__ __forceinline__ void chain_a(f32x4& s, uint32_t xad, const bf16x8 (&b)[16]) {
-  bf16x8 x[16];
+// Four score-shaped chains over a 32-row tile pair in LDS:
+//   s0, s1 = sum_ss X_c[ss] b[ss] (c = 0, 1),  d0, d1 = sum_ss X_c[ss] c[ss] (c = 2, 3)
+// (16 MFMA 16x16x32 each) with the A operands read from LDS (lane (l16, g4): 16
+// bytes at ad[c] + 64 ss) and b, c in registers.  One asm block issues the 64
+// reads through a ring of fixed registers, the reads of one group in flight
+// while the previous group's MFMAs issue, and waits for everything it reads
+// (the compiler does not see these LDS reads, so it inserts no wait for DMA
+// copies in flight into the other stage).  It ends with the wait states a VALU
+// read of the results needs.  chains_rows: b, c in AGPRs, a ring of 16 in
+// v128 .. v191; chains_keys: b, c in VGPRs, a ring of 8 in v192 .. v223, after
+// four 16-byte reads at sad + 64 i (row statistics).
+__device__ __forceinline__ void chains_rows(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16]) {
   asm volatile(
-      "ds_read_b128 %[x0], %[xa] offset:0\n\t"
-      "ds_read_b128 %[x1], %[xa] offset:64\n\t"
-      "ds_read_b128 %[x2], %[xa] offset:128\n\t"
-      "ds_read_b128 %[x3], %[xa] offset:192\n\t"
-      "ds_read_b128 %[x4], %[xa] offset:256\n\t"
-      "ds_read_b128 %[x5], %[xa] offset:320\n\t"
-      "ds_read_b128 %[x6], %[xa] offset:384\n\t"
-      "ds_read_b128 %[x7], %[xa] offset:448\n\t"
-      "ds_read_b128 %[x8], %[xa] offset:512\n\t"
-      "ds_read_b128 %[x9], %[xa] offset:576\n\t"
-      "ds_read_b128 %[x10], %[xa] offset:640\n\t"
-      "ds_read_b128 %[x11], %[xa] offset:704\n\t"
-      "ds_read_b128 %[x12], %[xa] offset:768\n\t"
-      "ds_read_b128 %[x13], %[xa] offset:832\n\t"
-      "ds_read_b128 %[x14], %[xa] offset:896\n\t"
-      "ds_read_b128 %[x15], %[xa] offset:960\n\t"
+      "ds_read_b128 v[128:131], %[a0] offset:0\n\t"
+      "ds_read_b128 v[132:135], %[a0] offset:64\n\t"
+      "ds_read_b128 v[136:139], %[a0] offset:128\n\t"
+      "ds_read_b128 v[140:143], %[a0] offset:192\n\t"
+      "ds_read_b128 v[144:147], %[a0] offset:256\n\t"
+      "ds_read_b128 v[148:151], %[a0] offset:320\n\t"
+      "ds_read_b128 v[152:155], %[a0] offset:384\n\t"
+      "ds_read_b128 v[156:159], %[a0] offset:448\n\t"
+      "ds_read_b128 v[160:163], %[a0] offset:512\n\t"
+      "ds_read_b128 v[164:167], %[a0] offset:576\n\t"
+      "ds_read_b128 v[168:171], %[a0] offset:640\n\t"
+      "ds_read_b128 v[172:175], %[a0] offset:704\n\t"
+      "ds_read_b128 v[176:179], %[a0] offset:768\n\t"
+      "ds_read_b128 v[180:183], %[a0] offset:832\n\t"
+      "ds_read_b128 v[184:187], %[a0] offset:896\n\t"
+      "ds_read_b128 v[188:191], %[a0] offset:960\n\t"
       "s_waitcnt lgkmcnt(8)\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x0], %[b0], 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x1], %[b1], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x2], %[b2], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x3], %[b3], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x4], %[b4], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x5], %[b5], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x6], %[b6], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x7], %[b7], %[s]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[128:131], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[132:135], %[b1], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[136:139], %[b2], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[140:143], %[b3], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[144:147], %[b4], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[148:151], %[b5], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[152:155], %[b6], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[156:159], %[b7], %[s0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x8], %[b8], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x9], %[b9], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x10], %[b10], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x11], %[b11], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x12], %[b12], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x13], %[b13], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x14], %[b14], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x15], %[b15], %[s]\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[128:131], %[a1] offset:0\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:64\n\t"
+      "ds_read_b128 v[136:139], %[a1] offset:128\n\t"
+      "ds_read_b128 v[140:143], %[a1] offset:192\n\t"
+      "ds_read_b128 v[144:147], %[a1] offset:256\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:320\n\t"
+      "ds_read_b128 v[152:155], %[a1] offset:384\n\t"
+      "ds_read_b128 v[156:159], %[a1] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[160:163], %[b8], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[164:167], %[b9], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[168:171], %[b10], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[172:175], %[b11], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[176:179], %[b12], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[180:183], %[b13], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[184:187], %[b14], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[188:191], %[b15], %[s0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[160:163], %[a1] offset:512\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:576\n\t"
+      "ds_read_b128 v[168:171], %[a1] offset:640\n\t"
+      "ds_read_b128 v[172:175], %[a1] offset:704\n\t"
+      "ds_read_b128 v[176:179], %[a1] offset:768\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:832\n\t"
+      "ds_read_b128 v[184:187], %[a1] offset:896\n\t"
+      "ds_read_b128 v[188:191], %[a1] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[128:131], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[132:135], %[b1], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[136:139], %[b2], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[140:143], %[b3], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[144:147], %[b4], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[148:151], %[b5], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[152:155], %[b6], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[156:159], %[b7], %[s1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[128:131], %[a2] offset:0\n\t"
+      "ds_read_b128 v[132:135], %[a2] offset:64\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:128\n\t"
+      "ds_read_b128 v[140:143], %[a2] offset:192\n\t"
+      "ds_read_b128 v[144:147], %[a2] offset:256\n\t"
+      "ds_read_b128 v[148:151], %[a2] offset:320\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:384\n\t"
+      "ds_read_b128 v[156:159], %[a2] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[160:163], %[b8], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[164:167], %[b9], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[168:171], %[b10], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[172:175], %[b11], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[176:179], %[b12], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[180:183], %[b13], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[184:187], %[b14], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[188:191], %[b15], %[s1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[160:163], %[a2] offset:512\n\t"
+      "ds_read_b128 v[164:167], %[a2] offset:576\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:640\n\t"
+      "ds_read_b128 v[172:175], %[a2] offset:704\n\t"
+      "ds_read_b128 v[176:179], %[a2] offset:768\n\t"
+      "ds_read_b128 v[180:183], %[a2] offset:832\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:896\n\t"
+      "ds_read_b128 v[188:191], %[a2] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[128:131], %[c0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[132:135], %[c1], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[136:139], %[c2], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[140:143], %[c3], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[144:147], %[c4], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[148:151], %[c5], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[152:155], %[c6], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[156:159], %[c7], %[d0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[128:131], %[a3] offset:0\n\t"
+      "ds_read_b128 v[132:135], %[a3] offset:64\n\t"
+      "ds_read_b128 v[136:139], %[a3] offset:128\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:192\n\t"
+      "ds_read_b128 v[144:147], %[a3] offset:256\n\t"
+      "ds_read_b128 v[148:151], %[a3] offset:320\n\t"
+      "ds_read_b128 v[152:155], %[a3] offset:384\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[160:163], %[c8], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[164:167], %[c9], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[168:171], %[c10], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[172:175], %[c11], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[176:179], %[c12], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[180:183], %[c13], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[184:187], %[c14], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[188:191], %[c15], %[d0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[160:163], %[a3] offset:512\n\t"
+      "ds_read_b128 v[164:167], %[a3] offset:576\n\t"
+      "ds_read_b128 v[168:171], %[a3] offset:640\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:704\n\t"
+      "ds_read_b128 v[176:179], %[a3] offset:768\n\t"
+      "ds_read_b128 v[180:183], %[a3] offset:832\n\t"
+      "ds_read_b128 v[184:187], %[a3] offset:896\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[128:131], %[c0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[132:135], %[c1], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[136:139], %[c2], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[140:143], %[c3], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[144:147], %[c4], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[148:151], %[c5], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[152:155], %[c6], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[156:159], %[c7], %[d1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[160:163], %[c8], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[164:167], %[c9], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[168:171], %[c10], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[172:175], %[c11], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[176:179], %[c12], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[180:183], %[c13], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[184:187], %[c14], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[188:191], %[c15], %[d1]\n\t"
       "s_nop 15\n\ts_nop 3"
-      : [s] "=&v"(s), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]),
-        [x3] "=&v"(x[3]), [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]),
-        [x7] "=&v"(x[7]), [x8] "=&v"(x[8]), [x9] "=&v"(x[9]), [x10] "=&v"(x[10]),
-        [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]), [x14] "=&v"(x[14]),
-        [x15] "=&v"(x[15])
-      : [xa] "v"(xad), [b0] "a"(b[0]), [b1] "a"(b[1]), [b2] "a"(b[2]),
-        [b3] "a"(b[3]), [b4] "a"(b[4]), [b5] "a"(b[5]), [b6] "a"(b[6]),
-        [b7] "a"(b[7]), [b8] "a"(b[8]), [b9] "a"(b[9]), [b10] "a"(b[10]),
-        [b11] "a"(b[11]), [b12] "a"(b[12]), [b13] "a"(b[13]), [b14] "a"(b[14]),
-        [b15] "a"(b[15])
-      : "memory");
+      : [s0] "=&v"(s0), [s1] "=&v"(s1), [d0] "=&v"(d0), [d1] "=&v"(d1)
+      : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),
+        [b0] "a"(b[0]), [b1] "a"(b[1]), [b2] "a"(b[2]), [b3] "a"(b[3]),
+        [b4] "a"(b[4]), [b5] "a"(b[5]), [b6] "a"(b[6]), [b7] "a"(b[7]),
+        [b8] "a"(b[8]), [b9] "a"(b[9]), [b10] "a"(b[10]), [b11] "a"(b[11]),
+        [b12] "a"(b[12]), [b13] "a"(b[13]), [b14] "a"(b[14]), [b15] "a"(b[15]),
+        [c0] "a"(c[0]), [c1] "a"(c[1]), [c2] "a"(c[2]), [c3] "a"(c[3]),
+        [c4] "a"(c[4]), [c5] "a"(c[5]), [c6] "a"(c[6]), [c7] "a"(c[7]),
+        [c8] "a"(c[8]), [c9] "a"(c[9]), [c10] "a"(c[10]), [c11] "a"(c[11]),
+        [c12] "a"(c[12]), [c13] "a"(c[13]), [c14] "a"(c[14]), [c15] "a"(c[15])
+      : "memory", "v128", "v129", "v130", "v131", "v132", "v133", "v134", "v135", "v136", "v137", "v138", "v139", "v140", "v141", "v142", "v143", "v144", "v145", "v146", "v147", "v148", "v149", "v150", "v151", "v152", "v153", "v154", "v155", "v156", "v157", "v158", "v159", "v160", "v161", "v162", "v163", "v164", "v165", "v166", "v167", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191");
 }
-// The same with B in VGPRs, after four 16-byte reads (row statistics).
-__device__ __forceinline__ void chain_vs(f32x4& s, uint32_t xad, const bf16x8 (&b)[16], uint32_t sad, f32x4 (&st)[4]) {
-  bf16x8 x[16];
+__device__ __forceinline__ void chains_keys(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16], uint32_t sad, f32x4 (&st)[4]) {
   asm volatile(
       "ds_read_b128 %[st0], %[sa] offset:0\n\t"
       "ds_read_b128 %[st1], %[sa] offset:64\n\t"
       "ds_read_b128 %[st2], %[sa] offset:128\n\t"
       "ds_read_b128 %[st3], %[sa] offset:192\n\t"
-      "ds_read_b128 %[x0], %[xa] offset:0\n\t"
-      "ds_read_b128 %[x1], %[xa] offset:64\n\t"
-      "ds_read_b128 %[x2], %[xa] offset:128\n\t"
-      "ds_read_b128 %[x3], %[xa] offset:192\n\t"
-      "ds_read_b128 %[x4], %[xa] offset:256\n\t"
-      "ds_read_b128 %[x5], %[xa] offset:320\n\t"
-      "ds_read_b128 %[x6], %[xa] offset:384\n\t"
-      "ds_read_b128 %[x7], %[xa] offset:448\n\t"
-      "ds_read_b128 %[x8], %[xa] offset:512\n\t"
-      "ds_read_b128 %[x9], %[xa] offset:576\n\t"
-      "ds_read_b128 %[x10], %[xa] offset:640\n\t"
-      "ds_read_b128 %[x11], %[xa] offset:704\n\t"
-      "ds_read_b128 %[x12], %[xa] offset:768\n\t"
-      "ds_read_b128 %[x13], %[xa] offset:832\n\t"
-      "ds_read_b128 %[x14], %[xa] offset:896\n\t"
-      "ds_read_b128 %[x15], %[xa] offset:960\n\t"
-      "s_waitcnt lgkmcnt(8)\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x0], %[b0], 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x1], %[b1], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x2], %[b2], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x3], %[b3], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x4], %[b4], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x5], %[b5], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x6], %[b6], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x7], %[b7], %[s]\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:0\n\t"
+      "ds_read_b128 v[196:199], %[a0] offset:64\n\t"
+      "ds_read_b128 v[200:203], %[a0] offset:128\n\t"
+      "ds_read_b128 v[204:207], %[a0] offset:192\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:256\n\t"
+      "ds_read_b128 v[212:215], %[a0] offset:320\n\t"
+      "ds_read_b128 v[216:219], %[a0] offset:384\n\t"
+      "ds_read_b128 v[220:223], %[a0] offset:448\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[192:195], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[196:199], %[b1], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[200:203], %[b2], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[204:207], %[b3], %[s0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x8], %[b8], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x9], %[b9], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x10], %[b10], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x11], %[b11], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x12], %[b12], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x13], %[b13], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x14], %[b14], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x15], %[b15], %[s]\n\t"
-      "s_nop 15\n\ts_nop 3"
-      : [s] "=&v"(s), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]),
-        [x3] "=&v"(x[3]), [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]),
-        [x7] "=&v"(x[7]), [x8] "=&v"(x[8]), [x9] "=&v"(x[9]), [x10] "=&v"(x[10]),
-        [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]), [x14] "=&v"(x[14]),
-        [x15] "=&v"(x[15]), [st0] "=&v"(st[0]), [st1] "=&v"(st[1]), [st2] "=&v"(st[2]),
-        [st3] "=&v"(st[3])
-      : [xa] "v"(xad), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]),
-        [b3] "v"(b[3]), [b4] "v"(b[4]), [b5] "v"(b[5]), [b6] "v"(b[6]),
-        [b7] "v"(b[7]), [b8] "v"(b[8]), [b9] "v"(b[9]), [b10] "v"(b[10]),
-        [b11] "v"(b[11]), [b12] "v"(b[12]), [b13] "v"(b[13]), [b14] "v"(b[14]),
-        [b15] "v"(b[15]), [sa] "v"(sad)
-      : "memory");
-}
-__device__ __forceinline__ void chain_v(f32x4& s, uint32_t xad, const bf16x8 (&b)[16]) {
-  bf16x8 x[16];
-  asm volatile(
-      "ds_read_b128 %[x0], %[xa] offset:0\n\t"
-      "ds_read_b128 %[x1], %[xa] offset:64\n\t"
-      "ds_read_b128 %[x2], %[xa] offset:128\n\t"
-      "ds_read_b128 %[x3], %[xa] offset:192\n\t"
-      "ds_read_b128 %[x4], %[xa] offset:256\n\t"
-      "ds_read_b128 %[x5], %[xa] offset:320\n\t"
-      "ds_read_b128 %[x6], %[xa] offset:384\n\t"
-      "ds_read_b128 %[x7], %[xa] offset:448\n\t"
-      "ds_read_b128 %[x8], %[xa] offset:512\n\t"
-      "ds_read_b128 %[x9], %[xa] offset:576\n\t"
-      "ds_read_b128 %[x10], %[xa] offset:640\n\t"
-      "ds_read_b128 %[x11], %[xa] offset:704\n\t"
-      "ds_read_b128 %[x12], %[xa] offset:768\n\t"
-      "ds_read_b128 %[x13], %[xa] offset:832\n\t"
-      "ds_read_b128 %[x14], %[xa] offset:896\n\t"
-      "ds_read_b128 %[x15], %[xa] offset:960\n\t"
-      "s_waitcnt lgkmcnt(8)\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x0], %[b0], 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x1], %[b1], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x2], %[b2], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x3], %[b3], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x4], %[b4], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x5], %[b5], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x6], %[b6], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x7], %[b7], %[s]\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:512\n\t"
+      "ds_read_b128 v[196:199], %[a0] offset:576\n\t"
+      "ds_read_b128 v[200:203], %[a0] offset:640\n\t"
+      "ds_read_b128 v[204:207], %[a0] offset:704\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[208:211], %[b4], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[212:215], %[b5], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[216:219], %[b6], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[220:223], %[b7], %[s0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x8], %[b8], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x9], %[b9], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x10], %[b10], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x11], %[b11], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x12], %[b12], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x13], %[b13], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x14], %[b14], %[s]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[s], %[x15], %[b15], %[s]\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:768\n\t"
+      "ds_read_b128 v[212:215], %[a0] offset:832\n\t"
+      "ds_read_b128 v[216:219], %[a0] offset:896\n\t"
+      "ds_read_b128 v[220:223], %[a0] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[192:195], %[b8], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[196:199], %[b9], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[200:203], %[b10], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[204:207], %[b11], %[s0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a1] offset:0\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:64\n\t"
+      "ds_read_b128 v[200:203], %[a1] offset:128\n\t"
+      "ds_read_b128 v[204:207], %[a1] offset:192\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[208:211], %[b12], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[212:215], %[b13], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[216:219], %[b14], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[220:223], %[b15], %[s0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a1] offset:256\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:320\n\t"
+      "ds_read_b128 v[216:219], %[a1] offset:384\n\t"
+      "ds_read_b128 v[220:223], %[a1] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[192:195], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[196:199], %[b1], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[200:203], %[b2], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[204:207], %[b3], %[s1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a1] offset:512\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:576\n\t"
+      "ds_read_b128 v[200:203], %[a1] offset:640\n\t"
+      "ds_read_b128 v[204:207], %[a1] offset:704\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[208:211], %[b4], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[212:215], %[b5], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[216:219], %[b6], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[220:223], %[b7], %[s1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a1] offset:768\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:832\n\t"
+      "ds_read_b128 v[216:219], %[a1] offset:896\n\t"
+      "ds_read_b128 v[220:223], %[a1] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[192:195], %[b8], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[196:199], %[b9], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[200:203], %[b10], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[204:207], %[b11], %[s1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a2] offset:0\n\t"
+      "ds_read_b128 v[196:199], %[a2] offset:64\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:128\n\t"
+      "ds_read_b128 v[204:207], %[a2] offset:192\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[208:211], %[b12], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[212:215], %[b13], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[216:219], %[b14], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[220:223], %[b15], %[s1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a2] offset:256\n\t"
+      "ds_read_b128 v[212:215], %[a2] offset:320\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:384\n\t"
+      "ds_read_b128 v[220:223], %[a2] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[192:195], %[c0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[196:199], %[c1], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[200:203], %[c2], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[204:207], %[c3], %[d0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a2] offset:512\n\t"
+      "ds_read_b128 v[196:199], %[a2] offset:576\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:640\n\t"
+      "ds_read_b128 v[204:207], %[a2] offset:704\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[208:211], %[c4], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[212:215], %[c5], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[216:219], %[c6], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[220:223], %[c7], %[d0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a2] offset:768\n\t"
+      "ds_read_b128 v[212:215], %[a2] offset:832\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:896\n\t"
+      "ds_read_b128 v[220:223], %[a2] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[192:195], %[c8], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[196:199], %[c9], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[200:203], %[c10], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[204:207], %[c11], %[d0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a3] offset:0\n\t"
+      "ds_read_b128 v[196:199], %[a3] offset:64\n\t"
+      "ds_read_b128 v[200:203], %[a3] offset:128\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:192\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[208:211], %[c12], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[212:215], %[c13], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[216:219], %[c14], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[220:223], %[c15], %[d0]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a3] offset:256\n\t"
+      "ds_read_b128 v[212:215], %[a3] offset:320\n\t"
+      "ds_read_b128 v[216:219], %[a3] offset:384\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[192:195], %[c0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[196:199], %[c1], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[200:203], %[c2], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[204:207], %[c3], %[d1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a3] offset:512\n\t"
+      "ds_read_b128 v[196:199], %[a3] offset:576\n\t"
+      "ds_read_b128 v[200:203], %[a3] offset:640\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:704\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[208:211], %[c4], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[212:215], %[c5], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[216:219], %[c6], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[220:223], %[c7], %[d1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a3] offset:768\n\t"
+      "ds_read_b128 v[212:215], %[a3] offset:832\n\t"
+      "ds_read_b128 v[216:219], %[a3] offset:896\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[192:195], %[c8], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[196:199], %[c9], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[200:203], %[c10], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[204:207], %[c11], %[d1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[208:211], %[c12], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[212:215], %[c13], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[216:219], %[c14], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[220:223], %[c15], %[d1]\n\t"
       "s_nop 15\n\ts_nop 3"
-      : [s] "=&v"(s), [x0] "=&v"(x[0]), [x1] "=&v"(x[1]), [x2] "=&v"(x[2]),
-        [x3] "=&v"(x[3]), [x4] "=&v"(x[4]), [x5] "=&v"(x[5]), [x6] "=&v"(x[6]),
-        [x7] "=&v"(x[7]), [x8] "=&v"(x[8]), [x9] "=&v"(x[9]), [x10] "=&v"(x[10]),
-        [x11] "=&v"(x[11]), [x12] "=&v"(x[12]), [x13] "=&v"(x[13]), [x14] "=&v"(x[14]),
-        [x15] "=&v"(x[15])
-      : [xa] "v"(xad), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]),
-        [b3] "v"(b[3]), [b4] "v"(b[4]), [b5] "v"(b[5]), [b6] "v"(b[6]),
-        [b7] "v"(b[7]), [b8] "v"(b[8]), [b9] "v"(b[9]), [b10] "v"(b[10]),
-        [b11] "v"(b[11]), [b12] "v"(b[12]), [b13] "v"(b[13]), [b14] "v"(b[14]),
-        [b15] "v"(b[15])
-      : "memory");
+      : [s0] "=&v"(s0), [s1] "=&v"(s1), [d0] "=&v"(d0), [d1] "=&v"(d1),
+        [st0] "=&v"(st[0]), [st1] "=&v"(st[1]), [st2] "=&v"(st[2]), [st3] "=&v"(st[3])
+      : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),
+        [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
+        [b4] "v"(b[4]), [b5] "v"(b[5]), [b6] "v"(b[6]), [b7] "v"(b[7]),
+        [b8] "v"(b[8]), [b9] "v"(b[9]), [b10] "v"(b[10]), [b11] "v"(b[11]),
+        [b12] "v"(b[12]), [b13] "v"(b[13]), [b14] "v"(b[14]), [b15] "v"(b[15]),
+        [c0] "v"(c[0]), [c1] "v"(c[1]), [c2] "v"(c[2]), [c3] "v"(c[3]),
+        [c4] "v"(c[4]), [c5] "v"(c[5]), [c6] "v"(c[6]), [c7] "v"(c[7]),
+        [c8] "v"(c[8]), [c9] "v"(c[9]), [c10] "v"(c[10]), [c11] "v"(c[11]),
+        [c12] "v"(c[12]), [c13] "v"(c[13]), [c14] "v"(c[14]), [c15] "v"(c[15]),
+        [sa] "v"(sad)
+      : "memory", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
@@ -546,12 +855,13 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
       arrive();
       uint8_t* const sk = kst(j);
       f32x4 sc[2], dp[2];  // S^T = K Q^T, dP^T = V dA^T
-      chain_a(sc[0], lds_addr(sk + foffF), qf);
-      chain_a(sc[1], lds_addr(sk + 16 * kRowF + foffF), qf);
-      if (j + 1 < nt) issue_k(j + 1, kRowF);
-      chain_a(dp[0], lds_addr(sk + kStage + foffT), daf);
-      chain_a(dp[1], lds_addr(sk + kStage + 16 * kRowT + foffT), daf);
-      if (j + 1 < nt) issue_v(j + 1, kRowT);
+      const uint32_t ad[4] = {lds_addr(sk + foffF), lds_addr(sk + 16 * kRowF + foffF),
+                              lds_addr(sk + kStage + foffT), lds_addr(sk + kStage + 16 * kRowT + foffT)};
+      chains_rows(sc[0], sc[1], dp[0], dp[1], ad, qf, daf);
+      if (j + 1 < nt) {
+        issue_k(j + 1, kRowF);
+        issue_v(j + 1, kRowT);
+      }
       int lo_v, hi_v;
       vis(j, lo_v, hi_v);
       float x[8], mt = -INFINITY;
@@ -577,7 +887,7 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
         pb[i] = (__bf16)e;
         lb += (float)pb[i];
       }
-      tr_tile32(o, lds_addr(sk + kStage + voff), lds_addr(sk + kStage + 16 * kRowT + voff), pb);
+      tr_rows(o, lds_addr(sk + kStage + voff), lds_addr(sk + kStage + 16 * kRowT + voff), pb);
     }
     // the workgroup walks the tiles again (all waves, barriers in step) if a
     // score of any row rose more than 2^64 above its reference
@@ -624,12 +934,13 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     arrive();
     uint8_t* const sk = kst(j);
     f32x4 sc[2], dp[2];
-    chain_a(sc[0], lds_addr(sk + foffT), qf);
-    chain_a(sc[1], lds_addr(sk + 16 * kRowT + foffT), qf);
-    if (j + 1 < nt) issue_k(j + 1, kRowT);
-    chain_a(dp[0], lds_addr(sk + kStage + foffF), daf);
-    chain_a(dp[1], lds_addr(sk + kStage + 16 * kRowF + foffF), daf);
-    if (j + 1 < nt) issue_v(j + 1, kRowF);
+    const uint32_t ad[4] = {lds_addr(sk + foffT), lds_addr(sk + 16 * kRowT + foffT),
+                            lds_addr(sk + kStage + foffF), lds_addr(sk + kStage + 16 * kRowF + foffF)};
+    chains_rows(sc[0], sc[1], dp[0], dp[1], ad, qf, daf);
+    if (j + 1 < nt) {
+      issue_k(j + 1, kRowT);
+      issue_v(j + 1, kRowF);
+    }
     int lo_v, hi_v;
     vis(j, lo_v, hi_v);
     bf16x8 dsb;
@@ -639,7 +950,7 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
       const float p = kk >= lo_v && kk < hi_v ? __builtin_amdgcn_exp2f(sc[i >> 2][i & 3] * a.c - lse) : 0.0f;
       dsb[i] = (__bf16)(p * (dp[i >> 2][i & 3] - dt));
     }
-    tr_tile32(o, lds_addr(sk + voff), lds_addr(sk + 16 * kRowT + voff), dsb);
+    tr_rows(o, lds_addr(sk + voff), lds_addr(sk + 16 * kRowT + voff), dsb);
   }
   mfma_drain();
   if (valid) {
@@ -740,12 +1051,13 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
     // S = Q K^T and dP = dA V^T: lane (key l16, g4) gets rows 16h + 4 g4 + r in
     // sc[h][r]; the statistics of rows 4 g4 .. and 16 + 4 g4 .. (lse, then Dt)
     f32x4 sc[2], dp[2], stt[4];
-    chain_vs(sc[0], lds_addr(sp + foff), kf, lds_addr(sp + 2 * kStage + 16 * g4), stt);
-    chain_v(sc[1], lds_addr(sp + 16 * kRowT + foff), kf);
-    if (i + 1 < nb) issue_q(i + 1);
-    chain_v(dp[0], lds_addr(sp + kStage + foff), vf);
-    chain_v(dp[1], lds_addr(sp + kStage + 16 * kRowT + foff), vf);
-    if (i + 1 < nb) issue_a(i + 1);
+    const uint32_t ad[4] = {lds_addr(sp + foff), lds_addr(sp + 16 * kRowT + foff),
+                            lds_addr(sp + kStage + foff), lds_addr(sp + kStage + 16 * kRowT + foff)};
+    chains_keys(sc[0], sc[1], dp[0], dp[1], ad, kf, vf, lds_addr(sp + 2 * kStage + 16 * g4), stt);
+    if (i + 1 < nb) {
+      issue_q(i + 1);
+      issue_a(i + 1);
+    }
     bf16x8 pb, dsb;
 #pragma unroll
     for (int i8 = 0; i8 < 8; ++i8) {
@@ -758,8 +1070,8 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
       dsb[i8] = (__bf16)(p * (dp[h][r] - stt[2 + h][r]));
     }
     // dV^T += dA^T P, dK^T += Q^T dS (transposing reads of the row tiles)
-    tr_tile32(dv, lds_addr(sp + kStage + voff), lds_addr(sp + kStage + 16 * kRowT + voff), pb);
-    tr_tile32(dk, lds_addr(sp + voff), lds_addr(sp + 16 * kRowT + voff), dsb);
+    tr_keys(dv, lds_addr(sp + kStage + voff), lds_addr(sp + kStage + 16 * kRowT + voff), pb);
+    tr_keys(dk, lds_addr(sp + voff), lds_addr(sp + 16 * kRowT + voff), dsb);
   }
   mfma_drain();
   // lane (key l16, g4) holds dims 16 db + 4 g4 .. +3 of key l16
