@@ -113,44 +113,75 @@ __global__ void __launch_bounds__(256, 1) gate_kernel(GateArgs a) {
   // Fragment offsets: lane (i = lane % 32, k half = lane / 32) of 32-row block
   // bi reads row 32 bi + i, logical chunk 2 kk + lane / 32.
   const int fi = lane & 31, fh = lane >> 5;
-
-  for (int s = 0; s < nk; ++s) {
-    // This wave's copies of step s have landed (steps s+1, s+2 may be in
-    // flight: 8 copies each), then every wave's, and every wave is done with
-    // step s-1, whose stage step s+3 reuses.
-    if (s + 2 < nk)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 16);  // vmcnt(16)
-    else if (s + 1 < nk)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 8);   // vmcnt(8)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
-    barrier_no_fence();
-    if (s + 3 < nk) {
-      uint8_t* st = lds + ((s + 3) % kStages) * kStageB;
-      dma_slice(rw, ld, (s + 3) * kBK, st, wave, lane);
-      dma_slice(rl, ld, (s + 3) * kBK, st + kOpBytes, wave, lane);
-    }
+  auto read_frags = [&](int s, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
     const uint8_t* sw = lds + (s % kStages) * kStageB;
     const uint8_t* sl = sw + kOpBytes;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        const int r = 128 * wa + 32 * bi + fi;
-        af[bi] = *reinterpret_cast<const bf16x8*>(sw + r * kRowB + 16 * chunk_pos(r, 2 * kk + fh));
-      }
-#pragma unroll
-      for (int bj = 0; bj < 4; ++bj) {
-        const int r = 128 * wb + 32 * bj + fi;
-        bfr[bj] = *reinterpret_cast<const bf16x8*>(sl + r * kRowB + 16 * chunk_pos(r, 2 * kk + fh));
-      }
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
-          mfma32(acc[bi][bj], af[bi], bfr[bj]);
+    for (int bi = 0; bi < 4; ++bi) {
+      const int r = 128 * wa + 32 * bi + fi;
+      af[bi] = *reinterpret_cast<const bf16x8*>(sw + r * kRowB + 16 * chunk_pos(r, 2 * kk + fh));
     }
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int r = 128 * wb + 32 * bj + fi;
+      bfr[bj] = *reinterpret_cast<const bf16x8*>(sl + r * kRowB + 16 * chunk_pos(r, 2 * kk + fh));
+    }
+  };
+  // This wave's copies of step s have landed: the copies of the steps after
+  // it that are already issued (up to s + 2, 8 each) may still be in flight.
+  // (s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at "no wait")
+  auto wait_step = [&](int s) {
+    if (s + 2 < nk)
+      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+    else if (s + 1 < nk)
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
+  // One DMA instruction of step t's copies (u = 0..7: W_g rows, then latent rows).
+  auto dma_one = [&](int t, int u) {
+    uint8_t* st = lds + (t % kStages) * kStageB + (u < 4 ? 0 : kOpBytes);
+    const int uu = u & 3, rr = lane >> 2, pos = lane & 3;
+    const int row = 64 * wave + 16 * uu + rr;
+    const int c = pos ^ ((row >> 2) & 3);
+    dma16_buf(u < 4 ? rw : rl, row * ld + 2 * t * kBK + 16 * c, (lds_void*)(st + (64 * wave + 16 * uu) * kRowB));
+  };
+
+  // Step s runs in two halves of 16 MFMAs (k = 0..15, then 16..31):
+  //   first half   MFMAs on the k 0..15 fragments (read during the previous
+  //                step), while this step's k 16..31 fragments are read and
+  //                step s+3's 8 copies issue, one after every other MFMA (an
+  //                issuing copy stalls the wave; spread out, the MFMAs already
+  //                issued keep the pipe busy);
+  //   sync         this wave's copies of step s+1 have landed and its reads of
+  //                step s are done; barrier: every wave's, so step s+1 may be
+  //                read and step s's stage may be refilled by step s+4;
+  //   second half  MFMAs on the k 16..31 fragments, while step s+1's k 0..15
+  //                fragments are read.
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  wait_step(0);
+  barrier_no_fence();
+  read_frags(0, 0, a0, b0);
+  for (int s = 0; s < nk; ++s) {
+    const bool copy = s + 3 < nk;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mfma32(acc[m >> 2][m & 3], a0[m >> 2], b0[m & 3]);
+      if (m == 1) {
+        // after the first MFMAs (which wait for the k 0..15 reads): a wait
+        // placed by the compiler for those would otherwise cover these too
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(s, 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if ((m & 1) && copy) dma_one(s + 3, m >> 1);
+    }
+    if (s + 1 < nk) wait_step(s + 1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's reads are done
+    barrier_no_fence();
+    if (s + 1 < nk) read_frags(s + 1, 0, a0, b0);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) mfma32(acc[m >> 2][m & 3], a1[m >> 2], b1[m & 3]);
   }
 
   asm volatile("s_nop 15\n\ts_nop 15");  // wait states before VALU reads of the accumulators
