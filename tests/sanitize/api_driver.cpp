@@ -85,7 +85,28 @@ int main() {
                                HCA_BF16, nullptr), HCA_ERR_UNSUPPORTED);
   EXPECT(hca_attn_decode_multi(P, P, P, P, 256, P, P, nullptr, P, pos, 64, 3, 64, 512, 128, 128,
                                sc, P, HCA_BF16, nullptr), HCA_ERR_INVALID_ARG);
-  if (g_launches < 8) ++failures;
+  // gate logits
+  EXPECT(hca_gate_logits(P, P, 1000, 1024, 32768, P, nullptr), HCA_OK);
+  EXPECT(hca_gate_logits(P, P, 0, 1024, 32768, P, nullptr), HCA_OK);
+  EXPECT(hca_gate_logits(P, P, 1000, 1000, 32768, P, nullptr), HCA_ERR_UNSUPPORTED);
+  EXPECT(hca_gate_logits(P, P, 1000, 1024, 1000, P, nullptr), HCA_ERR_UNSUPPORTED);
+  EXPECT(hca_gate_logits(MIS, P, 1000, 1024, 32768, P, nullptr), HCA_ERR_INVALID_ARG);
+  // backward
+  const size_t bneed = hca_backward_workspace_size(1000, 64, 512);
+  if (bneed == 0) ++failures;
+  EXPECT(hca_attn_backward(P, P, P, P, P, P, P, 1000, 64, 512, 128, 128, sc, P, P, P, P, P, bneed,
+                           nullptr), HCA_OK);
+  EXPECT(hca_attn_backward(P, P, P, P, P, P, P, 1000, 64, 512, 128, 128, sc, P, P, P, P, P,
+                           bneed - 1, nullptr), HCA_ERR_WORKSPACE);
+  EXPECT(hca_attn_backward(P, P, P, P, nullptr, nullptr, P, 100, 8, 512, 128, 128, sc, P, P, P, P,
+                           P, hca_backward_workspace_size(100, 8, 512), nullptr), HCA_OK);
+  EXPECT(hca_attn_backward(P, P, P, P, P, P, P, 1000, 0, 512, 128, 128, sc, P, P, P, P, P, bneed,
+                           nullptr), HCA_ERR_UNSUPPORTED);
+  EXPECT(hca_attn_backward(P, P, P, P, P, P, MIS, 1000, 64, 512, 128, 128, sc, P, P, P, P, P,
+                           bneed, nullptr), HCA_ERR_INVALID_ARG);
+  EXPECT(hca_attn_backward(nullptr, P, P, P, P, P, P, 0, 64, 512, 128, 128, sc, nullptr, P, P, P,
+                           nullptr, 0, nullptr), HCA_OK);
+  if (g_launches < 11) ++failures;
   if (hca_version() < 100) ++failures;
   std::printf("api sanitizer run: %d failures, %d stub launches\n", failures, g_launches);
   return failures == 0 ? 0 : 1;

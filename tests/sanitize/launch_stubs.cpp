@@ -26,6 +26,17 @@ int decode_splits(int B, int H, int64_t nc_cap) {
   if (n > 16) n = 16;
   return n < 1 ? 1 : n;
 }
+hipError_t launch_gate(const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, int,
+                       hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_backward(const BackwardProblem&, void*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+size_t backward_workspace_bytes(int64_t T, int H) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int64_t rows = T * H, Nc = T / kBlock;
+  return up(rows * 4) * 2 + up(rows * kD * 2) + up(Nc * kD * 4) * 2 + 256;
+}
 size_t decode_workspace_bytes(int B, int H, int64_t nc_cap) {
   const int n = decode_splits(B, H, nc_cap);
   return n <= 1 ? 0 : (size_t)B * ((H + 15) / 16) * n * (32 + 16 * kD) * sizeof(float);
