@@ -51,6 +51,8 @@ def bind(lib):
     lib.hca_oracle_decode.argtypes = [P, P, P, P, I64, P, P, P, I, I, I, I, I, D, P, I]
     lib.hca_oracle_attn_backward.argtypes = [P, P, P, I64, P, P, P, P, I64, I, I, I, I, D, P, P,
                                              P, P, P, P, I]
+    lib.hca_oracle_attn_backward_rows.argtypes = [P, P, P, P, I64, I64, P, P, P, P, I64, I, I, I,
+                                                  I, D, P, P, I]
     lib.hca_oracle_round_bf16.argtypes = [D]
     lib.hca_oracle_round_bf16.restype = ctypes.c_uint16
     lib.hca_oracle_widen_bf16.argtypes = [ctypes.c_uint16]
@@ -262,3 +264,33 @@ def attn_backward(q, g, dout, k, v, *, block=128, window=128, scale=None, nthrea
         dk[:Nc * block] += np.repeat(dck[:Nc] / block, block, axis=0)
         dv[:Nc * block] += np.repeat(dcv[:Nc] / block, block, axis=0)
     return dq, dk, dv, dg
+
+
+def attn_backward_rows(q, g, dout, positions, k, v, *, block=128, window=128, scale=None,
+                       nthreads=0):
+    """dq and dg of the query rows at the given positions of a whole sequence whose raw
+    rows are k, v [T, D] (entries = ``compress`` of them), by the same per-row routine
+    as ``attn_backward`` (C ``hca_oracle_attn_backward_rows``); the key gradients need
+    every row and are not formed.
+      q, g, dout [n, H, D]: bfloat16 bits of the rows of positions[i]
+    Returns float64 (dq [n, H, D], dg [n, H, D])."""
+    q, g, dout, k, v = _u16(q), _u16(g), _u16(dout), _u16(k), _u16(v)
+    n, H, D = q.shape
+    T = k.shape[0]
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    assert g.shape == q.shape and dout.shape == q.shape and k.shape == (T, D) == v.shape
+    assert pos.shape == (n,)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    ck, cv = compress(k, block), compress(v, block)
+    Nc = ck.shape[0]
+    dq = np.empty((n, H, D))
+    dg = np.empty((n, H, D))
+    rc = _load().hca_oracle_attn_backward_rows(
+        _ptr(q), _ptr(g), _ptr(dout), _ptr(pos), n, T, _ptr(k), _ptr(v),
+        _ptr(ck) if Nc else None, _ptr(cv) if Nc else None, Nc, H, D, block, window,
+        float(scale), _ptr(dq), _ptr(dg), int(nthreads))
+    if rc:
+        raise OracleError(f"hca_oracle_attn_backward_rows: {rc}")
+    return dq, dg
+

@@ -299,6 +299,85 @@ int hca_oracle_decode(const uint16_t *q, const uint16_t *g, const uint16_t *ck,
  * Each thread accumulates its own copy of dk, dv, dck, dcv; the copies are
  * added in thread order at the end.
  */
+/*
+ * One (t, h) row of the backward (row data at offset off of q, g, dout, dq,
+ * dg): gathers the row's keys, recomputes its weights p and ungated output a,
+ * writes dq and dg of the row and, when ak, av are given, adds the row's key
+ * gradients into them (accumulator row s for raw row s, T + b for entry b).
+ * kid, keys, vals, p, dp (Nc + window) and a, da (D) are the caller's scratch.
+ */
+static void backward_row(const uint16_t *q, const uint16_t *g, const uint16_t *dout, size_t off,
+                         int64_t t, int64_t T, const uint16_t *k, const uint16_t *v,
+                         const uint16_t *ck, const uint16_t *cv, int64_t Nc, int D, int block,
+                         int window, double scale, double *dq, double *dg, double *ak, double *av,
+                         int64_t *kid, const uint16_t **keys, const uint16_t **vals, double *p,
+                         double *dp, double *a, double *da)
+{
+    int64_t nk = 0;
+    for (int64_t b = 0; b < Nc; ++b) {
+        if (b * block + block - 1 <= t) {
+            keys[nk] = ck + b * D;
+            vals[nk] = cv + b * D;
+            kid[nk] = T + b;
+            ++nk;
+        }
+    }
+    const int64_t lo = t - window + 1 < 0 ? 0 : t - window + 1;
+    for (int64_t s = lo; s <= t; ++s) {
+        keys[nk] = k + s * D;
+        vals[nk] = v + s * D;
+        kid[nk] = s;
+        ++nk;
+    }
+    /* forward: weights and the ungated output */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nk; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += widen_bf16(q[off + d]) * widen_bf16(keys[j][d]);
+        p[j] = scale * dot;
+        if (p[j] > m) m = p[j];
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        p[j] = exp(p[j] - m);
+        z += p[j];
+    }
+    for (int64_t j = 0; j < nk; ++j) p[j] /= z;
+    for (int d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < nk; ++j) acc += p[j] * widen_bf16(vals[j][d]);
+        a[d] = acc;
+    }
+    /* gate and its gradient */
+    for (int d = 0; d < D; ++d) {
+        const double sig = 1.0 / (1.0 + exp(-widen_bf16(g[off + d])));
+        const double go = widen_bf16(dout[off + d]);
+        dg[off + d] = go * a[d] * sig * (1.0 - sig);
+        da[d] = go * sig;
+    }
+    /* softmax backward */
+    double dsum = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += da[d] * widen_bf16(vals[j][d]);
+        dp[j] = dot;
+        dsum += p[j] * dot;
+    }
+    for (int d = 0; d < D; ++d) dq[off + d] = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        const double ds = p[j] * (dp[j] - dsum);
+        double *akj = ak ? ak + (size_t)kid[j] * D : NULL;
+        double *avj = av ? av + (size_t)kid[j] * D : NULL;
+        for (int d = 0; d < D; ++d) {
+            dq[off + d] += scale * ds * widen_bf16(keys[j][d]);
+            if (akj) {
+                akj[d] += scale * ds * widen_bf16(q[off + d]);
+                avj[d] += p[j] * da[d];
+            }
+        }
+    }
+}
+
 int hca_oracle_attn_backward(const uint16_t *q, const uint16_t *g, const uint16_t *dout,
                              int64_t T, const uint16_t *k, const uint16_t *v,
                              const uint16_t *ck, const uint16_t *cv, int64_t Nc, int H, int D,
@@ -340,70 +419,9 @@ int hca_oracle_attn_backward(const uint16_t *q, const uint16_t *g, const uint16_
 #pragma omp barrier
         if (!failed) {
 #pragma omp for schedule(static)
-            for (int64_t r = 0; r < T * H; ++r) {
-                const int64_t t = r / H;
-                const size_t off = (size_t)r * D;
-                int64_t nk = 0;
-                for (int64_t b = 0; b < Nc; ++b) {
-                    if (b * block + block - 1 <= t) {
-                        keys[nk] = ck + b * D;
-                        vals[nk] = cv + b * D;
-                        kid[nk] = T + b;
-                        ++nk;
-                    }
-                }
-                const int64_t lo = t - window + 1 < 0 ? 0 : t - window + 1;
-                for (int64_t s = lo; s <= t; ++s) {
-                    keys[nk] = k + s * D;
-                    vals[nk] = v + s * D;
-                    kid[nk] = s;
-                    ++nk;
-                }
-                /* forward: weights and the ungated output */
-                double m = -INFINITY;
-                for (int64_t j = 0; j < nk; ++j) {
-                    double dot = 0.0;
-                    for (int d = 0; d < D; ++d) dot += widen_bf16(q[off + d]) * widen_bf16(keys[j][d]);
-                    p[j] = scale * dot;
-                    if (p[j] > m) m = p[j];
-                }
-                double z = 0.0;
-                for (int64_t j = 0; j < nk; ++j) {
-                    p[j] = exp(p[j] - m);
-                    z += p[j];
-                }
-                for (int64_t j = 0; j < nk; ++j) p[j] /= z;
-                for (int d = 0; d < D; ++d) {
-                    double acc = 0.0;
-                    for (int64_t j = 0; j < nk; ++j) acc += p[j] * widen_bf16(vals[j][d]);
-                    a[d] = acc;
-                }
-                /* gate and its gradient */
-                for (int d = 0; d < D; ++d) {
-                    const double sig = 1.0 / (1.0 + exp(-widen_bf16(g[off + d])));
-                    const double go = widen_bf16(dout[off + d]);
-                    dg[off + d] = go * a[d] * sig * (1.0 - sig);
-                    da[d] = go * sig;
-                }
-                /* softmax backward */
-                double dsum = 0.0;
-                for (int64_t j = 0; j < nk; ++j) {
-                    double dot = 0.0;
-                    for (int d = 0; d < D; ++d) dot += da[d] * widen_bf16(vals[j][d]);
-                    dp[j] = dot;
-                    dsum += p[j] * dot;
-                }
-                for (int d = 0; d < D; ++d) dq[off + d] = 0.0;
-                for (int64_t j = 0; j < nk; ++j) {
-                    const double ds = p[j] * (dp[j] - dsum);
-                    double *akj = ak + (size_t)kid[j] * D, *avj = av + (size_t)kid[j] * D;
-                    for (int d = 0; d < D; ++d) {
-                        dq[off + d] += scale * ds * widen_bf16(keys[j][d]);
-                        akj[d] += scale * ds * widen_bf16(q[off + d]);
-                        avj[d] += p[j] * da[d];
-                    }
-                }
-            }
+            for (int64_t r = 0; r < T * H; ++r)
+                backward_row(q, g, dout, (size_t)r * D, r / H, T, k, v, ck, cv, Nc, D, block,
+                             window, scale, dq, dg, ak, av, kid, keys, vals, p, dp, a, da);
         }
         free(kid);
         free(keys);
@@ -432,5 +450,58 @@ int hca_oracle_attn_backward(const uint16_t *q, const uint16_t *g, const uint16_
     }
     free(acc_k);
     free(acc_v);
+    return failed ? ORACLE_ENOMEM : 0;
+}
+
+/*
+ * dq and dg of the rows of chosen query positions only (the same per-row
+ * computation as hca_oracle_attn_backward; the key gradients, which need every
+ * row, are not formed): q, g, dout, dq, dg are [npos, H, D], row i of them
+ * belonging to position pos[i] of the sequence whose raw rows k, v are [T, D]
+ * and entries ck, cv [Nc, D].
+ */
+int hca_oracle_attn_backward_rows(const uint16_t *q, const uint16_t *g, const uint16_t *dout,
+                                  const int64_t *pos, int64_t npos, int64_t T, const uint16_t *k,
+                                  const uint16_t *v, const uint16_t *ck, const uint16_t *cv,
+                                  int64_t Nc, int H, int D, int block, int window, double scale,
+                                  double *dq, double *dg, int nthreads)
+{
+    if (!q || !g || !dout || !pos || !k || !v || !dq || !dg || npos < 0 || T < 0 || H <= 0 ||
+        D <= 0 || block <= 0 || window <= 0 || Nc < 0 || Nc > T / block)
+        return ORACLE_EBADARG;
+    if (Nc > 0 && (!ck || !cv)) return ORACLE_EBADARG;
+    for (int64_t i = 0; i < npos; ++i)
+        if (pos[i] < 0 || pos[i] >= T) return ORACLE_EBADARG;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    const int64_t maxkeys = Nc + window;
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        int64_t *kid = malloc(sizeof(*kid) * (size_t)maxkeys);
+        const uint16_t **keys = malloc(sizeof(*keys) * (size_t)maxkeys);
+        const uint16_t **vals = malloc(sizeof(*vals) * (size_t)maxkeys);
+        double *p = malloc(sizeof(*p) * (size_t)maxkeys);
+        double *dp = malloc(sizeof(*dp) * (size_t)maxkeys);
+        double *a = malloc(sizeof(*a) * (size_t)D);
+        double *da = malloc(sizeof(*da) * (size_t)D);
+        if (!kid || !keys || !vals || !p || !dp || !a || !da) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp barrier
+        if (!failed) {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < npos * H; ++r)
+                backward_row(q, g, dout, (size_t)r * D, pos[r / H], T, k, v, ck, cv, Nc, D, block,
+                             window, scale, dq, dg, NULL, NULL, kid, keys, vals, p, dp, a, da);
+        }
+        free(kid);
+        free(keys);
+        free(vals);
+        free(p);
+        free(dp);
+        free(a);
+        free(da);
+    }
     return failed ? ORACLE_ENOMEM : 0;
 }

@@ -155,3 +155,51 @@ def test_backward_empty():
     fk = torch.empty((0, D), dtype=torch.float32, device=dev())
     hca.hca_attn_backward(e, e, kv, kv, None, None, e, f, fk, fk.clone(), f.clone())
     torch.cuda.synchronize()
+
+
+def _sums_and_rows(T, seed, n_blocks, n_random):
+    """Full-size backward: every row of dq and dg at sampled positions against the
+    oracle's per-row routine (dg exact, dq with the bf16-rounded dA, see check()),
+    and over the whole sequence the key-gradient sums, which the mathematics fixes:
+    sum_t dk[t] = 0 (the score gradients of each row sum to zero) and
+    sum_t dv[t] = sum_(t,h) dO sigmoid(g) (the weights of each row sum to one),
+    each dim within 1e-2 of the sum of the magnitudes it adds."""
+    from tests.gpu_util import sample_positions
+    H = 64
+    print(f"backward T={T} H={H} (sampled rows)", flush=True)
+    b = Backward(seed, T, H)
+    b.run()
+    pos = sample_positions(0, T, seed, n_blocks=n_blocks, n_random=n_random)
+    idx = torch.as_tensor(pos, device=dev())
+    qs, gs, dos = (host(t.index_select(0, idx)) for t in (b.q, b.g, b.do))
+    kh, vh = host(b.k), host(b.v)
+    dq_e, dg_e = oracle.attn_backward_rows(qs, gs, dos, pos, kh, vh, nthreads=16)
+    gf = synth.bf16_bits_to_f32(gs).astype(np.float64)
+    dof = synth.bf16_bits_to_f32(dos).astype(np.float64)
+    da = synth.f64_to_bf16_bits(dof / (1.0 + np.exp(-gf)))
+    dq_r, _ = oracle.attn_backward_rows(qs, np.full(da.shape, 0x4220, np.uint16), da, pos, kh, vh,
+                                        nthreads=16)
+    got_dq = b.dq.index_select(0, idx).cpu().numpy().astype(np.float64)
+    got_dg = b.dg.index_select(0, idx).cpu().numpy().astype(np.float64)
+    f_dq, f_dg = _compare(got_dq, dq_r, "dq~"), _compare(got_dg, dg_e, "dg")
+    print(len(pos), "positions", {"dq~": f_dq, "dg": f_dg}, flush=True)
+    assert f_dq["ok"] and f_dg["ok"], (f_dq, f_dg)
+    # the sums over the whole sequence (fp64 on the GPU, from the inputs)
+    want_v = torch.zeros(D, dtype=torch.float64, device=dev())
+    for t0 in range(0, T, 8192):
+        sl = slice(t0, min(T, t0 + 8192))
+        want_v += (b.do[sl].double() * torch.sigmoid(b.g[sl].double())).sum(dim=(0, 1))
+    for name, t, want in (("dv", b.dv, want_v), ("dk", b.dk, torch.zeros_like(want_v))):
+        s = t.double().sum(dim=0)
+        mag = t.double().abs().sum(dim=0)
+        worst = float(((s - want).abs() / mag).max())
+        print(f"sum of {name}: worst dim error / magnitude {worst:.3g}", flush=True)
+        assert worst <= 1e-2, (name, worst)
+
+
+def test_backward_8k_sampled_rows_and_sums():
+    _sums_and_rows(8192, 88, n_blocks=16, n_random=64)
+
+
+def test_backward_128k_sampled_rows_and_sums():
+    _sums_and_rows(131072, 128, n_blocks=8, n_random=24)

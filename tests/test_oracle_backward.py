@@ -181,3 +181,29 @@ def mutant(tmp_path, request, monkeypatch):
 def test_backward_mutant_is_caught(mutant):
     q, g, do, k, v = _inputs(1, 23, 2, 8)
     assert _fd_check(q, g, do, k, v, 4, 4, 0.35, n_coords=12) > 1e-4, mutant
+
+
+def test_rows_equal_the_full_routine():
+    # the row-sampled entry point runs the same per-row code: bit for bit the rows
+    # of the whole-sequence result, for positions around block and window edges
+    T, H, D = 700, 3, 64
+    q, g, do, k, v = _inputs(21, T, H, D)
+    dq, _, _, dg = oracle.attn_backward(q, g, do, k, v, scale=0.125)
+    pos = np.array([0, 1, 126, 127, 128, 255, 256, 383, 511, 600, 699], dtype=np.int64)
+    dq_r, dg_r = oracle.attn_backward_rows(q[pos], g[pos], do[pos], pos, k, v, scale=0.125)
+    np.testing.assert_array_equal(dq_r, dq[pos])
+    np.testing.assert_array_equal(dg_r, dg[pos])
+
+
+def test_key_gradient_sums():
+    # sum_j ds_j = 0 for every row, so the key gradients sum to zero; the weights
+    # sum to one, so the value gradients sum to sum over rows of dO * sigmoid(g)
+    # (both through the entries too: an entry's gradient reaches its block's rows
+    # divided by the block size, which keeps the sums)
+    T, H, D = 600, 2, 32
+    q, g, do, k, v = _inputs(22, T, H, D)
+    _, dk, dv, _ = oracle.attn_backward(q, g, do, k, v, scale=0.3)
+    gf, dof = widen(g), widen(do)
+    want_v = (dof / (1.0 + np.exp(-gf))).sum(axis=(0, 1))
+    np.testing.assert_allclose(dv.sum(axis=0), want_v, rtol=1e-10, atol=1e-10)
+    assert np.abs(dk.sum(axis=0)).max() <= 1e-10 * np.abs(dk).sum()
