@@ -97,3 +97,19 @@ def test_empty_is_noop():
     lat, w = _inputs(1, 4, 64, 2048)
     g = torch.empty((0, 2048), dtype=torch.bfloat16, device=dev())
     hca.hca_gate_logits(lat[:0], w, g)
+
+
+def test_logits_128k_sampled_rows():
+    # the measured shape, 131072 x 1024 x 32768: the GEMM at full size, rows of
+    # seeded tiles (the first, last and random ones, every n) against the oracle
+    T, R, N = 131072, 1024, 32768
+    lat, w = _inputs(31, T, R, N)
+    g = torch.empty((T, N), dtype=torch.bfloat16, device=dev())
+    hca.hca_gate_logits(lat, w, g)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(T - 4, T), np.arange(255, 259),
+                                     rng.integers(0, T, 48)]))
+    idx = torch.as_tensor(rows, device=dev())
+    want = oracle.gate_logits(host(lat.index_select(0, idx)), host(w))
+    _check_logits(host(g.index_select(0, idx)), want)
