@@ -395,6 +395,31 @@ __device__ __forceinline__ TileSrc tile_src(const Keys& s, int j, const uint16_t
   }
   return t;
 }
+// A buffer descriptor as four words in scalar registers (what make_rsrc builds:
+// base, stride 0, `bytes` bytes, 32-bit data format), for copies issued from
+// inline asm.
+__device__ __forceinline__ u32x4 desc_words(const void* base, int bytes) {
+  const uint64_t ad = (uint64_t)(uintptr_t)base;
+  u32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane((uint32_t)ad);
+  d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(ad >> 32) & 0xFFFFu);
+  d[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+  d[3] = 0x00020000u;
+  return d;
+}
+// Tile j's K (or V) rows as descriptor words (the buffer tile_src makes).
+__device__ __forceinline__ u32x4 tile_desc(const Keys& s, int j, const uint16_t* ent,
+                                           const uint16_t* raw) {
+  if (j < s.n_et) {
+    const int first = kTile * j;
+    const int rows = s.nc - first < kTile ? s.nc - first : kTile;
+    return desc_words(ent + (int64_t)first * kD, rows * 1024);
+  }
+  const int first = s.lo + kTile * (j - s.n_et);
+  const int rows = s.lo + s.nraw - first < kTile ? s.lo + s.nraw - first : kTile;
+  return desc_words(raw + (int64_t)first * kD, rows * 1024);
+}
+
 // Rows 8w .. 8w+7 of a 32-row tile (buffer r of 1 KiB rows; rows past its end
 // arrive as zeros) into LDS rows `stride` bytes apart: 8 DMA instructions.
 __device__ __forceinline__ void copy8(__amdgpu_buffer_rsrc_t r, int w, int lane16, uint8_t* st,
@@ -754,6 +779,465 @@ __device__ __forceinline__ void chains_keys(f32x4& s0, f32x4& s1, f32x4& d0, f32
       : "memory", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223");
 }
 
+// The same chains with 16 LDS-DMA copies of the next tile issued from inside the
+// asm, two after each group of MFMAs: an issuing copy stalls the wave while the
+// CU's memory path is busy, and copies issued back to back by all four waves
+// queue; spread out, the MFMAs already issued keep the pipe busy meanwhile.
+// Copy u (0 .. 15) reads 16 bytes per lane at vo + so[u % 8] of buffer rk (u <
+// 8) or rv (u >= 8) into LDS at m0 = mad[u] (plus 16 bytes per lane); m0 is
+// saved first and restored last (the compiler keeps it for its own copies).
+__device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16], const u32x4& rk, const u32x4& rv, uint32_t vo, const uint32_t (&so)[8], const uint32_t (&mad)[16]) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "ds_read_b128 v[128:131], %[a0] offset:0\n\t"
+      "ds_read_b128 v[132:135], %[a0] offset:64\n\t"
+      "ds_read_b128 v[136:139], %[a0] offset:128\n\t"
+      "ds_read_b128 v[140:143], %[a0] offset:192\n\t"
+      "ds_read_b128 v[144:147], %[a0] offset:256\n\t"
+      "ds_read_b128 v[148:151], %[a0] offset:320\n\t"
+      "ds_read_b128 v[152:155], %[a0] offset:384\n\t"
+      "ds_read_b128 v[156:159], %[a0] offset:448\n\t"
+      "ds_read_b128 v[160:163], %[a0] offset:512\n\t"
+      "ds_read_b128 v[164:167], %[a0] offset:576\n\t"
+      "ds_read_b128 v[168:171], %[a0] offset:640\n\t"
+      "ds_read_b128 v[172:175], %[a0] offset:704\n\t"
+      "ds_read_b128 v[176:179], %[a0] offset:768\n\t"
+      "ds_read_b128 v[180:183], %[a0] offset:832\n\t"
+      "ds_read_b128 v[184:187], %[a0] offset:896\n\t"
+      "ds_read_b128 v[188:191], %[a0] offset:960\n\t"
+      "s_waitcnt lgkmcnt(8)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[128:131], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[132:135], %[b1], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[136:139], %[b2], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[140:143], %[b3], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[144:147], %[b4], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[148:151], %[b5], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[152:155], %[b6], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[156:159], %[b7], %[s0]\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so0] offen lds\n\t"
+      "s_mov_b32 m0, %[m1]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so1] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[128:131], %[a1] offset:0\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:64\n\t"
+      "ds_read_b128 v[136:139], %[a1] offset:128\n\t"
+      "ds_read_b128 v[140:143], %[a1] offset:192\n\t"
+      "ds_read_b128 v[144:147], %[a1] offset:256\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:320\n\t"
+      "ds_read_b128 v[152:155], %[a1] offset:384\n\t"
+      "ds_read_b128 v[156:159], %[a1] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[160:163], %[b8], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[164:167], %[b9], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[168:171], %[b10], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[172:175], %[b11], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[176:179], %[b12], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[180:183], %[b13], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[184:187], %[b14], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[188:191], %[b15], %[s0]\n\t"
+      "s_mov_b32 m0, %[m2]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so2] offen lds\n\t"
+      "s_mov_b32 m0, %[m3]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so3] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[160:163], %[a1] offset:512\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:576\n\t"
+      "ds_read_b128 v[168:171], %[a1] offset:640\n\t"
+      "ds_read_b128 v[172:175], %[a1] offset:704\n\t"
+      "ds_read_b128 v[176:179], %[a1] offset:768\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:832\n\t"
+      "ds_read_b128 v[184:187], %[a1] offset:896\n\t"
+      "ds_read_b128 v[188:191], %[a1] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[128:131], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[132:135], %[b1], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[136:139], %[b2], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[140:143], %[b3], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[144:147], %[b4], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[148:151], %[b5], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[152:155], %[b6], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[156:159], %[b7], %[s1]\n\t"
+      "s_mov_b32 m0, %[m4]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so4] offen lds\n\t"
+      "s_mov_b32 m0, %[m5]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so5] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[128:131], %[a2] offset:0\n\t"
+      "ds_read_b128 v[132:135], %[a2] offset:64\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:128\n\t"
+      "ds_read_b128 v[140:143], %[a2] offset:192\n\t"
+      "ds_read_b128 v[144:147], %[a2] offset:256\n\t"
+      "ds_read_b128 v[148:151], %[a2] offset:320\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:384\n\t"
+      "ds_read_b128 v[156:159], %[a2] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[160:163], %[b8], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[164:167], %[b9], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[168:171], %[b10], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[172:175], %[b11], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[176:179], %[b12], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[180:183], %[b13], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[184:187], %[b14], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[188:191], %[b15], %[s1]\n\t"
+      "s_mov_b32 m0, %[m6]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so6] offen lds\n\t"
+      "s_mov_b32 m0, %[m7]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so7] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[160:163], %[a2] offset:512\n\t"
+      "ds_read_b128 v[164:167], %[a2] offset:576\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:640\n\t"
+      "ds_read_b128 v[172:175], %[a2] offset:704\n\t"
+      "ds_read_b128 v[176:179], %[a2] offset:768\n\t"
+      "ds_read_b128 v[180:183], %[a2] offset:832\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:896\n\t"
+      "ds_read_b128 v[188:191], %[a2] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[128:131], %[c0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[132:135], %[c1], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[136:139], %[c2], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[140:143], %[c3], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[144:147], %[c4], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[148:151], %[c5], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[152:155], %[c6], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[156:159], %[c7], %[d0]\n\t"
+      "s_mov_b32 m0, %[m8]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so0] offen lds\n\t"
+      "s_mov_b32 m0, %[m9]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so1] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[128:131], %[a3] offset:0\n\t"
+      "ds_read_b128 v[132:135], %[a3] offset:64\n\t"
+      "ds_read_b128 v[136:139], %[a3] offset:128\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:192\n\t"
+      "ds_read_b128 v[144:147], %[a3] offset:256\n\t"
+      "ds_read_b128 v[148:151], %[a3] offset:320\n\t"
+      "ds_read_b128 v[152:155], %[a3] offset:384\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[160:163], %[c8], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[164:167], %[c9], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[168:171], %[c10], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[172:175], %[c11], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[176:179], %[c12], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[180:183], %[c13], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[184:187], %[c14], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[188:191], %[c15], %[d0]\n\t"
+      "s_mov_b32 m0, %[m10]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so2] offen lds\n\t"
+      "s_mov_b32 m0, %[m11]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so3] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[160:163], %[a3] offset:512\n\t"
+      "ds_read_b128 v[164:167], %[a3] offset:576\n\t"
+      "ds_read_b128 v[168:171], %[a3] offset:640\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:704\n\t"
+      "ds_read_b128 v[176:179], %[a3] offset:768\n\t"
+      "ds_read_b128 v[180:183], %[a3] offset:832\n\t"
+      "ds_read_b128 v[184:187], %[a3] offset:896\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[128:131], %[c0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[132:135], %[c1], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[136:139], %[c2], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[140:143], %[c3], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[144:147], %[c4], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[148:151], %[c5], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[152:155], %[c6], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[156:159], %[c7], %[d1]\n\t"
+      "s_mov_b32 m0, %[m12]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so4] offen lds\n\t"
+      "s_mov_b32 m0, %[m13]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so5] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[160:163], %[c8], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[164:167], %[c9], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[168:171], %[c10], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[172:175], %[c11], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[176:179], %[c12], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[180:183], %[c13], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[184:187], %[c14], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[188:191], %[c15], %[d1]\n\t"
+      "s_mov_b32 m0, %[m14]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so6] offen lds\n\t"
+      "s_mov_b32 m0, %[m15]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so7] offen lds\n\t"
+      "s_nop 15\n\ts_nop 3\n\t"
+      "s_mov_b32 m0, %[m0s]"
+      : [m0s] "=&s"(m0_saved), [s0] "=&v"(s0), [s1] "=&v"(s1), [d0] "=&v"(d0), [d1] "=&v"(d1)
+      : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),
+        [b0] "a"(b[0]), [b1] "a"(b[1]), [b2] "a"(b[2]), [b3] "a"(b[3]),
+        [b4] "a"(b[4]), [b5] "a"(b[5]), [b6] "a"(b[6]), [b7] "a"(b[7]),
+        [b8] "a"(b[8]), [b9] "a"(b[9]), [b10] "a"(b[10]), [b11] "a"(b[11]),
+        [b12] "a"(b[12]), [b13] "a"(b[13]), [b14] "a"(b[14]), [b15] "a"(b[15]),
+        [c0] "a"(c[0]), [c1] "a"(c[1]), [c2] "a"(c[2]), [c3] "a"(c[3]),
+        [c4] "a"(c[4]), [c5] "a"(c[5]), [c6] "a"(c[6]), [c7] "a"(c[7]),
+        [c8] "a"(c[8]), [c9] "a"(c[9]), [c10] "a"(c[10]), [c11] "a"(c[11]),
+        [c12] "a"(c[12]), [c13] "a"(c[13]), [c14] "a"(c[14]), [c15] "a"(c[15]),
+        [rk] "s"(rk), [rv] "s"(rv), [vo] "v"(vo), [so0] "s"(so[0]),
+        [so1] "s"(so[1]), [so2] "s"(so[2]), [so3] "s"(so[3]), [so4] "s"(so[4]),
+        [so5] "s"(so[5]), [so6] "s"(so[6]), [so7] "s"(so[7]), [m0] "s"(mad[0]),
+        [m1] "s"(mad[1]), [m2] "s"(mad[2]), [m3] "s"(mad[3]), [m4] "s"(mad[4]),
+        [m5] "s"(mad[5]), [m6] "s"(mad[6]), [m7] "s"(mad[7]), [m8] "s"(mad[8]),
+        [m9] "s"(mad[9]), [m10] "s"(mad[10]), [m11] "s"(mad[11]), [m12] "s"(mad[12]),
+        [m13] "s"(mad[13]), [m14] "s"(mad[14]), [m15] "s"(mad[15])
+      : "memory", "v128", "v129", "v130", "v131", "v132", "v133", "v134", "v135", "v136", "v137", "v138", "v139", "v140", "v141", "v142", "v143", "v144", "v145", "v146", "v147", "v148", "v149", "v150", "v151", "v152", "v153", "v154", "v155", "v156", "v157", "v158", "v159", "v160", "v161", "v162", "v163", "v164", "v165", "v166", "v167", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191");
+}
+__device__ __forceinline__ void chains_keys_dma(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16], uint32_t sad, f32x4 (&st)[4], const u32x4& rk, const u32x4& rv, uint32_t vo, const uint32_t (&so)[8], const uint32_t (&mad)[16]) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %[m0s], m0\n\t"
+      "ds_read_b128 %[st0], %[sa] offset:0\n\t"
+      "ds_read_b128 %[st1], %[sa] offset:64\n\t"
+      "ds_read_b128 %[st2], %[sa] offset:128\n\t"
+      "ds_read_b128 %[st3], %[sa] offset:192\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:0\n\t"
+      "ds_read_b128 v[196:199], %[a0] offset:64\n\t"
+      "ds_read_b128 v[200:203], %[a0] offset:128\n\t"
+      "ds_read_b128 v[204:207], %[a0] offset:192\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:256\n\t"
+      "ds_read_b128 v[212:215], %[a0] offset:320\n\t"
+      "ds_read_b128 v[216:219], %[a0] offset:384\n\t"
+      "ds_read_b128 v[220:223], %[a0] offset:448\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[192:195], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[196:199], %[b1], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[200:203], %[b2], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[204:207], %[b3], %[s0]\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so0] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:512\n\t"
+      "ds_read_b128 v[196:199], %[a0] offset:576\n\t"
+      "ds_read_b128 v[200:203], %[a0] offset:640\n\t"
+      "ds_read_b128 v[204:207], %[a0] offset:704\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[208:211], %[b4], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[212:215], %[b5], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[216:219], %[b6], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[220:223], %[b7], %[s0]\n\t"
+      "s_mov_b32 m0, %[m1]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so1] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:768\n\t"
+      "ds_read_b128 v[212:215], %[a0] offset:832\n\t"
+      "ds_read_b128 v[216:219], %[a0] offset:896\n\t"
+      "ds_read_b128 v[220:223], %[a0] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[192:195], %[b8], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[196:199], %[b9], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[200:203], %[b10], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[204:207], %[b11], %[s0]\n\t"
+      "s_mov_b32 m0, %[m2]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so2] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a1] offset:0\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:64\n\t"
+      "ds_read_b128 v[200:203], %[a1] offset:128\n\t"
+      "ds_read_b128 v[204:207], %[a1] offset:192\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[208:211], %[b12], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[212:215], %[b13], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[216:219], %[b14], %[s0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s0], v[220:223], %[b15], %[s0]\n\t"
+      "s_mov_b32 m0, %[m3]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so3] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a1] offset:256\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:320\n\t"
+      "ds_read_b128 v[216:219], %[a1] offset:384\n\t"
+      "ds_read_b128 v[220:223], %[a1] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[192:195], %[b0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[196:199], %[b1], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[200:203], %[b2], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[204:207], %[b3], %[s1]\n\t"
+      "s_mov_b32 m0, %[m4]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so4] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a1] offset:512\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:576\n\t"
+      "ds_read_b128 v[200:203], %[a1] offset:640\n\t"
+      "ds_read_b128 v[204:207], %[a1] offset:704\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[208:211], %[b4], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[212:215], %[b5], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[216:219], %[b6], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[220:223], %[b7], %[s1]\n\t"
+      "s_mov_b32 m0, %[m5]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so5] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a1] offset:768\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:832\n\t"
+      "ds_read_b128 v[216:219], %[a1] offset:896\n\t"
+      "ds_read_b128 v[220:223], %[a1] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[192:195], %[b8], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[196:199], %[b9], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[200:203], %[b10], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[204:207], %[b11], %[s1]\n\t"
+      "s_mov_b32 m0, %[m6]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so6] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a2] offset:0\n\t"
+      "ds_read_b128 v[196:199], %[a2] offset:64\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:128\n\t"
+      "ds_read_b128 v[204:207], %[a2] offset:192\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[208:211], %[b12], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[212:215], %[b13], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[216:219], %[b14], %[s1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[s1], v[220:223], %[b15], %[s1]\n\t"
+      "s_mov_b32 m0, %[m7]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rk], %[so7] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a2] offset:256\n\t"
+      "ds_read_b128 v[212:215], %[a2] offset:320\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:384\n\t"
+      "ds_read_b128 v[220:223], %[a2] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[192:195], %[c0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[196:199], %[c1], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[200:203], %[c2], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[204:207], %[c3], %[d0]\n\t"
+      "s_mov_b32 m0, %[m8]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so0] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a2] offset:512\n\t"
+      "ds_read_b128 v[196:199], %[a2] offset:576\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:640\n\t"
+      "ds_read_b128 v[204:207], %[a2] offset:704\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[208:211], %[c4], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[212:215], %[c5], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[216:219], %[c6], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[220:223], %[c7], %[d0]\n\t"
+      "s_mov_b32 m0, %[m9]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so1] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a2] offset:768\n\t"
+      "ds_read_b128 v[212:215], %[a2] offset:832\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:896\n\t"
+      "ds_read_b128 v[220:223], %[a2] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[192:195], %[c8], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[196:199], %[c9], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[200:203], %[c10], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[204:207], %[c11], %[d0]\n\t"
+      "s_mov_b32 m0, %[m10]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so2] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a3] offset:0\n\t"
+      "ds_read_b128 v[196:199], %[a3] offset:64\n\t"
+      "ds_read_b128 v[200:203], %[a3] offset:128\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:192\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[208:211], %[c12], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[212:215], %[c13], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[216:219], %[c14], %[d0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d0], v[220:223], %[c15], %[d0]\n\t"
+      "s_mov_b32 m0, %[m11]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so3] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a3] offset:256\n\t"
+      "ds_read_b128 v[212:215], %[a3] offset:320\n\t"
+      "ds_read_b128 v[216:219], %[a3] offset:384\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:448\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[192:195], %[c0], 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[196:199], %[c1], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[200:203], %[c2], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[204:207], %[c3], %[d1]\n\t"
+      "s_mov_b32 m0, %[m12]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so4] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[192:195], %[a3] offset:512\n\t"
+      "ds_read_b128 v[196:199], %[a3] offset:576\n\t"
+      "ds_read_b128 v[200:203], %[a3] offset:640\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:704\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[208:211], %[c4], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[212:215], %[c5], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[216:219], %[c6], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[220:223], %[c7], %[d1]\n\t"
+      "s_mov_b32 m0, %[m13]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so5] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b128 v[208:211], %[a3] offset:768\n\t"
+      "ds_read_b128 v[212:215], %[a3] offset:832\n\t"
+      "ds_read_b128 v[216:219], %[a3] offset:896\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:960\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[192:195], %[c8], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[196:199], %[c9], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[200:203], %[c10], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[204:207], %[c11], %[d1]\n\t"
+      "s_mov_b32 m0, %[m14]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so6] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[208:211], %[c12], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[212:215], %[c13], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[216:219], %[c14], %[d1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[d1], v[220:223], %[c15], %[d1]\n\t"
+      "s_mov_b32 m0, %[m15]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rv], %[so7] offen lds\n\t"
+      "s_nop 15\n\ts_nop 3\n\t"
+      "s_mov_b32 m0, %[m0s]"
+      : [m0s] "=&s"(m0_saved), [s0] "=&v"(s0), [s1] "=&v"(s1), [d0] "=&v"(d0), [d1] "=&v"(d1),
+        [st0] "=&v"(st[0]), [st1] "=&v"(st[1]), [st2] "=&v"(st[2]), [st3] "=&v"(st[3])
+      : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),
+        [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
+        [b4] "v"(b[4]), [b5] "v"(b[5]), [b6] "v"(b[6]), [b7] "v"(b[7]),
+        [b8] "v"(b[8]), [b9] "v"(b[9]), [b10] "v"(b[10]), [b11] "v"(b[11]),
+        [b12] "v"(b[12]), [b13] "v"(b[13]), [b14] "v"(b[14]), [b15] "v"(b[15]),
+        [c0] "v"(c[0]), [c1] "v"(c[1]), [c2] "v"(c[2]), [c3] "v"(c[3]),
+        [c4] "v"(c[4]), [c5] "v"(c[5]), [c6] "v"(c[6]), [c7] "v"(c[7]),
+        [c8] "v"(c[8]), [c9] "v"(c[9]), [c10] "v"(c[10]), [c11] "v"(c[11]),
+        [c12] "v"(c[12]), [c13] "v"(c[13]), [c14] "v"(c[14]), [c15] "v"(c[15]),
+        [sa] "v"(sad), [rk] "s"(rk), [rv] "s"(rv), [vo] "v"(vo),
+        [so0] "s"(so[0]), [so1] "s"(so[1]), [so2] "s"(so[2]), [so3] "s"(so[3]),
+        [so4] "s"(so[4]), [so5] "s"(so[5]), [so6] "s"(so[6]), [so7] "s"(so[7]),
+        [m0] "s"(mad[0]), [m1] "s"(mad[1]), [m2] "s"(mad[2]), [m3] "s"(mad[3]),
+        [m4] "s"(mad[4]), [m5] "s"(mad[5]), [m6] "s"(mad[6]), [m7] "s"(mad[7]),
+        [m8] "s"(mad[8]), [m9] "s"(mad[9]), [m10] "s"(mad[10]), [m11] "s"(mad[11]),
+        [m12] "s"(mad[12]), [m13] "s"(mad[13]), [m14] "s"(mad[14]), [m15] "s"(mad[15])
+      : "memory", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)p;
 }
@@ -830,6 +1314,17 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   };
   const int voff = (4 * g4 + (l16 >> 2)) * kRowT + 8 * (l16 & 3);  // transposing reads
   const int foffF = l16 * kRowF + 16 * g4, foffT = l16 * kRowT + 16 * g4;
+  // Copies of this wave's rows 8W .. 8W+7 of a tile: buffer offsets and LDS rows.
+  uint32_t soff[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) soff[u] = (uint32_t)((8 * W + u) * 1024);
+  auto next_rows = [&](int j, int kstride, int vstride, uint32_t (&mad)[16]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      mad[u] = __builtin_amdgcn_readfirstlane(lds_addr(kst(j) + (8 * W + u) * kstride));
+      mad[8 + u] = __builtin_amdgcn_readfirstlane(lds_addr(kst(j) + kStage + (8 * W + u) * vstride));
+    }
+  };
 
   // ---- pass A: per row the maximum (fixed reference m), the weights
   // e_j = 2^(x_j - m) and, with them,
@@ -857,10 +1352,13 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
       f32x4 sc[2], dp[2];  // S^T = K Q^T, dP^T = V dA^T
       const uint32_t ad[4] = {lds_addr(sk + foffF), lds_addr(sk + 16 * kRowF + foffF),
                               lds_addr(sk + kStage + foffT), lds_addr(sk + kStage + 16 * kRowT + foffT)};
-      chains_rows(sc[0], sc[1], dp[0], dp[1], ad, qf, daf);
       if (j + 1 < nt) {
-        issue_k(j + 1, kRowF);
-        issue_v(j + 1, kRowT);
+        uint32_t mad[16];
+        next_rows(j + 1, kRowF, kRowT, mad);
+        chains_rows_dma(sc[0], sc[1], dp[0], dp[1], ad, qf, daf, tile_desc(s, j + 1, a.ck, a.k),
+                        tile_desc(s, j + 1, a.cv, a.v), (uint32_t)lane16, soff, mad);
+      } else {
+        chains_rows(sc[0], sc[1], dp[0], dp[1], ad, qf, daf);
       }
       int lo_v, hi_v;
       vis(j, lo_v, hi_v);
@@ -936,10 +1434,13 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     f32x4 sc[2], dp[2];
     const uint32_t ad[4] = {lds_addr(sk + foffT), lds_addr(sk + 16 * kRowT + foffT),
                             lds_addr(sk + kStage + foffF), lds_addr(sk + kStage + 16 * kRowF + foffF)};
-    chains_rows(sc[0], sc[1], dp[0], dp[1], ad, qf, daf);
     if (j + 1 < nt) {
-      issue_k(j + 1, kRowT);
-      issue_v(j + 1, kRowF);
+      uint32_t mad[16];
+      next_rows(j + 1, kRowT, kRowF, mad);
+      chains_rows_dma(sc[0], sc[1], dp[0], dp[1], ad, qf, daf, tile_desc(s, j + 1, a.ck, a.k),
+                      tile_desc(s, j + 1, a.cv, a.v), (uint32_t)lane16, soff, mad);
+    } else {
+      chains_rows(sc[0], sc[1], dp[0], dp[1], ad, qf, daf);
     }
     int lo_v, hi_v;
     vis(j, lo_v, hi_v);
@@ -1041,6 +1542,9 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
   };
   const int voff = (4 * g4 + (l16 >> 2)) * kRowT + 8 * (l16 & 3);
   const int foff = l16 * kRowT + 16 * g4;
+  uint32_t soff[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) soff[u] = (uint32_t)((8 * W + u) * 1024);
   issue_q(0);
   issue_a(0);
   for (int i = 0; i < nb; ++i) {
@@ -1053,10 +1557,28 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
     f32x4 sc[2], dp[2], stt[4];
     const uint32_t ad[4] = {lds_addr(sp + foff), lds_addr(sp + 16 * kRowT + foff),
                             lds_addr(sp + kStage + foff), lds_addr(sp + kStage + 16 * kRowT + foff)};
-    chains_keys(sc[0], sc[1], dp[0], dp[1], ad, kf, vf, lds_addr(sp + 2 * kStage + 16 * g4), stt);
     if (i + 1 < nb) {
-      issue_q(i + 1);
-      issue_a(i + 1);
+      // block i+1's statistics (2 copies, lanes 0 and 1), then its Q and dA rows
+      // from inside the chains
+      const int64_t n0 = (rb0 + i + 1) * kTile;
+      const int nr = nrows - n0 < kTile ? (int)(nrows - n0) : kTile;
+      uint8_t* const sq = st(i + 1);
+      if (lane < 2) {
+        dma16_buf(make_rsrc(a.lse + n0, nr * 4), 32 * W + lane16, (lds_void*)(sq + 2 * kStage + 32 * W));
+        dma16_buf(make_rsrc(a.dt + n0, nr * 4), 32 * W + lane16,
+                  (lds_void*)(sq + 2 * kStage + 128 + 32 * W));
+      }
+      uint32_t mad[16];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        mad[u] = __builtin_amdgcn_readfirstlane(lds_addr(sq + (8 * W + u) * kRowT));
+        mad[8 + u] = __builtin_amdgcn_readfirstlane(lds_addr(sq + kStage + (8 * W + u) * kRowT));
+      }
+      chains_keys_dma(sc[0], sc[1], dp[0], dp[1], ad, kf, vf, lds_addr(sp + 2 * kStage + 16 * g4),
+                      stt, desc_words(a.q + n0 * kD, nr * 1024), desc_words(a.da + n0 * kD, nr * 1024),
+                      (uint32_t)lane16, soff, mad);
+    } else {
+      chains_keys(sc[0], sc[1], dp[0], dp[1], ad, kf, vf, lds_addr(sp + 2 * kStage + 16 * g4), stt);
     }
     bf16x8 pb, dsb;
 #pragma unroll
