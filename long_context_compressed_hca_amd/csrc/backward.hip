@@ -44,12 +44,16 @@ namespace hca {
 namespace {
 
 constexpr int kTile = 32;                // keys per tile (rows kernel), rows per block (keys kernel)
-// LDS row strides: rows that are also read with transposing reads sit 1024 +
-// 64 bytes apart (4 consecutive rows cover the banks once), rows read only as
-// b128 fragments 1024 + 16 apart (8 consecutive rows cover them once).
-constexpr int kRowT = 1024 + 64;
-constexpr int kRowF = 1024 + 16;
-constexpr int kStage = kTile * kRowT;    // one 32-row tile at either stride: 34816 bytes
+// LDS tile layout: row r at r * kRow, its 16-byte chunk c at chunk c ^ (r & 15)
+// of the row.  Both read patterns then touch every bank once per phase: the
+// b128 fragment reads (16 lanes: 16 rows, one chunk column each) and the
+// transposing reads (32 lanes: 8 rows x 4 eight-byte pieces).  Every read
+// address is one of a few per-lane bases plus an immediate offset.
+constexpr int kRow = 1024 + 128;
+constexpr int kStage = kTile * kRow;     // one 32-row tile: 36864 bytes
+constexpr int kHalf = 16 * kRow;         // rows 16 .. 31 of a tile
+// the asm helpers below carry these offsets as immediates
+static_assert(kHalf == 18432 && kStage == 36864, "asm read offsets");
 constexpr float kHeadroom = 64.0f;
 constexpr int kRowsPerWg = 64;
 constexpr int kKeysPerWg = 64;
@@ -104,53 +108,54 @@ __device__ __forceinline__ void wait_vm() {
 // VALU read of accumulators written by the last MFMAs needs.
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15"); }
 
-// O^T[512 dims x 16] += M^T P over a 32-row LDS tile M (rows kRowT apart),
-// with 16x16x32 MFMAs (full rate; the 16x16x16 form costs about as many cycles
-// for half the work).  The contraction index of lane group g4 is the 8 rows
-// {4 g4 .. 4 g4 + 3, 16 + 4 g4 .. 16 + 4 g4 + 3}: the A operand M^T comes from
-// two transposing reads, at ad (rows 4 g4 ..) and ad2 = ad + 16 rows, into the
-// two halves of one 4-register group, and P (B operand, 8 bf16 per lane) holds
-// the same rows in that order.  The groups are fixed registers (clobbered:
+// O^T[512 dims x 16] += M^T P over a 32-row LDS tile M, with 16x16x32 MFMAs
+// (full rate; the 16x16x16 form costs about as many cycles for half the work).
+// The contraction index of lane group g4 is the 8 rows {4 g4 .. 4 g4 + 3,
+// 16 + 4 g4 .. 16 + 4 g4 + 3}: the A operand M^T comes from two transposing
+// reads, of rows 4 g4 .. and of the same rows + 16, into the two halves of one
+// 4-register group, and P (B operand, 8 bf16 per lane) holds
+// the same rows in that order.  Dim block db = 8 a + b is read at ta[b] + 256 a
+// (and + kHalf for rows 16 ..).  The groups are fixed registers (clobbered:
 // inline asm cannot name the halves of an operand) used as a ring: the reads of
 // one half of the ring are in flight while the other half's MFMAs issue, and a
 // group is refilled only after the MFMA reading it has issued and the reads in
 // between have been waited for.  Accumulators in AGPRs.  tr_rows: a ring of 16
 // groups in v192 .. v255; tr_keys: 8 groups in v224 .. v255 (the key kernel
 // keeps its K and V fragments in VGPRs).
-__device__ __forceinline__ void tr_rows(f32x4 (&o)[32], uint32_t ad, uint32_t ad2, const bf16x8& p) {
+__device__ __forceinline__ void tr_rows(f32x4 (&o)[32], const uint32_t (&ta)[8], const bf16x8& p) {
   asm volatile(
-      "ds_read_b64_tr_b16 v[192:193], %[ad] offset:0\n\t"
-      "ds_read_b64_tr_b16 v[194:195], %[ad2] offset:0\n\t"
-      "ds_read_b64_tr_b16 v[196:197], %[ad] offset:32\n\t"
-      "ds_read_b64_tr_b16 v[198:199], %[ad2] offset:32\n\t"
-      "ds_read_b64_tr_b16 v[200:201], %[ad] offset:64\n\t"
-      "ds_read_b64_tr_b16 v[202:203], %[ad2] offset:64\n\t"
-      "ds_read_b64_tr_b16 v[204:205], %[ad] offset:96\n\t"
-      "ds_read_b64_tr_b16 v[206:207], %[ad2] offset:96\n\t"
-      "ds_read_b64_tr_b16 v[208:209], %[ad] offset:128\n\t"
-      "ds_read_b64_tr_b16 v[210:211], %[ad2] offset:128\n\t"
-      "ds_read_b64_tr_b16 v[212:213], %[ad] offset:160\n\t"
-      "ds_read_b64_tr_b16 v[214:215], %[ad2] offset:160\n\t"
-      "ds_read_b64_tr_b16 v[216:217], %[ad] offset:192\n\t"
-      "ds_read_b64_tr_b16 v[218:219], %[ad2] offset:192\n\t"
-      "ds_read_b64_tr_b16 v[220:221], %[ad] offset:224\n\t"
-      "ds_read_b64_tr_b16 v[222:223], %[ad2] offset:224\n\t"
-      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:256\n\t"
-      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:256\n\t"
-      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:288\n\t"
-      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:288\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:320\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:320\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:352\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:352\n\t"
-      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:384\n\t"
-      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:384\n\t"
-      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:416\n\t"
-      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:416\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:448\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:448\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:480\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:480\n\t"
+      "ds_read_b64_tr_b16 v[192:193], %[t0] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[194:195], %[t0] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[196:197], %[t1] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[198:199], %[t1] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[200:201], %[t2] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[202:203], %[t2] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[204:205], %[t3] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[206:207], %[t3] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[208:209], %[t4] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[210:211], %[t4] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[212:213], %[t5] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[214:215], %[t5] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[216:217], %[t6] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[218:219], %[t6] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[220:221], %[t7] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[222:223], %[t7] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:18688\n\t"
       "s_waitcnt lgkmcnt(15)\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o0], v[192:195], %[p], %[o0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o1], v[196:199], %[p], %[o1]\n\t"
@@ -162,22 +167,22 @@ __device__ __forceinline__ void tr_rows(f32x4 (&o)[32], uint32_t ad, uint32_t ad
       "v_mfma_f32_16x16x32_bf16 %[o7], v[220:223], %[p], %[o7]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b64_tr_b16 v[192:193], %[ad] offset:512\n\t"
-      "ds_read_b64_tr_b16 v[194:195], %[ad2] offset:512\n\t"
-      "ds_read_b64_tr_b16 v[196:197], %[ad] offset:544\n\t"
-      "ds_read_b64_tr_b16 v[198:199], %[ad2] offset:544\n\t"
-      "ds_read_b64_tr_b16 v[200:201], %[ad] offset:576\n\t"
-      "ds_read_b64_tr_b16 v[202:203], %[ad2] offset:576\n\t"
-      "ds_read_b64_tr_b16 v[204:205], %[ad] offset:608\n\t"
-      "ds_read_b64_tr_b16 v[206:207], %[ad2] offset:608\n\t"
-      "ds_read_b64_tr_b16 v[208:209], %[ad] offset:640\n\t"
-      "ds_read_b64_tr_b16 v[210:211], %[ad2] offset:640\n\t"
-      "ds_read_b64_tr_b16 v[212:213], %[ad] offset:672\n\t"
-      "ds_read_b64_tr_b16 v[214:215], %[ad2] offset:672\n\t"
-      "ds_read_b64_tr_b16 v[216:217], %[ad] offset:704\n\t"
-      "ds_read_b64_tr_b16 v[218:219], %[ad2] offset:704\n\t"
-      "ds_read_b64_tr_b16 v[220:221], %[ad] offset:736\n\t"
-      "ds_read_b64_tr_b16 v[222:223], %[ad2] offset:736\n\t"
+      "ds_read_b64_tr_b16 v[192:193], %[t0] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[194:195], %[t0] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[196:197], %[t1] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[198:199], %[t1] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[200:201], %[t2] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[202:203], %[t2] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[204:205], %[t3] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[206:207], %[t3] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[208:209], %[t4] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[210:211], %[t4] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[212:213], %[t5] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[214:215], %[t5] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[216:217], %[t6] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[218:219], %[t6] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[220:221], %[t7] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[222:223], %[t7] offset:18944\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o8], v[224:227], %[p], %[o8]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o9], v[228:231], %[p], %[o9]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o10], v[232:235], %[p], %[o10]\n\t"
@@ -188,22 +193,22 @@ __device__ __forceinline__ void tr_rows(f32x4 (&o)[32], uint32_t ad, uint32_t ad
       "v_mfma_f32_16x16x32_bf16 %[o15], v[252:255], %[p], %[o15]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:768\n\t"
-      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:768\n\t"
-      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:800\n\t"
-      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:800\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:832\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:832\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:864\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:864\n\t"
-      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:896\n\t"
-      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:896\n\t"
-      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:928\n\t"
-      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:928\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:960\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:960\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:992\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:992\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:19200\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o16], v[192:195], %[p], %[o16]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o17], v[196:199], %[p], %[o17]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o18], v[200:203], %[p], %[o18]\n\t"
@@ -229,27 +234,29 @@ __device__ __forceinline__ void tr_rows(f32x4 (&o)[32], uint32_t ad, uint32_t ad
         [o20] "+a"(o[20]), [o21] "+a"(o[21]), [o22] "+a"(o[22]), [o23] "+a"(o[23]),
         [o24] "+a"(o[24]), [o25] "+a"(o[25]), [o26] "+a"(o[26]), [o27] "+a"(o[27]),
         [o28] "+a"(o[28]), [o29] "+a"(o[29]), [o30] "+a"(o[30]), [o31] "+a"(o[31])
-      : [ad] "v"(ad), [ad2] "v"(ad2), [p] "v"(p)
+      : [t0] "v"(ta[0]), [t1] "v"(ta[1]), [t2] "v"(ta[2]), [t3] "v"(ta[3]),
+        [t4] "v"(ta[4]), [t5] "v"(ta[5]), [t6] "v"(ta[6]), [t7] "v"(ta[7]),
+        [p] "v"(p)
       : "memory", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
 }
-__device__ __forceinline__ void tr_keys(f32x4 (&o)[32], uint32_t ad, uint32_t ad2, const bf16x8& p) {
+__device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8], const bf16x8& p) {
   asm volatile(
-      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:0\n\t"
-      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:0\n\t"
-      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:32\n\t"
-      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:32\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:64\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:64\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:96\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:96\n\t"
-      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:128\n\t"
-      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:128\n\t"
-      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:160\n\t"
-      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:160\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:192\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:192\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:224\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:224\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:18432\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:18432\n\t"
       "s_waitcnt lgkmcnt(8)\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o0], v[224:227], %[p], %[o0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o1], v[228:231], %[p], %[o1]\n\t"
@@ -257,84 +264,84 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], uint32_t ad, uint32_t ad
       "v_mfma_f32_16x16x32_bf16 %[o3], v[236:239], %[p], %[o3]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:256\n\t"
-      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:256\n\t"
-      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:288\n\t"
-      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:288\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:320\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:320\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:352\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:352\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:18688\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o4], v[240:243], %[p], %[o4]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o5], v[244:247], %[p], %[o5]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o6], v[248:251], %[p], %[o6]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o7], v[252:255], %[p], %[o7]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:384\n\t"
-      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:384\n\t"
-      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:416\n\t"
-      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:416\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:448\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:448\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:480\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:480\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:18688\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:18688\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o8], v[224:227], %[p], %[o8]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o9], v[228:231], %[p], %[o9]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o10], v[232:235], %[p], %[o10]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o11], v[236:239], %[p], %[o11]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:512\n\t"
-      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:512\n\t"
-      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:544\n\t"
-      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:544\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:576\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:576\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:608\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:608\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:18944\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o12], v[240:243], %[p], %[o12]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o13], v[244:247], %[p], %[o13]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o14], v[248:251], %[p], %[o14]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o15], v[252:255], %[p], %[o15]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:640\n\t"
-      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:640\n\t"
-      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:672\n\t"
-      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:672\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:704\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:704\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:736\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:736\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:18944\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:18944\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o16], v[224:227], %[p], %[o16]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o17], v[228:231], %[p], %[o17]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o18], v[232:235], %[p], %[o18]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o19], v[236:239], %[p], %[o19]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b64_tr_b16 v[224:225], %[ad] offset:768\n\t"
-      "ds_read_b64_tr_b16 v[226:227], %[ad2] offset:768\n\t"
-      "ds_read_b64_tr_b16 v[228:229], %[ad] offset:800\n\t"
-      "ds_read_b64_tr_b16 v[230:231], %[ad2] offset:800\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[ad] offset:832\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[ad2] offset:832\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[ad] offset:864\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[ad2] offset:864\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:19200\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o20], v[240:243], %[p], %[o20]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o21], v[244:247], %[p], %[o21]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o22], v[248:251], %[p], %[o22]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o23], v[252:255], %[p], %[o23]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b64_tr_b16 v[240:241], %[ad] offset:896\n\t"
-      "ds_read_b64_tr_b16 v[242:243], %[ad2] offset:896\n\t"
-      "ds_read_b64_tr_b16 v[244:245], %[ad] offset:928\n\t"
-      "ds_read_b64_tr_b16 v[246:247], %[ad2] offset:928\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[ad] offset:960\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[ad2] offset:960\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[ad] offset:992\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[ad2] offset:992\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:19200\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:19200\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o24], v[224:227], %[p], %[o24]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o25], v[228:231], %[p], %[o25]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[o26], v[232:235], %[p], %[o26]\n\t"
@@ -352,7 +359,9 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], uint32_t ad, uint32_t ad
         [o20] "+a"(o[20]), [o21] "+a"(o[21]), [o22] "+a"(o[22]), [o23] "+a"(o[23]),
         [o24] "+a"(o[24]), [o25] "+a"(o[25]), [o26] "+a"(o[26]), [o27] "+a"(o[27]),
         [o28] "+a"(o[28]), [o29] "+a"(o[29]), [o30] "+a"(o[30]), [o31] "+a"(o[31])
-      : [ad] "v"(ad), [ad2] "v"(ad2), [p] "v"(p)
+      : [t0] "v"(ta[0]), [t1] "v"(ta[1]), [t2] "v"(ta[2]), [t3] "v"(ta[3]),
+        [t4] "v"(ta[4]), [t5] "v"(ta[5]), [t6] "v"(ta[6]), [t7] "v"(ta[7]),
+        [p] "v"(p)
       : "memory", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
 }
 
@@ -421,20 +430,39 @@ __device__ __forceinline__ u32x4 tile_desc(const Keys& s, int j, const uint16_t*
 }
 
 // Rows 8w .. 8w+7 of a 32-row tile (buffer r of 1 KiB rows; rows past its end
-// arrive as zeros) into LDS rows `stride` bytes apart: 8 DMA instructions.
-__device__ __forceinline__ void copy8(__amdgpu_buffer_rsrc_t r, int w, int lane16, uint8_t* st,
-                                      int stride) {
+// arrive as zeros) into the tile at st: 8 DMA instructions.  A copy writes 16
+// bytes per lane to consecutive LDS chunks, so lane L of row rr fetches the
+// row's chunk L ^ (rr & 15) (byte offset vo[u] = 16 (L ^ (rr & 15))).
+__device__ __forceinline__ void copy8(__amdgpu_buffer_rsrc_t r, int w, const uint32_t (&vo)[8],
+                                      uint8_t* st) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int rr = 8 * w + u;
-    dma16_buf(r, rr * 1024 + lane16, (lds_void*)(st + rr * stride));
+    dma16_buf(r, rr * 1024 + (int)vo[u], (lds_void*)(st + rr * kRow));
   }
 }
 
-// Four score-shaped chains over a 32-row tile pair in LDS:
+// Per-lane read bases within a tile (lane (l16, g4)):
+//   fragment reads, 16 bytes of row x = l16 at byte 64 ss + 16 g4, ss = 4 a + b:
+//     cb[b] + 256 a (+ kHalf for row 16 + x, + kStage for the stage's second tile);
+//   transposing reads, 8 bytes of row y = 4 g4 + (l16 >> 2) at byte
+//     32 db + 8 (l16 & 3), db = 8 a + b: tb[b] + 256 a (+ kHalf for row y + 16).
+__device__ __forceinline__ void read_bases(int l16, int g4, uint32_t (&cb)[4], uint32_t (&tb)[8]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    cb[b] = (uint32_t)(l16 * kRow + 16 * (g4 ^ (l16 & 3)) + 64 * (b ^ (l16 >> 2)));
+  const int y = 4 * g4 + (l16 >> 2), h = (l16 >> 1) & 1;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) tb[b] = (uint32_t)(y * kRow + 16 * ((2 * b + h) ^ y) + 8 * (l16 & 1));
+}
+
+// Four score-shaped chains over the two 32-row tiles of a stage in LDS:
 //   s0, s1 = sum_ss X_c[ss] b[ss] (c = 0, 1),  d0, d1 = sum_ss X_c[ss] c[ss] (c = 2, 3)
-// (16 MFMA 16x16x32 each) with the A operands read from LDS (lane (l16, g4): 16
-// bytes at ad[c] + 64 ss) and b, c in registers.  One asm block issues the 64
+// (16 MFMA 16x16x32 each), X_0, X_1 rows 0 .. 15 and 16 .. 31 of the first
+// tile, X_2, X_3 those of the second, with the A operands read from LDS (lane
+// (l16, g4), fragment ss = 4 a + b: 16 bytes at ad[b] + 256 a + 0, kHalf,
+// kStage, kStage + kHalf for c = 0 .. 3; ad = the stage + cb) and b, c in
+// registers.  One asm block issues the 64
 // reads through a ring of fixed registers, the reads of one group in flight
 // while the previous group's MFMAs issue, and waits for everything it reads
 // (the compiler does not see these LDS reads, so it inserts no wait for DMA
@@ -445,21 +473,21 @@ __device__ __forceinline__ void copy8(__amdgpu_buffer_rsrc_t r, int w, int lane1
 __device__ __forceinline__ void chains_rows(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16]) {
   asm volatile(
       "ds_read_b128 v[128:131], %[a0] offset:0\n\t"
-      "ds_read_b128 v[132:135], %[a0] offset:64\n\t"
-      "ds_read_b128 v[136:139], %[a0] offset:128\n\t"
-      "ds_read_b128 v[140:143], %[a0] offset:192\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:0\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:0\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:0\n\t"
       "ds_read_b128 v[144:147], %[a0] offset:256\n\t"
-      "ds_read_b128 v[148:151], %[a0] offset:320\n\t"
-      "ds_read_b128 v[152:155], %[a0] offset:384\n\t"
-      "ds_read_b128 v[156:159], %[a0] offset:448\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:256\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:256\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:256\n\t"
       "ds_read_b128 v[160:163], %[a0] offset:512\n\t"
-      "ds_read_b128 v[164:167], %[a0] offset:576\n\t"
-      "ds_read_b128 v[168:171], %[a0] offset:640\n\t"
-      "ds_read_b128 v[172:175], %[a0] offset:704\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:512\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:512\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:512\n\t"
       "ds_read_b128 v[176:179], %[a0] offset:768\n\t"
-      "ds_read_b128 v[180:183], %[a0] offset:832\n\t"
-      "ds_read_b128 v[184:187], %[a0] offset:896\n\t"
-      "ds_read_b128 v[188:191], %[a0] offset:960\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:768\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:768\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:768\n\t"
       "s_waitcnt lgkmcnt(8)\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[128:131], %[b0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[132:135], %[b1], %[s0]\n\t"
@@ -471,14 +499,14 @@ __device__ __forceinline__ void chains_rows(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "v_mfma_f32_16x16x32_bf16 %[s0], v[156:159], %[b7], %[s0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[128:131], %[a1] offset:0\n\t"
-      "ds_read_b128 v[132:135], %[a1] offset:64\n\t"
-      "ds_read_b128 v[136:139], %[a1] offset:128\n\t"
-      "ds_read_b128 v[140:143], %[a1] offset:192\n\t"
-      "ds_read_b128 v[144:147], %[a1] offset:256\n\t"
-      "ds_read_b128 v[148:151], %[a1] offset:320\n\t"
-      "ds_read_b128 v[152:155], %[a1] offset:384\n\t"
-      "ds_read_b128 v[156:159], %[a1] offset:448\n\t"
+      "ds_read_b128 v[128:131], %[a0] offset:18432\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:18432\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:18432\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:18432\n\t"
+      "ds_read_b128 v[144:147], %[a0] offset:18688\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:18688\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:18688\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:18688\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[160:163], %[b8], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[164:167], %[b9], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[168:171], %[b10], %[s0]\n\t"
@@ -489,14 +517,14 @@ __device__ __forceinline__ void chains_rows(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "v_mfma_f32_16x16x32_bf16 %[s0], v[188:191], %[b15], %[s0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[160:163], %[a1] offset:512\n\t"
-      "ds_read_b128 v[164:167], %[a1] offset:576\n\t"
-      "ds_read_b128 v[168:171], %[a1] offset:640\n\t"
-      "ds_read_b128 v[172:175], %[a1] offset:704\n\t"
-      "ds_read_b128 v[176:179], %[a1] offset:768\n\t"
-      "ds_read_b128 v[180:183], %[a1] offset:832\n\t"
-      "ds_read_b128 v[184:187], %[a1] offset:896\n\t"
-      "ds_read_b128 v[188:191], %[a1] offset:960\n\t"
+      "ds_read_b128 v[160:163], %[a0] offset:18944\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:18944\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:18944\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:18944\n\t"
+      "ds_read_b128 v[176:179], %[a0] offset:19200\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:19200\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:19200\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:19200\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[128:131], %[b0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[132:135], %[b1], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[136:139], %[b2], %[s1]\n\t"
@@ -507,14 +535,14 @@ __device__ __forceinline__ void chains_rows(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "v_mfma_f32_16x16x32_bf16 %[s1], v[156:159], %[b7], %[s1]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[128:131], %[a2] offset:0\n\t"
-      "ds_read_b128 v[132:135], %[a2] offset:64\n\t"
-      "ds_read_b128 v[136:139], %[a2] offset:128\n\t"
-      "ds_read_b128 v[140:143], %[a2] offset:192\n\t"
-      "ds_read_b128 v[144:147], %[a2] offset:256\n\t"
-      "ds_read_b128 v[148:151], %[a2] offset:320\n\t"
-      "ds_read_b128 v[152:155], %[a2] offset:384\n\t"
-      "ds_read_b128 v[156:159], %[a2] offset:448\n\t"
+      "ds_read_b128 v[128:131], %[a0] offset:36864\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:36864\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:36864\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:36864\n\t"
+      "ds_read_b128 v[144:147], %[a0] offset:37120\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:37120\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:37120\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:37120\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[160:163], %[b8], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[164:167], %[b9], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[168:171], %[b10], %[s1]\n\t"
@@ -525,14 +553,14 @@ __device__ __forceinline__ void chains_rows(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "v_mfma_f32_16x16x32_bf16 %[s1], v[188:191], %[b15], %[s1]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[160:163], %[a2] offset:512\n\t"
-      "ds_read_b128 v[164:167], %[a2] offset:576\n\t"
-      "ds_read_b128 v[168:171], %[a2] offset:640\n\t"
-      "ds_read_b128 v[172:175], %[a2] offset:704\n\t"
-      "ds_read_b128 v[176:179], %[a2] offset:768\n\t"
-      "ds_read_b128 v[180:183], %[a2] offset:832\n\t"
-      "ds_read_b128 v[184:187], %[a2] offset:896\n\t"
-      "ds_read_b128 v[188:191], %[a2] offset:960\n\t"
+      "ds_read_b128 v[160:163], %[a0] offset:37376\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:37376\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:37376\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:37376\n\t"
+      "ds_read_b128 v[176:179], %[a0] offset:37632\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:37632\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:37632\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:37632\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[128:131], %[c0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[132:135], %[c1], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[136:139], %[c2], %[d0]\n\t"
@@ -543,14 +571,14 @@ __device__ __forceinline__ void chains_rows(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "v_mfma_f32_16x16x32_bf16 %[d0], v[156:159], %[c7], %[d0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[128:131], %[a3] offset:0\n\t"
-      "ds_read_b128 v[132:135], %[a3] offset:64\n\t"
-      "ds_read_b128 v[136:139], %[a3] offset:128\n\t"
-      "ds_read_b128 v[140:143], %[a3] offset:192\n\t"
-      "ds_read_b128 v[144:147], %[a3] offset:256\n\t"
-      "ds_read_b128 v[148:151], %[a3] offset:320\n\t"
-      "ds_read_b128 v[152:155], %[a3] offset:384\n\t"
-      "ds_read_b128 v[156:159], %[a3] offset:448\n\t"
+      "ds_read_b128 v[128:131], %[a0] offset:55296\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:55296\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:55296\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:55296\n\t"
+      "ds_read_b128 v[144:147], %[a0] offset:55552\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:55552\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:55552\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:55552\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[160:163], %[c8], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[164:167], %[c9], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[168:171], %[c10], %[d0]\n\t"
@@ -561,14 +589,14 @@ __device__ __forceinline__ void chains_rows(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "v_mfma_f32_16x16x32_bf16 %[d0], v[188:191], %[c15], %[d0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[160:163], %[a3] offset:512\n\t"
-      "ds_read_b128 v[164:167], %[a3] offset:576\n\t"
-      "ds_read_b128 v[168:171], %[a3] offset:640\n\t"
-      "ds_read_b128 v[172:175], %[a3] offset:704\n\t"
-      "ds_read_b128 v[176:179], %[a3] offset:768\n\t"
-      "ds_read_b128 v[180:183], %[a3] offset:832\n\t"
-      "ds_read_b128 v[184:187], %[a3] offset:896\n\t"
-      "ds_read_b128 v[188:191], %[a3] offset:960\n\t"
+      "ds_read_b128 v[160:163], %[a0] offset:55808\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:55808\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:55808\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:55808\n\t"
+      "ds_read_b128 v[176:179], %[a0] offset:56064\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:56064\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:56064\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:56064\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[128:131], %[c0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[132:135], %[c1], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[136:139], %[c2], %[d1]\n\t"
@@ -606,13 +634,13 @@ __device__ __forceinline__ void chains_keys(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "ds_read_b128 %[st2], %[sa] offset:128\n\t"
       "ds_read_b128 %[st3], %[sa] offset:192\n\t"
       "ds_read_b128 v[192:195], %[a0] offset:0\n\t"
-      "ds_read_b128 v[196:199], %[a0] offset:64\n\t"
-      "ds_read_b128 v[200:203], %[a0] offset:128\n\t"
-      "ds_read_b128 v[204:207], %[a0] offset:192\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:0\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:0\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:0\n\t"
       "ds_read_b128 v[208:211], %[a0] offset:256\n\t"
-      "ds_read_b128 v[212:215], %[a0] offset:320\n\t"
-      "ds_read_b128 v[216:219], %[a0] offset:384\n\t"
-      "ds_read_b128 v[220:223], %[a0] offset:448\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:256\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:256\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:256\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[192:195], %[b0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[196:199], %[b1], %[s0]\n\t"
@@ -621,9 +649,9 @@ __device__ __forceinline__ void chains_keys(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b128 v[192:195], %[a0] offset:512\n\t"
-      "ds_read_b128 v[196:199], %[a0] offset:576\n\t"
-      "ds_read_b128 v[200:203], %[a0] offset:640\n\t"
-      "ds_read_b128 v[204:207], %[a0] offset:704\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:512\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:512\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:512\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[208:211], %[b4], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[212:215], %[b5], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[216:219], %[b6], %[s0]\n\t"
@@ -631,129 +659,129 @@ __device__ __forceinline__ void chains_keys(f32x4& s0, f32x4& s1, f32x4& d0, f32
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b128 v[208:211], %[a0] offset:768\n\t"
-      "ds_read_b128 v[212:215], %[a0] offset:832\n\t"
-      "ds_read_b128 v[216:219], %[a0] offset:896\n\t"
-      "ds_read_b128 v[220:223], %[a0] offset:960\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:768\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:768\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:768\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[192:195], %[b8], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[196:199], %[b9], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[200:203], %[b10], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[204:207], %[b11], %[s0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a1] offset:0\n\t"
-      "ds_read_b128 v[196:199], %[a1] offset:64\n\t"
-      "ds_read_b128 v[200:203], %[a1] offset:128\n\t"
-      "ds_read_b128 v[204:207], %[a1] offset:192\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:18432\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:18432\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:18432\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:18432\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[208:211], %[b12], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[212:215], %[b13], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[216:219], %[b14], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[220:223], %[b15], %[s0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a1] offset:256\n\t"
-      "ds_read_b128 v[212:215], %[a1] offset:320\n\t"
-      "ds_read_b128 v[216:219], %[a1] offset:384\n\t"
-      "ds_read_b128 v[220:223], %[a1] offset:448\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:18688\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:18688\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:18688\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:18688\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[192:195], %[b0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[196:199], %[b1], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[200:203], %[b2], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[204:207], %[b3], %[s1]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a1] offset:512\n\t"
-      "ds_read_b128 v[196:199], %[a1] offset:576\n\t"
-      "ds_read_b128 v[200:203], %[a1] offset:640\n\t"
-      "ds_read_b128 v[204:207], %[a1] offset:704\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:18944\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:18944\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:18944\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:18944\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[208:211], %[b4], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[212:215], %[b5], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[216:219], %[b6], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[220:223], %[b7], %[s1]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a1] offset:768\n\t"
-      "ds_read_b128 v[212:215], %[a1] offset:832\n\t"
-      "ds_read_b128 v[216:219], %[a1] offset:896\n\t"
-      "ds_read_b128 v[220:223], %[a1] offset:960\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:19200\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:19200\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:19200\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:19200\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[192:195], %[b8], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[196:199], %[b9], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[200:203], %[b10], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[204:207], %[b11], %[s1]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a2] offset:0\n\t"
-      "ds_read_b128 v[196:199], %[a2] offset:64\n\t"
-      "ds_read_b128 v[200:203], %[a2] offset:128\n\t"
-      "ds_read_b128 v[204:207], %[a2] offset:192\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:36864\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:36864\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:36864\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:36864\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[208:211], %[b12], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[212:215], %[b13], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[216:219], %[b14], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[220:223], %[b15], %[s1]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a2] offset:256\n\t"
-      "ds_read_b128 v[212:215], %[a2] offset:320\n\t"
-      "ds_read_b128 v[216:219], %[a2] offset:384\n\t"
-      "ds_read_b128 v[220:223], %[a2] offset:448\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:37120\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:37120\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:37120\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:37120\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[192:195], %[c0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[196:199], %[c1], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[200:203], %[c2], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[204:207], %[c3], %[d0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a2] offset:512\n\t"
-      "ds_read_b128 v[196:199], %[a2] offset:576\n\t"
-      "ds_read_b128 v[200:203], %[a2] offset:640\n\t"
-      "ds_read_b128 v[204:207], %[a2] offset:704\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:37376\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:37376\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:37376\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:37376\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[208:211], %[c4], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[212:215], %[c5], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[216:219], %[c6], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[220:223], %[c7], %[d0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a2] offset:768\n\t"
-      "ds_read_b128 v[212:215], %[a2] offset:832\n\t"
-      "ds_read_b128 v[216:219], %[a2] offset:896\n\t"
-      "ds_read_b128 v[220:223], %[a2] offset:960\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:37632\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:37632\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:37632\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:37632\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[192:195], %[c8], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[196:199], %[c9], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[200:203], %[c10], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[204:207], %[c11], %[d0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a3] offset:0\n\t"
-      "ds_read_b128 v[196:199], %[a3] offset:64\n\t"
-      "ds_read_b128 v[200:203], %[a3] offset:128\n\t"
-      "ds_read_b128 v[204:207], %[a3] offset:192\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:55296\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:55296\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:55296\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:55296\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[208:211], %[c12], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[212:215], %[c13], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[216:219], %[c14], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[220:223], %[c15], %[d0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a3] offset:256\n\t"
-      "ds_read_b128 v[212:215], %[a3] offset:320\n\t"
-      "ds_read_b128 v[216:219], %[a3] offset:384\n\t"
-      "ds_read_b128 v[220:223], %[a3] offset:448\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:55552\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:55552\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:55552\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:55552\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[192:195], %[c0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[196:199], %[c1], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[200:203], %[c2], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[204:207], %[c3], %[d1]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a3] offset:512\n\t"
-      "ds_read_b128 v[196:199], %[a3] offset:576\n\t"
-      "ds_read_b128 v[200:203], %[a3] offset:640\n\t"
-      "ds_read_b128 v[204:207], %[a3] offset:704\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:55808\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:55808\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:55808\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:55808\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[208:211], %[c4], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[212:215], %[c5], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[216:219], %[c6], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[220:223], %[c7], %[d1]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a3] offset:768\n\t"
-      "ds_read_b128 v[212:215], %[a3] offset:832\n\t"
-      "ds_read_b128 v[216:219], %[a3] offset:896\n\t"
-      "ds_read_b128 v[220:223], %[a3] offset:960\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:56064\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:56064\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:56064\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:56064\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[192:195], %[c8], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[196:199], %[c9], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[200:203], %[c10], %[d1]\n\t"
@@ -783,29 +811,29 @@ __device__ __forceinline__ void chains_keys(f32x4& s0, f32x4& s1, f32x4& d0, f32
 // asm, two after each group of MFMAs: an issuing copy stalls the wave while the
 // CU's memory path is busy, and copies issued back to back by all four waves
 // queue; spread out, the MFMAs already issued keep the pipe busy meanwhile.
-// Copy u (0 .. 15) reads 16 bytes per lane at vo + so[u % 8] of buffer rk (u <
+// Copy u (0 .. 15) reads 16 bytes per lane at vo[u % 8] + so[u % 8] of buffer rk (u <
 // 8) or rv (u >= 8) into LDS at m0 = mad[u] (plus 16 bytes per lane); m0 is
 // saved first and restored last (the compiler keeps it for its own copies).
-__device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16], const u32x4& rk, const u32x4& rv, uint32_t vo, const uint32_t (&so)[8], const uint32_t (&mad)[16]) {
+__device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16], const u32x4& rk, const u32x4& rv, const uint32_t (&vo)[8], const uint32_t (&so)[8], const uint32_t (&mad)[16]) {
   uint32_t m0_saved;
   asm volatile(
       "s_mov_b32 %[m0s], m0\n\t"
       "ds_read_b128 v[128:131], %[a0] offset:0\n\t"
-      "ds_read_b128 v[132:135], %[a0] offset:64\n\t"
-      "ds_read_b128 v[136:139], %[a0] offset:128\n\t"
-      "ds_read_b128 v[140:143], %[a0] offset:192\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:0\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:0\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:0\n\t"
       "ds_read_b128 v[144:147], %[a0] offset:256\n\t"
-      "ds_read_b128 v[148:151], %[a0] offset:320\n\t"
-      "ds_read_b128 v[152:155], %[a0] offset:384\n\t"
-      "ds_read_b128 v[156:159], %[a0] offset:448\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:256\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:256\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:256\n\t"
       "ds_read_b128 v[160:163], %[a0] offset:512\n\t"
-      "ds_read_b128 v[164:167], %[a0] offset:576\n\t"
-      "ds_read_b128 v[168:171], %[a0] offset:640\n\t"
-      "ds_read_b128 v[172:175], %[a0] offset:704\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:512\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:512\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:512\n\t"
       "ds_read_b128 v[176:179], %[a0] offset:768\n\t"
-      "ds_read_b128 v[180:183], %[a0] offset:832\n\t"
-      "ds_read_b128 v[184:187], %[a0] offset:896\n\t"
-      "ds_read_b128 v[188:191], %[a0] offset:960\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:768\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:768\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:768\n\t"
       "s_waitcnt lgkmcnt(8)\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[128:131], %[b0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[132:135], %[b1], %[s0]\n\t"
@@ -817,20 +845,20 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[s0], v[156:159], %[b7], %[s0]\n\t"
       "s_mov_b32 m0, %[m0]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so0] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo0], %[rk], %[so0] offen lds\n\t"
       "s_mov_b32 m0, %[m1]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so1] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo1], %[rk], %[so1] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[128:131], %[a1] offset:0\n\t"
-      "ds_read_b128 v[132:135], %[a1] offset:64\n\t"
-      "ds_read_b128 v[136:139], %[a1] offset:128\n\t"
-      "ds_read_b128 v[140:143], %[a1] offset:192\n\t"
-      "ds_read_b128 v[144:147], %[a1] offset:256\n\t"
-      "ds_read_b128 v[148:151], %[a1] offset:320\n\t"
-      "ds_read_b128 v[152:155], %[a1] offset:384\n\t"
-      "ds_read_b128 v[156:159], %[a1] offset:448\n\t"
+      "ds_read_b128 v[128:131], %[a0] offset:18432\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:18432\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:18432\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:18432\n\t"
+      "ds_read_b128 v[144:147], %[a0] offset:18688\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:18688\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:18688\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:18688\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[160:163], %[b8], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[164:167], %[b9], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[168:171], %[b10], %[s0]\n\t"
@@ -841,20 +869,20 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[s0], v[188:191], %[b15], %[s0]\n\t"
       "s_mov_b32 m0, %[m2]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so2] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo2], %[rk], %[so2] offen lds\n\t"
       "s_mov_b32 m0, %[m3]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so3] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo3], %[rk], %[so3] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[160:163], %[a1] offset:512\n\t"
-      "ds_read_b128 v[164:167], %[a1] offset:576\n\t"
-      "ds_read_b128 v[168:171], %[a1] offset:640\n\t"
-      "ds_read_b128 v[172:175], %[a1] offset:704\n\t"
-      "ds_read_b128 v[176:179], %[a1] offset:768\n\t"
-      "ds_read_b128 v[180:183], %[a1] offset:832\n\t"
-      "ds_read_b128 v[184:187], %[a1] offset:896\n\t"
-      "ds_read_b128 v[188:191], %[a1] offset:960\n\t"
+      "ds_read_b128 v[160:163], %[a0] offset:18944\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:18944\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:18944\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:18944\n\t"
+      "ds_read_b128 v[176:179], %[a0] offset:19200\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:19200\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:19200\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:19200\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[128:131], %[b0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[132:135], %[b1], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[136:139], %[b2], %[s1]\n\t"
@@ -865,20 +893,20 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[s1], v[156:159], %[b7], %[s1]\n\t"
       "s_mov_b32 m0, %[m4]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so4] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo4], %[rk], %[so4] offen lds\n\t"
       "s_mov_b32 m0, %[m5]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so5] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo5], %[rk], %[so5] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[128:131], %[a2] offset:0\n\t"
-      "ds_read_b128 v[132:135], %[a2] offset:64\n\t"
-      "ds_read_b128 v[136:139], %[a2] offset:128\n\t"
-      "ds_read_b128 v[140:143], %[a2] offset:192\n\t"
-      "ds_read_b128 v[144:147], %[a2] offset:256\n\t"
-      "ds_read_b128 v[148:151], %[a2] offset:320\n\t"
-      "ds_read_b128 v[152:155], %[a2] offset:384\n\t"
-      "ds_read_b128 v[156:159], %[a2] offset:448\n\t"
+      "ds_read_b128 v[128:131], %[a0] offset:36864\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:36864\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:36864\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:36864\n\t"
+      "ds_read_b128 v[144:147], %[a0] offset:37120\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:37120\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:37120\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:37120\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[160:163], %[b8], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[164:167], %[b9], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[168:171], %[b10], %[s1]\n\t"
@@ -889,20 +917,20 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[s1], v[188:191], %[b15], %[s1]\n\t"
       "s_mov_b32 m0, %[m6]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so6] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo6], %[rk], %[so6] offen lds\n\t"
       "s_mov_b32 m0, %[m7]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so7] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo7], %[rk], %[so7] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[160:163], %[a2] offset:512\n\t"
-      "ds_read_b128 v[164:167], %[a2] offset:576\n\t"
-      "ds_read_b128 v[168:171], %[a2] offset:640\n\t"
-      "ds_read_b128 v[172:175], %[a2] offset:704\n\t"
-      "ds_read_b128 v[176:179], %[a2] offset:768\n\t"
-      "ds_read_b128 v[180:183], %[a2] offset:832\n\t"
-      "ds_read_b128 v[184:187], %[a2] offset:896\n\t"
-      "ds_read_b128 v[188:191], %[a2] offset:960\n\t"
+      "ds_read_b128 v[160:163], %[a0] offset:37376\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:37376\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:37376\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:37376\n\t"
+      "ds_read_b128 v[176:179], %[a0] offset:37632\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:37632\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:37632\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:37632\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[128:131], %[c0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[132:135], %[c1], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[136:139], %[c2], %[d0]\n\t"
@@ -913,20 +941,20 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[d0], v[156:159], %[c7], %[d0]\n\t"
       "s_mov_b32 m0, %[m8]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so0] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo0], %[rv], %[so0] offen lds\n\t"
       "s_mov_b32 m0, %[m9]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so1] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo1], %[rv], %[so1] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[128:131], %[a3] offset:0\n\t"
-      "ds_read_b128 v[132:135], %[a3] offset:64\n\t"
-      "ds_read_b128 v[136:139], %[a3] offset:128\n\t"
-      "ds_read_b128 v[140:143], %[a3] offset:192\n\t"
-      "ds_read_b128 v[144:147], %[a3] offset:256\n\t"
-      "ds_read_b128 v[148:151], %[a3] offset:320\n\t"
-      "ds_read_b128 v[152:155], %[a3] offset:384\n\t"
-      "ds_read_b128 v[156:159], %[a3] offset:448\n\t"
+      "ds_read_b128 v[128:131], %[a0] offset:55296\n\t"
+      "ds_read_b128 v[132:135], %[a1] offset:55296\n\t"
+      "ds_read_b128 v[136:139], %[a2] offset:55296\n\t"
+      "ds_read_b128 v[140:143], %[a3] offset:55296\n\t"
+      "ds_read_b128 v[144:147], %[a0] offset:55552\n\t"
+      "ds_read_b128 v[148:151], %[a1] offset:55552\n\t"
+      "ds_read_b128 v[152:155], %[a2] offset:55552\n\t"
+      "ds_read_b128 v[156:159], %[a3] offset:55552\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[160:163], %[c8], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[164:167], %[c9], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[168:171], %[c10], %[d0]\n\t"
@@ -937,20 +965,20 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[d0], v[188:191], %[c15], %[d0]\n\t"
       "s_mov_b32 m0, %[m10]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so2] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo2], %[rv], %[so2] offen lds\n\t"
       "s_mov_b32 m0, %[m11]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so3] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo3], %[rv], %[so3] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[160:163], %[a3] offset:512\n\t"
-      "ds_read_b128 v[164:167], %[a3] offset:576\n\t"
-      "ds_read_b128 v[168:171], %[a3] offset:640\n\t"
-      "ds_read_b128 v[172:175], %[a3] offset:704\n\t"
-      "ds_read_b128 v[176:179], %[a3] offset:768\n\t"
-      "ds_read_b128 v[180:183], %[a3] offset:832\n\t"
-      "ds_read_b128 v[184:187], %[a3] offset:896\n\t"
-      "ds_read_b128 v[188:191], %[a3] offset:960\n\t"
+      "ds_read_b128 v[160:163], %[a0] offset:55808\n\t"
+      "ds_read_b128 v[164:167], %[a1] offset:55808\n\t"
+      "ds_read_b128 v[168:171], %[a2] offset:55808\n\t"
+      "ds_read_b128 v[172:175], %[a3] offset:55808\n\t"
+      "ds_read_b128 v[176:179], %[a0] offset:56064\n\t"
+      "ds_read_b128 v[180:183], %[a1] offset:56064\n\t"
+      "ds_read_b128 v[184:187], %[a2] offset:56064\n\t"
+      "ds_read_b128 v[188:191], %[a3] offset:56064\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[128:131], %[c0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[132:135], %[c1], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[136:139], %[c2], %[d1]\n\t"
@@ -961,10 +989,10 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[d1], v[156:159], %[c7], %[d1]\n\t"
       "s_mov_b32 m0, %[m12]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so4] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo4], %[rv], %[so4] offen lds\n\t"
       "s_mov_b32 m0, %[m13]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so5] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo5], %[rv], %[so5] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[160:163], %[c8], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[164:167], %[c9], %[d1]\n\t"
@@ -976,13 +1004,14 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[d1], v[188:191], %[c15], %[d1]\n\t"
       "s_mov_b32 m0, %[m14]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so6] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo6], %[rv], %[so6] offen lds\n\t"
       "s_mov_b32 m0, %[m15]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so7] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo7], %[rv], %[so7] offen lds\n\t"
       "s_nop 15\n\ts_nop 3\n\t"
       "s_mov_b32 m0, %[m0s]"
-      : [m0s] "=&s"(m0_saved), [s0] "=&v"(s0), [s1] "=&v"(s1), [d0] "=&v"(d0), [d1] "=&v"(d1)
+      : [m0s] "=&s"(m0_saved), [s0] "=&v"(s0), [s1] "=&v"(s1), [d0] "=&v"(d0),
+        [d1] "=&v"(d1)
       : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),
         [b0] "a"(b[0]), [b1] "a"(b[1]), [b2] "a"(b[2]), [b3] "a"(b[3]),
         [b4] "a"(b[4]), [b5] "a"(b[5]), [b6] "a"(b[6]), [b7] "a"(b[7]),
@@ -992,16 +1021,18 @@ __device__ __forceinline__ void chains_rows_dma(f32x4& s0, f32x4& s1, f32x4& d0,
         [c4] "a"(c[4]), [c5] "a"(c[5]), [c6] "a"(c[6]), [c7] "a"(c[7]),
         [c8] "a"(c[8]), [c9] "a"(c[9]), [c10] "a"(c[10]), [c11] "a"(c[11]),
         [c12] "a"(c[12]), [c13] "a"(c[13]), [c14] "a"(c[14]), [c15] "a"(c[15]),
-        [rk] "s"(rk), [rv] "s"(rv), [vo] "v"(vo), [so0] "s"(so[0]),
-        [so1] "s"(so[1]), [so2] "s"(so[2]), [so3] "s"(so[3]), [so4] "s"(so[4]),
-        [so5] "s"(so[5]), [so6] "s"(so[6]), [so7] "s"(so[7]), [m0] "s"(mad[0]),
-        [m1] "s"(mad[1]), [m2] "s"(mad[2]), [m3] "s"(mad[3]), [m4] "s"(mad[4]),
-        [m5] "s"(mad[5]), [m6] "s"(mad[6]), [m7] "s"(mad[7]), [m8] "s"(mad[8]),
-        [m9] "s"(mad[9]), [m10] "s"(mad[10]), [m11] "s"(mad[11]), [m12] "s"(mad[12]),
-        [m13] "s"(mad[13]), [m14] "s"(mad[14]), [m15] "s"(mad[15])
+        [rk] "s"(rk), [rv] "s"(rv), [vo0] "v"(vo[0]), [vo1] "v"(vo[1]),
+        [vo2] "v"(vo[2]), [vo3] "v"(vo[3]), [vo4] "v"(vo[4]), [vo5] "v"(vo[5]),
+        [vo6] "v"(vo[6]), [vo7] "v"(vo[7]), [so0] "s"(so[0]), [so1] "s"(so[1]),
+        [so2] "s"(so[2]), [so3] "s"(so[3]), [so4] "s"(so[4]), [so5] "s"(so[5]),
+        [so6] "s"(so[6]), [so7] "s"(so[7]), [m0] "s"(mad[0]), [m1] "s"(mad[1]),
+        [m2] "s"(mad[2]), [m3] "s"(mad[3]), [m4] "s"(mad[4]), [m5] "s"(mad[5]),
+        [m6] "s"(mad[6]), [m7] "s"(mad[7]), [m8] "s"(mad[8]), [m9] "s"(mad[9]),
+        [m10] "s"(mad[10]), [m11] "s"(mad[11]), [m12] "s"(mad[12]), [m13] "s"(mad[13]),
+        [m14] "s"(mad[14]), [m15] "s"(mad[15])
       : "memory", "v128", "v129", "v130", "v131", "v132", "v133", "v134", "v135", "v136", "v137", "v138", "v139", "v140", "v141", "v142", "v143", "v144", "v145", "v146", "v147", "v148", "v149", "v150", "v151", "v152", "v153", "v154", "v155", "v156", "v157", "v158", "v159", "v160", "v161", "v162", "v163", "v164", "v165", "v166", "v167", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191");
 }
-__device__ __forceinline__ void chains_keys_dma(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16], uint32_t sad, f32x4 (&st)[4], const u32x4& rk, const u32x4& rv, uint32_t vo, const uint32_t (&so)[8], const uint32_t (&mad)[16]) {
+__device__ __forceinline__ void chains_keys_dma(f32x4& s0, f32x4& s1, f32x4& d0, f32x4& d1, const uint32_t (&ad)[4], const bf16x8 (&b)[16], const bf16x8 (&c)[16], uint32_t sad, f32x4 (&st)[4], const u32x4& rk, const u32x4& rv, const uint32_t (&vo)[8], const uint32_t (&so)[8], const uint32_t (&mad)[16]) {
   uint32_t m0_saved;
   asm volatile(
       "s_mov_b32 %[m0s], m0\n\t"
@@ -1010,13 +1041,13 @@ __device__ __forceinline__ void chains_keys_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "ds_read_b128 %[st2], %[sa] offset:128\n\t"
       "ds_read_b128 %[st3], %[sa] offset:192\n\t"
       "ds_read_b128 v[192:195], %[a0] offset:0\n\t"
-      "ds_read_b128 v[196:199], %[a0] offset:64\n\t"
-      "ds_read_b128 v[200:203], %[a0] offset:128\n\t"
-      "ds_read_b128 v[204:207], %[a0] offset:192\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:0\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:0\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:0\n\t"
       "ds_read_b128 v[208:211], %[a0] offset:256\n\t"
-      "ds_read_b128 v[212:215], %[a0] offset:320\n\t"
-      "ds_read_b128 v[216:219], %[a0] offset:384\n\t"
-      "ds_read_b128 v[220:223], %[a0] offset:448\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:256\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:256\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:256\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[192:195], %[b0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[196:199], %[b1], %[s0]\n\t"
@@ -1024,189 +1055,189 @@ __device__ __forceinline__ void chains_keys_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[s0], v[204:207], %[b3], %[s0]\n\t"
       "s_mov_b32 m0, %[m0]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so0] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo0], %[rk], %[so0] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b128 v[192:195], %[a0] offset:512\n\t"
-      "ds_read_b128 v[196:199], %[a0] offset:576\n\t"
-      "ds_read_b128 v[200:203], %[a0] offset:640\n\t"
-      "ds_read_b128 v[204:207], %[a0] offset:704\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:512\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:512\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:512\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[208:211], %[b4], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[212:215], %[b5], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[216:219], %[b6], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[220:223], %[b7], %[s0]\n\t"
       "s_mov_b32 m0, %[m1]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so1] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo1], %[rk], %[so1] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b128 v[208:211], %[a0] offset:768\n\t"
-      "ds_read_b128 v[212:215], %[a0] offset:832\n\t"
-      "ds_read_b128 v[216:219], %[a0] offset:896\n\t"
-      "ds_read_b128 v[220:223], %[a0] offset:960\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:768\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:768\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:768\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[192:195], %[b8], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[196:199], %[b9], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[200:203], %[b10], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[204:207], %[b11], %[s0]\n\t"
       "s_mov_b32 m0, %[m2]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so2] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo2], %[rk], %[so2] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a1] offset:0\n\t"
-      "ds_read_b128 v[196:199], %[a1] offset:64\n\t"
-      "ds_read_b128 v[200:203], %[a1] offset:128\n\t"
-      "ds_read_b128 v[204:207], %[a1] offset:192\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:18432\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:18432\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:18432\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:18432\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[208:211], %[b12], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[212:215], %[b13], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[216:219], %[b14], %[s0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s0], v[220:223], %[b15], %[s0]\n\t"
       "s_mov_b32 m0, %[m3]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so3] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo3], %[rk], %[so3] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a1] offset:256\n\t"
-      "ds_read_b128 v[212:215], %[a1] offset:320\n\t"
-      "ds_read_b128 v[216:219], %[a1] offset:384\n\t"
-      "ds_read_b128 v[220:223], %[a1] offset:448\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:18688\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:18688\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:18688\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:18688\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[192:195], %[b0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[196:199], %[b1], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[200:203], %[b2], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[204:207], %[b3], %[s1]\n\t"
       "s_mov_b32 m0, %[m4]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so4] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo4], %[rk], %[so4] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a1] offset:512\n\t"
-      "ds_read_b128 v[196:199], %[a1] offset:576\n\t"
-      "ds_read_b128 v[200:203], %[a1] offset:640\n\t"
-      "ds_read_b128 v[204:207], %[a1] offset:704\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:18944\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:18944\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:18944\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:18944\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[208:211], %[b4], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[212:215], %[b5], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[216:219], %[b6], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[220:223], %[b7], %[s1]\n\t"
       "s_mov_b32 m0, %[m5]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so5] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo5], %[rk], %[so5] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a1] offset:768\n\t"
-      "ds_read_b128 v[212:215], %[a1] offset:832\n\t"
-      "ds_read_b128 v[216:219], %[a1] offset:896\n\t"
-      "ds_read_b128 v[220:223], %[a1] offset:960\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:19200\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:19200\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:19200\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:19200\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[192:195], %[b8], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[196:199], %[b9], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[200:203], %[b10], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[204:207], %[b11], %[s1]\n\t"
       "s_mov_b32 m0, %[m6]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so6] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo6], %[rk], %[so6] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a2] offset:0\n\t"
-      "ds_read_b128 v[196:199], %[a2] offset:64\n\t"
-      "ds_read_b128 v[200:203], %[a2] offset:128\n\t"
-      "ds_read_b128 v[204:207], %[a2] offset:192\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:36864\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:36864\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:36864\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:36864\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[208:211], %[b12], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[212:215], %[b13], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[216:219], %[b14], %[s1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[s1], v[220:223], %[b15], %[s1]\n\t"
       "s_mov_b32 m0, %[m7]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rk], %[so7] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo7], %[rk], %[so7] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a2] offset:256\n\t"
-      "ds_read_b128 v[212:215], %[a2] offset:320\n\t"
-      "ds_read_b128 v[216:219], %[a2] offset:384\n\t"
-      "ds_read_b128 v[220:223], %[a2] offset:448\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:37120\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:37120\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:37120\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:37120\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[192:195], %[c0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[196:199], %[c1], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[200:203], %[c2], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[204:207], %[c3], %[d0]\n\t"
       "s_mov_b32 m0, %[m8]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so0] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo0], %[rv], %[so0] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a2] offset:512\n\t"
-      "ds_read_b128 v[196:199], %[a2] offset:576\n\t"
-      "ds_read_b128 v[200:203], %[a2] offset:640\n\t"
-      "ds_read_b128 v[204:207], %[a2] offset:704\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:37376\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:37376\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:37376\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:37376\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[208:211], %[c4], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[212:215], %[c5], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[216:219], %[c6], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[220:223], %[c7], %[d0]\n\t"
       "s_mov_b32 m0, %[m9]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so1] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo1], %[rv], %[so1] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a2] offset:768\n\t"
-      "ds_read_b128 v[212:215], %[a2] offset:832\n\t"
-      "ds_read_b128 v[216:219], %[a2] offset:896\n\t"
-      "ds_read_b128 v[220:223], %[a2] offset:960\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:37632\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:37632\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:37632\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:37632\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[192:195], %[c8], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[196:199], %[c9], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[200:203], %[c10], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[204:207], %[c11], %[d0]\n\t"
       "s_mov_b32 m0, %[m10]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so2] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo2], %[rv], %[so2] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a3] offset:0\n\t"
-      "ds_read_b128 v[196:199], %[a3] offset:64\n\t"
-      "ds_read_b128 v[200:203], %[a3] offset:128\n\t"
-      "ds_read_b128 v[204:207], %[a3] offset:192\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:55296\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:55296\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:55296\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:55296\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[208:211], %[c12], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[212:215], %[c13], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[216:219], %[c14], %[d0]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d0], v[220:223], %[c15], %[d0]\n\t"
       "s_mov_b32 m0, %[m11]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so3] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo3], %[rv], %[so3] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a3] offset:256\n\t"
-      "ds_read_b128 v[212:215], %[a3] offset:320\n\t"
-      "ds_read_b128 v[216:219], %[a3] offset:384\n\t"
-      "ds_read_b128 v[220:223], %[a3] offset:448\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:55552\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:55552\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:55552\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:55552\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[192:195], %[c0], 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[196:199], %[c1], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[200:203], %[c2], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[204:207], %[c3], %[d1]\n\t"
       "s_mov_b32 m0, %[m12]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so4] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo4], %[rv], %[so4] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[192:195], %[a3] offset:512\n\t"
-      "ds_read_b128 v[196:199], %[a3] offset:576\n\t"
-      "ds_read_b128 v[200:203], %[a3] offset:640\n\t"
-      "ds_read_b128 v[204:207], %[a3] offset:704\n\t"
+      "ds_read_b128 v[192:195], %[a0] offset:55808\n\t"
+      "ds_read_b128 v[196:199], %[a1] offset:55808\n\t"
+      "ds_read_b128 v[200:203], %[a2] offset:55808\n\t"
+      "ds_read_b128 v[204:207], %[a3] offset:55808\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[208:211], %[c4], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[212:215], %[c5], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[216:219], %[c6], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[220:223], %[c7], %[d1]\n\t"
       "s_mov_b32 m0, %[m13]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so5] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo5], %[rv], %[so5] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
-      "ds_read_b128 v[208:211], %[a3] offset:768\n\t"
-      "ds_read_b128 v[212:215], %[a3] offset:832\n\t"
-      "ds_read_b128 v[216:219], %[a3] offset:896\n\t"
-      "ds_read_b128 v[220:223], %[a3] offset:960\n\t"
+      "ds_read_b128 v[208:211], %[a0] offset:56064\n\t"
+      "ds_read_b128 v[212:215], %[a1] offset:56064\n\t"
+      "ds_read_b128 v[216:219], %[a2] offset:56064\n\t"
+      "ds_read_b128 v[220:223], %[a3] offset:56064\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[192:195], %[c8], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[196:199], %[c9], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[200:203], %[c10], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[204:207], %[c11], %[d1]\n\t"
       "s_mov_b32 m0, %[m14]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so6] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo6], %[rv], %[so6] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[208:211], %[c12], %[d1]\n\t"
       "v_mfma_f32_16x16x32_bf16 %[d1], v[212:215], %[c13], %[d1]\n\t"
@@ -1214,11 +1245,12 @@ __device__ __forceinline__ void chains_keys_dma(f32x4& s0, f32x4& s1, f32x4& d0,
       "v_mfma_f32_16x16x32_bf16 %[d1], v[220:223], %[c15], %[d1]\n\t"
       "s_mov_b32 m0, %[m15]\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vo], %[rv], %[so7] offen lds\n\t"
+      "buffer_load_dwordx4 %[vo7], %[rv], %[so7] offen lds\n\t"
       "s_nop 15\n\ts_nop 3\n\t"
       "s_mov_b32 m0, %[m0s]"
-      : [m0s] "=&s"(m0_saved), [s0] "=&v"(s0), [s1] "=&v"(s1), [d0] "=&v"(d0), [d1] "=&v"(d1),
-        [st0] "=&v"(st[0]), [st1] "=&v"(st[1]), [st2] "=&v"(st[2]), [st3] "=&v"(st[3])
+      : [m0s] "=&s"(m0_saved), [s0] "=&v"(s0), [s1] "=&v"(s1), [d0] "=&v"(d0),
+        [d1] "=&v"(d1), [st0] "=&v"(st[0]), [st1] "=&v"(st[1]), [st2] "=&v"(st[2]),
+        [st3] "=&v"(st[3])
       : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),
         [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
         [b4] "v"(b[4]), [b5] "v"(b[5]), [b6] "v"(b[6]), [b7] "v"(b[7]),
@@ -1228,13 +1260,15 @@ __device__ __forceinline__ void chains_keys_dma(f32x4& s0, f32x4& s1, f32x4& d0,
         [c4] "v"(c[4]), [c5] "v"(c[5]), [c6] "v"(c[6]), [c7] "v"(c[7]),
         [c8] "v"(c[8]), [c9] "v"(c[9]), [c10] "v"(c[10]), [c11] "v"(c[11]),
         [c12] "v"(c[12]), [c13] "v"(c[13]), [c14] "v"(c[14]), [c15] "v"(c[15]),
-        [sa] "v"(sad), [rk] "s"(rk), [rv] "s"(rv), [vo] "v"(vo),
-        [so0] "s"(so[0]), [so1] "s"(so[1]), [so2] "s"(so[2]), [so3] "s"(so[3]),
-        [so4] "s"(so[4]), [so5] "s"(so[5]), [so6] "s"(so[6]), [so7] "s"(so[7]),
-        [m0] "s"(mad[0]), [m1] "s"(mad[1]), [m2] "s"(mad[2]), [m3] "s"(mad[3]),
-        [m4] "s"(mad[4]), [m5] "s"(mad[5]), [m6] "s"(mad[6]), [m7] "s"(mad[7]),
-        [m8] "s"(mad[8]), [m9] "s"(mad[9]), [m10] "s"(mad[10]), [m11] "s"(mad[11]),
-        [m12] "s"(mad[12]), [m13] "s"(mad[13]), [m14] "s"(mad[14]), [m15] "s"(mad[15])
+        [sa] "v"(sad), [rk] "s"(rk), [rv] "s"(rv), [vo0] "v"(vo[0]),
+        [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3]), [vo4] "v"(vo[4]),
+        [vo5] "v"(vo[5]), [vo6] "v"(vo[6]), [vo7] "v"(vo[7]), [so0] "s"(so[0]),
+        [so1] "s"(so[1]), [so2] "s"(so[2]), [so3] "s"(so[3]), [so4] "s"(so[4]),
+        [so5] "s"(so[5]), [so6] "s"(so[6]), [so7] "s"(so[7]), [m0] "s"(mad[0]),
+        [m1] "s"(mad[1]), [m2] "s"(mad[2]), [m3] "s"(mad[3]), [m4] "s"(mad[4]),
+        [m5] "s"(mad[5]), [m6] "s"(mad[6]), [m7] "s"(mad[7]), [m8] "s"(mad[8]),
+        [m9] "s"(mad[9]), [m10] "s"(mad[10]), [m11] "s"(mad[11]), [m12] "s"(mad[12]),
+        [m13] "s"(mad[13]), [m14] "s"(mad[14]), [m15] "s"(mad[15])
       : "memory", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223");
 }
 
@@ -1247,7 +1281,7 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   // stage s (0, 1): the K rows of a 32-key tile at lds + 2 s kStage, its V rows after them
   __shared__ __attribute__((aligned(256))) uint8_t lds[4 * kStage];
   const int W = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4, lane16 = lane * 16;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const int64_t nrows = a.T * a.H;
   const int64_t g0 = (int64_t)blockIdx.x * kRowsPerWg;  // the workgroup's rows g0 .. glast
   const int64_t glast = g0 + kRowsPerWg - 1 < nrows ? g0 + kRowsPerWg - 1 : nrows - 1;
@@ -1300,11 +1334,17 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     }
   };
   // Tile j's stage; this wave's quarter of its K and V rows into it.
+  // Copies of this wave's rows 8W .. 8W+7 of a tile: per-lane (swizzled) and
+  // per-row buffer offsets.
+  uint32_t vo[8], soff[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    vo[u] = (uint32_t)(16 * (lane ^ ((8 * W + u) & 15)));
+    soff[u] = (uint32_t)((8 * W + u) * 1024);
+  }
   auto kst = [&](int j) { return lds + (j & 1) * (2 * kStage); };
-  auto issue_k = [&](int j, int stride) { copy8(tile_src(s, j, a.ck, a.k).r, W, lane16, kst(j), stride); };
-  auto issue_v = [&](int j, int stride) {
-    copy8(tile_src(s, j, a.cv, a.v).r, W, lane16, kst(j) + kStage, stride);
-  };
+  auto issue_k = [&](int j) { copy8(tile_src(s, j, a.ck, a.k).r, W, vo, kst(j)); };
+  auto issue_v = [&](int j) { copy8(tile_src(s, j, a.cv, a.v).r, W, vo, kst(j) + kStage); };
   // Top of tile j: this wave's copies of it (issued during tile j-1) have
   // landed, then every wave's; every wave is also done with tile j-1, whose
   // stage tile j+1 takes.
@@ -1312,18 +1352,23 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     wait_vm<0>();
     barrier_no_fence();
   };
-  const int voff = (4 * g4 + (l16 >> 2)) * kRowT + 8 * (l16 & 3);  // transposing reads
-  const int foffF = l16 * kRowF + 16 * g4, foffT = l16 * kRowT + 16 * g4;
-  // Copies of this wave's rows 8W .. 8W+7 of a tile: buffer offsets and LDS rows.
-  uint32_t soff[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) soff[u] = (uint32_t)((8 * W + u) * 1024);
-  auto next_rows = [&](int j, int kstride, int vstride, uint32_t (&mad)[16]) {
+  uint32_t cb[4], tb[8];
+  read_bases(l16, g4, cb, tb);
+  // LDS rows of this wave's copies of tile j (K rows, then V rows)
+  auto next_rows = [&](int j, uint32_t (&mad)[16]) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      mad[u] = __builtin_amdgcn_readfirstlane(lds_addr(kst(j) + (8 * W + u) * kstride));
-      mad[8 + u] = __builtin_amdgcn_readfirstlane(lds_addr(kst(j) + kStage + (8 * W + u) * vstride));
+      mad[u] = __builtin_amdgcn_readfirstlane(lds_addr(kst(j) + (8 * W + u) * kRow));
+      mad[8 + u] = __builtin_amdgcn_readfirstlane(lds_addr(kst(j) + kStage + (8 * W + u) * kRow));
     }
+  };
+  auto chain_bases = [&](const uint8_t* st, uint32_t (&ad)[4]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) ad[b] = lds_addr(st) + cb[b];
+  };
+  auto tr_bases = [&](const uint8_t* tile, uint32_t (&ta)[8]) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) ta[b] = lds_addr(tile) + tb[b];
   };
 
   // ---- pass A: per row the maximum (fixed reference m), the weights
@@ -1332,9 +1377,9 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   //   the forward's ungated output a = (sum bf16(e_j) v_j) / (sum bf16(e_j)),
   // whence lse = m + log2 l and Dt = ldp / l = sum p_j dp_j: the same p and dp
   // the score gradients use, so that sum_j p_j (dp_j - Dt) = 0 holds to fp32
-  // rounding (an exact-zero gradient stays zero).  K is read as fragments
-  // only (rows kRowF apart), V also transposed (kRowT).  Keys 16h + 4 g4 + r
-  // of a tile are in sc[h][r] (h = 0, 1).
+  // rounding (an exact-zero gradient stays zero).  K is read as fragments,
+  // V as fragments and transposed.  Keys 16h + 4 g4 + r of a tile are in
+  // sc[h][r] (h = 0, 1).
   f32x4 o[32];
   float m = -INFINITY, mseen = -INFINITY, l = 0.0f, lb = 0.0f, ldp = 0.0f;
   bool fixed_m = false;
@@ -1344,19 +1389,19 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     l = lb = ldp = 0.0f;
     bool over = false;
     barrier_no_fence();  // every wave is done with the stages
-    issue_k(0, kRowF);
-    issue_v(0, kRowT);
+    issue_k(0);
+    issue_v(0);
     for (int j = 0; j < nt; ++j) {
       arrive();
       uint8_t* const sk = kst(j);
       f32x4 sc[2], dp[2];  // S^T = K Q^T, dP^T = V dA^T
-      const uint32_t ad[4] = {lds_addr(sk + foffF), lds_addr(sk + 16 * kRowF + foffF),
-                              lds_addr(sk + kStage + foffT), lds_addr(sk + kStage + 16 * kRowT + foffT)};
+      uint32_t ad[4];
+      chain_bases(sk, ad);
       if (j + 1 < nt) {
         uint32_t mad[16];
-        next_rows(j + 1, kRowF, kRowT, mad);
+        next_rows(j + 1, mad);
         chains_rows_dma(sc[0], sc[1], dp[0], dp[1], ad, qf, daf, tile_desc(s, j + 1, a.ck, a.k),
-                        tile_desc(s, j + 1, a.cv, a.v), (uint32_t)lane16, soff, mad);
+                        tile_desc(s, j + 1, a.cv, a.v), vo, soff, mad);
       } else {
         chains_rows(sc[0], sc[1], dp[0], dp[1], ad, qf, daf);
       }
@@ -1385,7 +1430,9 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
         pb[i] = (__bf16)e;
         lb += (float)pb[i];
       }
-      tr_rows(o, lds_addr(sk + kStage + voff), lds_addr(sk + kStage + 16 * kRowT + voff), pb);
+      uint32_t ta[8];
+      tr_bases(sk + kStage, ta);
+      tr_rows(o, ta, pb);
     }
     // the workgroup walks the tiles again (all waves, barriers in step) if a
     // score of any row rose more than 2^64 above its reference
@@ -1422,23 +1469,23 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     if (valid) *reinterpret_cast<float4*>(a.dg + ro + d0) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
   }
 
-  // ---- pass B: dq.  K is also read transposed (kRowT), V as fragments only.
+  // ---- pass B: dq.  K is read as fragments and transposed, V as fragments.
 #pragma unroll
   for (int db = 0; db < 32; ++db) o[db] = f32x4{};
   barrier_no_fence();  // every wave is done with the stages
-  issue_k(0, kRowT);
-  issue_v(0, kRowF);
+  issue_k(0);
+  issue_v(0);
   for (int j = 0; j < nt; ++j) {
     arrive();
     uint8_t* const sk = kst(j);
     f32x4 sc[2], dp[2];
-    const uint32_t ad[4] = {lds_addr(sk + foffT), lds_addr(sk + 16 * kRowT + foffT),
-                            lds_addr(sk + kStage + foffF), lds_addr(sk + kStage + 16 * kRowF + foffF)};
+    uint32_t ad[4];
+    chain_bases(sk, ad);
     if (j + 1 < nt) {
       uint32_t mad[16];
-      next_rows(j + 1, kRowT, kRowF, mad);
+      next_rows(j + 1, mad);
       chains_rows_dma(sc[0], sc[1], dp[0], dp[1], ad, qf, daf, tile_desc(s, j + 1, a.ck, a.k),
-                      tile_desc(s, j + 1, a.cv, a.v), (uint32_t)lane16, soff, mad);
+                      tile_desc(s, j + 1, a.cv, a.v), vo, soff, mad);
     } else {
       chains_rows(sc[0], sc[1], dp[0], dp[1], ad, qf, daf);
     }
@@ -1451,7 +1498,9 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
       const float p = kk >= lo_v && kk < hi_v ? __builtin_amdgcn_exp2f(sc[i >> 2][i & 3] * a.c - lse) : 0.0f;
       dsb[i] = (__bf16)(p * (dp[i >> 2][i & 3] - dt));
     }
-    tr_rows(o, lds_addr(sk + voff), lds_addr(sk + 16 * kRowT + voff), dsb);
+    uint32_t ta[8];
+    tr_bases(sk, ta);
+    tr_rows(o, ta, dsb);
   }
   mfma_drain();
   if (valid) {
@@ -1523,12 +1572,18 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
   // Row block i's stage; this wave's quarter of its Q and dA rows, and of its
   // statistics (lanes 0, 1: 8 rows' lse, then their Dt): 18 DMA instructions.
   const int nb = (int)(rb1 - rb0 + 1);
+  uint32_t vo[8], soff[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    vo[u] = (uint32_t)(16 * (lane ^ ((8 * W + u) & 15)));
+    soff[u] = (uint32_t)((8 * W + u) * 1024);
+  }
   auto st = [&](int i) { return lds + (i & 1) * kKStage; };
   auto issue_q = [&](int i) {
     const int64_t r0 = (rb0 + i) * kTile;
     const int nr = nrows - r0 < kTile ? (int)(nrows - r0) : kTile;
     uint8_t* sp = st(i);
-    copy8(make_rsrc(a.q + r0 * kD, nr * 1024), W, lane16, sp, kRowT);
+    copy8(make_rsrc(a.q + r0 * kD, nr * 1024), W, vo, sp);
     if (lane < 2) {
       dma16_buf(make_rsrc(a.lse + r0, nr * 4), 32 * W + lane16, (lds_void*)(sp + 2 * kStage + 32 * W));
       dma16_buf(make_rsrc(a.dt + r0, nr * 4), 32 * W + lane16,
@@ -1538,13 +1593,10 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
   auto issue_a = [&](int i) {
     const int64_t r0 = (rb0 + i) * kTile;
     const int nr = nrows - r0 < kTile ? (int)(nrows - r0) : kTile;
-    copy8(make_rsrc(a.da + r0 * kD, nr * 1024), W, lane16, st(i) + kStage, kRowT);
+    copy8(make_rsrc(a.da + r0 * kD, nr * 1024), W, vo, st(i) + kStage);
   };
-  const int voff = (4 * g4 + (l16 >> 2)) * kRowT + 8 * (l16 & 3);
-  const int foff = l16 * kRowT + 16 * g4;
-  uint32_t soff[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) soff[u] = (uint32_t)((8 * W + u) * 1024);
+  uint32_t cb[4], tb[8];
+  read_bases(l16, g4, cb, tb);
   issue_q(0);
   issue_a(0);
   for (int i = 0; i < nb; ++i) {
@@ -1555,8 +1607,9 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
     // S = Q K^T and dP = dA V^T: lane (key l16, g4) gets rows 16h + 4 g4 + r in
     // sc[h][r]; the statistics of rows 4 g4 .. and 16 + 4 g4 .. (lse, then Dt)
     f32x4 sc[2], dp[2], stt[4];
-    const uint32_t ad[4] = {lds_addr(sp + foff), lds_addr(sp + 16 * kRowT + foff),
-                            lds_addr(sp + kStage + foff), lds_addr(sp + kStage + 16 * kRowT + foff)};
+    uint32_t ad[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) ad[b] = lds_addr(sp) + cb[b];
     if (i + 1 < nb) {
       // block i+1's statistics (2 copies, lanes 0 and 1), then its Q and dA rows
       // from inside the chains
@@ -1571,12 +1624,12 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
       uint32_t mad[16];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        mad[u] = __builtin_amdgcn_readfirstlane(lds_addr(sq + (8 * W + u) * kRowT));
-        mad[8 + u] = __builtin_amdgcn_readfirstlane(lds_addr(sq + kStage + (8 * W + u) * kRowT));
+        mad[u] = __builtin_amdgcn_readfirstlane(lds_addr(sq + (8 * W + u) * kRow));
+        mad[8 + u] = __builtin_amdgcn_readfirstlane(lds_addr(sq + kStage + (8 * W + u) * kRow));
       }
       chains_keys_dma(sc[0], sc[1], dp[0], dp[1], ad, kf, vf, lds_addr(sp + 2 * kStage + 16 * g4),
                       stt, desc_words(a.q + n0 * kD, nr * 1024), desc_words(a.da + n0 * kD, nr * 1024),
-                      (uint32_t)lane16, soff, mad);
+                      vo, soff, mad);
     } else {
       chains_keys(sc[0], sc[1], dp[0], dp[1], ad, kf, vf, lds_addr(sp + 2 * kStage + 16 * g4), stt);
     }
@@ -1592,8 +1645,13 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
       dsb[i8] = (__bf16)(p * (dp[h][r] - stt[2 + h][r]));
     }
     // dV^T += dA^T P, dK^T += Q^T dS (transposing reads of the row tiles)
-    tr_keys(dv, lds_addr(sp + kStage + voff), lds_addr(sp + kStage + 16 * kRowT + voff), pb);
-    tr_keys(dk, lds_addr(sp + voff), lds_addr(sp + 16 * kRowT + voff), dsb);
+    uint32_t ta[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) ta[b] = lds_addr(sp + kStage) + tb[b];
+    tr_keys(dv, ta, pb);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) ta[b] = lds_addr(sp) + tb[b];
+    tr_keys(dk, ta, dsb);
   }
   mfma_drain();
   // lane (key l16, g4) holds dims 16 db + 4 g4 .. +3 of key l16
