@@ -53,6 +53,9 @@ def bind(lib):
                                              P, P, P, P, I]
     lib.hca_oracle_attn_backward_rows.argtypes = [P, P, P, P, I64, I64, P, P, P, P, I64, I, I, I,
                                                   I, D, P, P, I]
+    lib.hca_oracle_attn_lse.argtypes = [P, P, I64, P, I64, I64, P, I64, I, I, I, I, D, P, I]
+    lib.hca_oracle_attn_backward_saved.argtypes = [P, P, P, P, P, I64, P, P, P, P, I64, I, I, I,
+                                                   I, D, I, P, P, P, P, P, P, I]
     lib.hca_oracle_round_bf16.argtypes = [D]
     lib.hca_oracle_round_bf16.restype = ctypes.c_uint16
     lib.hca_oracle_widen_bf16.argtypes = [ctypes.c_uint16]
@@ -294,3 +297,60 @@ def attn_backward_rows(q, g, dout, positions, k, v, *, block=128, window=128, sc
         raise OracleError(f"hca_oracle_attn_backward_rows: {rc}")
     return dq, dg
 
+
+
+def attn_lse(q, tpos, k, kv_start, ck, *, block=128, window=128, scale=None, nthreads=0):
+    """Per-row log-sum-exp of the scores, ln sum_j exp(scale <q, key_j>) over the keys
+    each query sees (C ``hca_oracle_attn_lse``; the key list of ``attn``).
+      q [n, H, D], k [Tkv, D] (positions kv_start ..), ck [Nc, D]: bfloat16 bits
+    Returns float64 [n, H]."""
+    q, k = _u16(q), _u16(k)
+    n, H, D = q.shape
+    tpos = np.ascontiguousarray(tpos, dtype=np.int64)
+    assert tpos.shape == (n,) and k.shape[1] == D
+    ck = None if ck is None or len(ck) == 0 else _u16(ck)
+    Nc = 0 if ck is None else ck.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    lse = np.empty((n, H))
+    rc = _load().hca_oracle_attn_lse(_ptr(q), _ptr(tpos), n, _ptr(k), k.shape[0], int(kv_start),
+                                     _ptr(ck), Nc, H, D, block, window, float(scale), _ptr(lse),
+                                     int(nthreads))
+    if rc:
+        raise OracleError(f"hca_oracle_attn_lse: {rc}")
+    return lse
+
+
+def attn_backward_saved(q, g, dout, out, lse, k, v, *, round_da=False, block=128, window=128,
+                        scale=None, nthreads=0):
+    """Gradients of a whole-sequence prefill from the forward's saved gated output
+    ``out`` and row log-sum-exp ``lse`` (C ``hca_oracle_attn_backward_saved``: the
+    weights come from lse, D = <dout, out>); entry gradients pooled to their raw
+    rows as in ``attn_backward``.  With the exact out and lse and round_da off this
+    equals ``attn_backward``; round_da rounds dA = dout * sigmoid(g) to bfloat16.
+      q, g, dout [T, H, D], k, v [T, D]: bfloat16 bits;  out [T, H, D], lse [T, H]: float
+    Returns float64 (dq [T, H, D], dk [T, D], dv [T, D], dg [T, H, D])."""
+    q, g, dout, k, v = _u16(q), _u16(g), _u16(dout), _u16(k), _u16(v)
+    T, H, D = q.shape
+    out = np.ascontiguousarray(out, dtype=np.float64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    assert g.shape == q.shape == dout.shape == out.shape and lse.shape == (T, H)
+    assert k.shape == (T, D) == v.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    ck, cv = compress(k, block), compress(v, block)
+    Nc = ck.shape[0]
+    dq = np.empty((T, H, D)); dg = np.empty((T, H, D))
+    dk = np.empty((T, D)); dv = np.empty((T, D))
+    dck = np.zeros((max(Nc, 1), D)); dcv = np.zeros((max(Nc, 1), D))
+    rc = _load().hca_oracle_attn_backward_saved(
+        _ptr(q), _ptr(g), _ptr(dout), _ptr(out), _ptr(lse), T, _ptr(k), _ptr(v),
+        _ptr(ck) if Nc else None, _ptr(cv) if Nc else None, Nc, H, D, block, window,
+        float(scale), int(bool(round_da)), _ptr(dq), _ptr(dg), _ptr(dk), _ptr(dv), _ptr(dck),
+        _ptr(dcv), int(nthreads))
+    if rc:
+        raise OracleError(f"hca_oracle_attn_backward_saved: {rc}")
+    if Nc:
+        dk[:Nc * block] += np.repeat(dck[:Nc] / block, block, axis=0)
+        dv[:Nc * block] += np.repeat(dcv[:Nc] / block, block, axis=0)
+    return dq, dk, dv, dg

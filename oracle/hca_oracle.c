@@ -505,3 +505,190 @@ int hca_oracle_attn_backward_rows(const uint16_t *q, const uint16_t *g, const ui
     }
     return failed ? ORACLE_ENOMEM : 0;
 }
+
+/*
+ * Log-sum-exp of each row's scores (the statistic the forward keeps for the
+ * training pass): lse[i, h] = ln sum_j exp(scale <q[i, h], key_j>) over the keys
+ * query position tpos[i] sees (entries, then window rows, as in hca_oracle_attn).
+ *   q [n, H, D] bfloat16 bits;  lse [n, H] double
+ * The largest score is subtracted before exponentiating and added back.
+ */
+int hca_oracle_attn_lse(const uint16_t *q, const int64_t *tpos, int64_t n, const uint16_t *k,
+                        int64_t Tkv, int64_t kv_start, const uint16_t *ck, int64_t Nc, int H,
+                        int D, int block, int window, double scale, double *lse, int nthreads)
+{
+    if (!q || !tpos || !lse || n < 0 || H <= 0 || D <= 0 || block <= 0 || window <= 0 ||
+        Nc < 0 || Tkv < 0)
+        return ORACLE_EBADARG;
+    if ((Nc > 0 && !ck) || (Tkv > 0 && !k)) return ORACLE_EBADARG;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t t = tpos[i];
+        const int64_t first = t - window + 1 < 0 ? 0 : t - window + 1;
+        if (t < 0 || first < kv_start || t >= kv_start + Tkv) return ORACLE_ERANGE;
+    }
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    const int64_t cap = Nc + window;
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *sc = malloc(sizeof(*sc) * (size_t)cap);
+        if (!sc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp barrier
+        if (!failed) {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n * H; ++r) {
+                const int64_t t = tpos[r / H];
+                const uint16_t *qr = q + (size_t)r * D;
+                int64_t cnt = 0;
+                double top = -INFINITY;
+                /* entries b with b*block + block - 1 <= t, then raw positions */
+                const int64_t first = t - window + 1 < 0 ? 0 : t - window + 1;
+                for (int64_t j = 0; j < Nc + (t - first + 1); ++j) {
+                    const uint16_t *key;
+                    if (j < Nc) {
+                        if (j * block + block - 1 > t) continue;
+                        key = ck + j * D;
+                    } else {
+                        key = k + (first + (j - Nc) - kv_start) * D;
+                    }
+                    double acc = 0.0;
+                    for (int d = 0; d < D; ++d) acc += widen_bf16(qr[d]) * widen_bf16(key[d]);
+                    sc[cnt] = scale * acc;
+                    if (sc[cnt] > top) top = sc[cnt];
+                    ++cnt;
+                }
+                double sum = 0.0;
+                for (int64_t j = 0; j < cnt; ++j) sum += exp(sc[j] - top);
+                lse[r] = top + log(sum);
+            }
+        }
+        free(sc);
+    }
+    return failed ? ORACLE_ENOMEM : 0;
+}
+
+/*
+ * Backward from the forward's saved state, the way training frameworks run it:
+ * the caller keeps the gated output o and the per-row log-sum-exp lse of the
+ * forward, and for row (t, h)
+ *   p_j  = exp(scale <q, k_j> - lse)           (the row's attention weights)
+ *   D    = <dO, o>                              (= <dA, a>, since o = a sigmoid(g))
+ *   dA   = dO sigmoid(g), rounded to bfloat16 when round_da is set (the operand
+ *          the GPU kernels multiply)
+ *   ds_j = p_j (<dA, v_j> - D)
+ *   dq   = scale sum_j ds_j k_j,   dk_j += scale ds_j q,   dv_j += p_j dA
+ *   dg   = dO o (1 - sigmoid(g))               (= dO a s (1 - s))
+ * With the exact o and lse (and round_da off) this is the exact gradient of
+ * hca_oracle_attn_backward.  Arguments as there, plus o [T, H, D] and
+ * lse [T, H] (double).  Entry gradients go to dck, dcv (not pooled).
+ */
+static void saved_backward_row(const uint16_t *q, const uint16_t *g, const uint16_t *dout,
+                               const double *o, double lse, size_t off, int64_t t, int64_t T,
+                               const uint16_t *k, const uint16_t *v, const uint16_t *ck,
+                               const uint16_t *cv, int64_t Nc, int D, int block, int window,
+                               double scale, int round_da, double *dq, double *dg, double *gk,
+                               double *gv, double *dA)
+{
+    double dsum_o = 0.0;
+    for (int d = 0; d < D; ++d) {
+        const double s_g = 1.0 / (1.0 + exp(-widen_bf16(g[off + d])));
+        const double up = widen_bf16(dout[off + d]);
+        dsum_o += up * o[off + d];
+        dg[off + d] = up * o[off + d] * (1.0 - s_g);
+        dA[d] = round_da ? widen_bf16(round_bf16(up * s_g)) : up * s_g;
+        dq[off + d] = 0.0;
+    }
+    const int64_t w0 = t - window + 1 < 0 ? 0 : t - window + 1;
+    for (int64_t j = 0; j < Nc + (t - w0 + 1); ++j) {
+        const uint16_t *kr, *vr;
+        int64_t acc_row;
+        if (j < Nc) {
+            if (j * block + block - 1 > t) continue;
+            kr = ck + j * D;
+            vr = cv + j * D;
+            acc_row = T + j;
+        } else {
+            acc_row = w0 + (j - Nc);
+            kr = k + acc_row * D;
+            vr = v + acc_row * D;
+        }
+        double qk = 0.0, av = 0.0;
+        for (int d = 0; d < D; ++d) {
+            qk += widen_bf16(q[off + d]) * widen_bf16(kr[d]);
+            av += dA[d] * widen_bf16(vr[d]);
+        }
+        const double pj = exp(scale * qk - lse);
+        const double dsj = pj * (av - dsum_o);
+        for (int d = 0; d < D; ++d) {
+            dq[off + d] += scale * dsj * widen_bf16(kr[d]);
+            gk[(size_t)acc_row * D + d] += scale * dsj * widen_bf16(q[off + d]);
+            gv[(size_t)acc_row * D + d] += pj * dA[d];
+        }
+    }
+}
+
+int hca_oracle_attn_backward_saved(const uint16_t *q, const uint16_t *g, const uint16_t *dout,
+                                   const double *o, const double *lse, int64_t T,
+                                   const uint16_t *k, const uint16_t *v, const uint16_t *ck,
+                                   const uint16_t *cv, int64_t Nc, int H, int D, int block,
+                                   int window, double scale, int round_da, double *dq,
+                                   double *dg, double *dk, double *dv, double *dck, double *dcv,
+                                   int nthreads)
+{
+    if (!q || !g || !dout || !o || !lse || !k || !v || !dq || !dg || !dk || !dv || T < 0 ||
+        H <= 0 || D <= 0 || block <= 0 || window <= 0 || Nc < 0 || Nc > T / block)
+        return ORACLE_EBADARG;
+    if (Nc > 0 && (!ck || !cv || !dck || !dcv)) return ORACLE_EBADARG;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    if (nthreads > 8) nthreads = 8;
+    const size_t rows_acc = (size_t)(T + Nc) * D;  /* raw rows, then entries */
+    double *all_k = calloc((size_t)nthreads * rows_acc, sizeof(double));
+    double *all_v = calloc((size_t)nthreads * rows_acc, sizeof(double));
+    if (!all_k || !all_v) {
+        free(all_k);
+        free(all_v);
+        return ORACLE_ENOMEM;
+    }
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        const int me = omp_get_thread_num();
+        double *dA = malloc(sizeof(*dA) * (size_t)D);
+        if (!dA) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp barrier
+        if (!failed) {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < T * H; ++r)
+                saved_backward_row(q, g, dout, o, lse[r], (size_t)r * D, r / H, T, k, v, ck, cv,
+                                   Nc, D, block, window, scale, round_da, dq, dg,
+                                   all_k + (size_t)me * rows_acc, all_v + (size_t)me * rows_acc,
+                                   dA);
+        }
+        free(dA);
+    }
+    if (!failed) {
+        for (size_t i = 0; i < rows_acc; ++i) {
+            double tk = 0.0, tv = 0.0;
+            for (int th = 0; th < nthreads; ++th) {
+                tk += all_k[(size_t)th * rows_acc + i];
+                tv += all_v[(size_t)th * rows_acc + i];
+            }
+            if (i < (size_t)T * D) {
+                dk[i] = tk;
+                dv[i] = tv;
+            } else {
+                dck[i - (size_t)T * D] = tk;
+                dcv[i - (size_t)T * D] = tv;
+            }
+        }
+    }
+    free(all_k);
+    free(all_v);
+    return failed ? ORACLE_ENOMEM : 0;
+}

@@ -207,3 +207,146 @@ def test_key_gradient_sums():
     want_v = (dof / (1.0 + np.exp(-gf))).sum(axis=(0, 1))
     np.testing.assert_allclose(dv.sum(axis=0), want_v, rtol=1e-10, atol=1e-10)
     assert np.abs(dk.sum(axis=0)).max() <= 1e-10 * np.abs(dk).sum()
+
+
+# ---- the forward's row log-sum-exp and the backward from saved state
+
+
+def _dense_lse(q, tpos, k, kv_start, ck, block, window, scale):
+    """Brute force: scores against one dense key matrix with a boolean visibility
+    mask, then numpy's maximum-shifted log of the summed exponentials."""
+    kaug = np.concatenate([widen(k), widen(ck)], axis=0)
+    raw_pos = kv_start + np.arange(k.shape[0])
+    block_last = np.arange(ck.shape[0]) * block + (block - 1)
+    t = np.asarray(tpos, dtype=np.int64)[:, None]
+    vis = np.concatenate([(raw_pos[None] <= t) & (raw_pos[None] > t - window),
+                          block_last[None] <= t], axis=1)
+    s = scale * np.einsum("nhd,jd->nhj", widen(q), kaug)
+    s = np.where(vis[:, None, :], s, -np.inf)
+    top = s.max(axis=2)
+    return top + np.log(np.exp(s - top[..., None]).sum(axis=2))
+
+
+def test_lse_against_brute_force():
+    T, H, D = 45, 3, 8
+    q, _, _, k, _ = _inputs(31, T, H, D)
+    ck = oracle.compress(k, 4)
+    pos = np.arange(T)
+    got = oracle.attn_lse(q, pos, k, 0, ck, block=4, window=5, scale=0.4)
+    np.testing.assert_allclose(got, _dense_lse(q, pos, k, 0, ck, 4, 5, 0.4), rtol=1e-13,
+                               atol=1e-13)
+    # a chunk of later queries whose raw rows start past position 0
+    pos2 = np.arange(30, 45)
+    got2 = oracle.attn_lse(q[30:], pos2, k[26:], 26, ck, block=4, window=5, scale=0.4)
+    np.testing.assert_allclose(got2, got[30:], rtol=1e-13, atol=1e-13)
+
+
+def test_lse_of_zero_queries_counts_the_visible_keys():
+    # q = 0: every score is 0, so lse = ln(number of keys the row sees), which
+    # pins the two visibility rules at block and window edges
+    T, H, D, block, window = 50, 2, 8, 4, 6
+    q = np.zeros((T, H, D), np.uint16)
+    k = _dyadic(32, (T, D))
+    ck = oracle.compress(k, block)
+    lse = oracle.attn_lse(q, np.arange(T), k, 0, ck, block=block, window=window, scale=1.0)
+    for t in range(T):
+        n = min(t + 1, window) + (t + 1) // block
+        np.testing.assert_allclose(lse[t], np.log(n), rtol=0, atol=1e-14)
+
+
+def _exact_state(q, g, k, v, block, window, scale):
+    """The forward's exact gated output and row log-sum-exp (oracle, fp64)."""
+    T = q.shape[0]
+    ck, cv = oracle.compress(k, block), oracle.compress(v, block)
+    pos = np.arange(T)
+    out = oracle.attn(q, g, pos, k, v, 0, ck, cv, block=block, window=window, scale=scale)
+    lse = oracle.attn_lse(q, pos, k, 0, ck, block=block, window=window, scale=scale)
+    return out, lse
+
+
+def test_saved_state_backward_is_the_exact_gradient():
+    # with the exact output and log-sum-exp, D = <dO, o> = <dA, a> and the
+    # weights exp(x - lse) are the softmax: the exact gradients, which finite
+    # differences and torch autograd pin above
+    T, H, D, block, window, scale = 41, 2, 8, 4, 5, 0.35
+    q, g, do, k, v = _inputs(33, T, H, D)
+    out, lse = _exact_state(q, g, k, v, block, window, scale)
+    got = oracle.attn_backward_saved(q, g, do, out, lse, k, v, block=block, window=window,
+                                     scale=scale)
+    want = oracle.attn_backward(q, g, do, k, v, block=block, window=window, scale=scale)
+    for a, b, name in zip(got, want, ["dq", "dk", "dv", "dg"]):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_saved_state_closed_forms():
+    T, H, D, block, window, scale = 30, 2, 8, 4, 4, 0.3
+    q, g, do, k, v = _inputs(34, T, H, D)
+    out, lse = _exact_state(q, g, k, v, block, window, scale)
+    base = oracle.attn_backward_saved(q, g, do, out, lse, k, v, block=block, window=window,
+                                      scale=scale)
+    # lse raised by delta scales every weight, so dq, dk, dv, by exp(-delta);
+    # dg does not involve the weights
+    shifted = oracle.attn_backward_saved(q, g, do, out, lse + 0.5, k, v, block=block,
+                                         window=window, scale=scale)
+    for a, b in zip(shifted[:3], base[:3]):
+        np.testing.assert_allclose(a, b * np.exp(-0.5), rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(shifted[3], base[3])
+    # a gate of logit 40 has sigmoid exactly 1 in fp64: dA = dO is already a
+    # bfloat16 value, so rounding it changes nothing, and dg = dO o (1 - 1) = 0
+    g40 = np.full(q.shape, 0x4220, np.uint16)
+    plain = oracle.attn_backward_saved(q, g40, do, out, lse, k, v, block=block, window=window,
+                                       scale=scale)
+    rounded = oracle.attn_backward_saved(q, g40, do, out, lse, k, v, round_da=True, block=block,
+                                         window=window, scale=scale)
+    for a, b in zip(plain, rounded):
+        np.testing.assert_array_equal(a, b)
+    assert np.all(plain[3] == 0)
+    # rounding dA is the same as passing the rounded product as dout with that
+    # gate; dv = sum of weights times dA is the gradient that involves dA alone
+    gf, dof = widen(g), widen(do)
+    da_bits = synth.f64_to_bf16_bits(dof / (1.0 + np.exp(-gf)))
+    r1 = oracle.attn_backward_saved(q, g, do, out, lse, k, v, round_da=True, block=block,
+                                    window=window, scale=scale)
+    r2 = oracle.attn_backward_saved(q, g40, da_bits, out, lse, k, v, block=block, window=window,
+                                    scale=scale)
+    np.testing.assert_allclose(r1[2], r2[2], rtol=1e-12, atol=1e-14)
+
+
+SAVED_MUTANTS = {
+    "saved_d_from_da": ("dsum_o += up * o[off + d];", "dsum_o += up * s_g * o[off + d];"),
+    "saved_weights_ignore_lse": ("const double pj = exp(scale * qk - lse);",
+                                 "const double pj = exp(scale * qk);"),
+    "saved_gate_grad_with_sigmoid": ("dg[off + d] = up * o[off + d] * (1.0 - s_g);",
+                                     "dg[off + d] = up * o[off + d] * s_g * (1.0 - s_g);"),
+    "saved_dk_from_v": ("gk[(size_t)acc_row * D + d] += scale * dsj * widen_bf16(q[off + d]);",
+                        "gk[(size_t)acc_row * D + d] += scale * dsj * widen_bf16(vr[d]);"),
+    "saved_window_short": ("const int64_t w0 = t - window + 1 < 0 ? 0 : t - window + 1;",
+                           "const int64_t w0 = t - window + 2 < 0 ? 0 : t - window + 2;"),
+}
+
+
+@pytest.fixture()
+def saved_mutant(tmp_path, request, monkeypatch):
+    name = request.param
+    src = open(oracle.SRC).read()
+    old, new = SAVED_MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path_c = tmp_path / f"{name}.c"
+    path_c.write_text(src.replace(old, new))
+    path_so = tmp_path / f"{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared",
+                           "-ffp-contract=off", str(path_c), "-o", str(path_so), "-lm"])
+    monkeypatch.setattr(oracle, "_lib", oracle.bind(ctypes.CDLL(str(path_so))))
+    return name
+
+
+@pytest.mark.parametrize("saved_mutant", sorted(SAVED_MUTANTS), indirect=True)
+def test_saved_state_mutant_is_caught(saved_mutant):
+    T, H, D, block, window, scale = 23, 2, 8, 4, 4, 0.35
+    q, g, do, k, v = _inputs(35, T, H, D)
+    out, lse = _exact_state(q, g, k, v, block, window, scale)
+    got = oracle.attn_backward_saved(q, g, do, out, lse, k, v, block=block, window=window,
+                                     scale=scale)
+    want = oracle.attn_backward(q, g, do, k, v, block=block, window=window, scale=scale)
+    worst = max(float(np.abs(a - b).max() / np.abs(b).max()) for a, b in zip(got, want))
+    assert worst > 1e-6, saved_mutant
