@@ -109,6 +109,24 @@ hca_status_t hca_attn_prefill(const void* q, const void* g, const void* k, const
                               void* stream);
 
 /*
+ * Prefill attention that also keeps, for the training pass, each query row's
+ * log-sum-exp of its scores (the state hca_attn_backward_saved takes):
+ *   lse[t, h] = ln sum_j exp(scale <q[t, h], key_j>)   over the keys row (t, h) sees,
+ * as the kernel forms it: the weights exp(x_j - m) rounded to bfloat16 (the ones
+ * the value product uses) summed in fp32, then m + ln(sum); so lse is within
+ * ln(1 + 2^-8) of the exact value.
+ *   lse    device, f32 [Tq, H] (overwritten); not NULL when Tq > 0 (else
+ *          HCA_ERR_INVALID_ARG)
+ * Other arguments, requirements and the output out exactly as hca_attn_prefill
+ * (out is bitwise the same as hca_attn_prefill's).
+ */
+hca_status_t hca_attn_prefill_lse(const void* q, const void* g, const void* k, const void* v,
+                                  const void* ck, const void* cv, int64_t Tq, int64_t q_start,
+                                  int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D,
+                                  int block, int window, float scale, void* out,
+                                  hca_dtype_t out_dtype, float* lse, void* stream);
+
+/*
  * Prefill attention followed by the VHA head mix (virtual head attention:
  * blog.derekhsu.net, section 潛在閘控稀疏注意力, the VHA item: after attention a
  * light low-rank mix across heads with an identity skip, fused into the attention
@@ -270,6 +288,28 @@ hca_status_t hca_attn_backward(const void* q, const void* g, const void* k, cons
                                int D, int block, int window, float scale, void* dq, void* dk,
                                void* dv, void* dg, void* workspace, size_t ws_bytes,
                                void* stream);
+
+/*
+ * The same backward pass from the forward's saved state, as training frameworks
+ * run it: the forward's gated output out and row log-sum-exp lse (as
+ * hca_attn_prefill_lse writes them) replace the recomputed forward, so the row
+ * pass walks the keys once instead of twice.  For row (t, h):
+ *   p_j = exp(scale <q, k_j> - lse[t, h]),   Dt = <dout, out>  (= <da, a>),
+ *   dg = dout * out * (1 - s),   dq = scale * sum_j p_j (<da, v_j> - Dt) k_j,
+ * dk, dv and the entries' share as for hca_attn_backward.  With the exact out and
+ * lse these are the exact gradients; with a bf16 out, Dt carries its rounding
+ * (relative 2^-9 per element), the usual trade of a saved-state backward.
+ *   out       device, [T, H, D] bf16 or f32 (out_dtype)
+ *   lse       device, f32 [T, H]
+ * Other arguments, the workspace and the requirements as hca_attn_backward; out and
+ * lse must not be NULL when T > 0 (else HCA_ERR_INVALID_ARG).
+ */
+hca_status_t hca_attn_backward_saved(const void* q, const void* g, const void* k, const void* v,
+                                     const void* ck, const void* cv, const void* out,
+                                     hca_dtype_t out_dtype, const float* lse, const void* dout,
+                                     int64_t T, int H, int D, int block, int window, float scale,
+                                     void* dq, void* dk, void* dv, void* dg, void* workspace,
+                                     size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

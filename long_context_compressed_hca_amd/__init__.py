@@ -65,6 +65,12 @@ def lib():
         L.hca_attn_backward.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I, F, P, P, P, P, P,
                                         ctypes.c_size_t, P]
         L.hca_attn_backward.restype = I
+        L.hca_attn_prefill_lse.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, I,
+                                           F, P, I, P, P]
+        L.hca_attn_prefill_lse.restype = I
+        L.hca_attn_backward_saved.argtypes = [P, P, P, P, P, P, P, I, P, P, I64, I, I, I, I, F, P,
+                                              P, P, P, P, ctypes.c_size_t, P]
+        L.hca_attn_backward_saved.restype = I
         _lib = L
     return _lib
 
@@ -169,6 +175,28 @@ def hca_attn_prefill(q, g, k, v, ck, cv, out, *, q_start: int = 0, kv_start: int
         Tq, q_start, k.shape[0], kv_start, nc, H, Dd, block, window, float(scale),
         _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
         _stream(q.device)))
+
+
+def hca_attn_prefill_lse(q, g, k, v, ck, cv, out, lse, *, q_start: int = 0, kv_start: int = 0,
+                         scale: float | None = None, block: int = BLOCK, window: int = WINDOW):
+    """hca_attn_prefill, and lse [Tq, H] (float32) <- each row's log-sum-exp of its
+    scores (natural log), the state hca_attn_backward_saved takes."""
+    import torch
+    Tq, H, Dd = q.shape
+    nc = _check_prefill_shapes(q, g, k, v, ck, cv, out)
+    _expect(lse, (Tq, H), "lse")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _same_device(q, lse)
+    if scale is None:
+        scale = Dd ** -0.5
+    _check(lib().hca_attn_prefill_lse(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
+        _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+        _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
+        Tq, q_start, k.shape[0], kv_start, nc, H, Dd, block, window, float(scale),
+        _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
+        _dev_ptr(lse, "lse", torch.float32), _stream(q.device)))
 
 
 def _check_cache_shapes(B, Dd, ck, cv, wk, wv, pos, window) -> int:
@@ -350,6 +378,50 @@ def hca_attn_backward(q, g, k, v, ck, cv, dout, dq, dk, dv, dg, *, scale: float 
     a device uint8 tensor of at least backward_workspace_size(T, H) bytes; allocated
     here (through torch) when None."""
     import torch
+    T, H, Dd, scale, workspace, ws_bytes = _backward_args(q, g, k, v, ck, cv, dout, dq, dk, dv,
+                                                          dg, scale, workspace, block)
+    _check(lib().hca_attn_backward(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
+        _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+        _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
+        _dev_ptr(dout, "dout", torch.bfloat16), T, H, Dd, block, window, float(scale),
+        _dev_ptr(dq, "dq", torch.float32), _dev_ptr(dk, "dk", torch.float32),
+        _dev_ptr(dv, "dv", torch.float32), _dev_ptr(dg, "dg", torch.float32),
+        _dev_ptr(workspace, "workspace", optional=True), ws_bytes, _stream(q.device)))
+
+
+def hca_attn_backward_saved(q, g, k, v, ck, cv, out, lse, dout, dq, dk, dv, dg, *,
+                            scale: float | None = None, workspace=None, block: int = BLOCK,
+                            window: int = WINDOW):
+    """hca_attn_backward from the forward's saved state: its gated output out [T, H, 512]
+    (bfloat16 or float32) and row log-sum-exp lse [T, H] (float32), as
+    hca_attn_prefill_lse writes them."""
+    import torch
+    T, H, Dd, scale, workspace, ws_bytes = _backward_args(q, g, k, v, ck, cv, dout, dq, dk, dv,
+                                                          dg, scale, workspace, block)
+    _expect(out, q.shape, "out")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _expect(lse, (T, H), "lse")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _same_device(q, out, lse)
+    _check(lib().hca_attn_backward_saved(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
+        _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+        _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
+        _dev_ptr(out, "out"), HCA_F32 if out.dtype == torch.float32 else HCA_BF16,
+        _dev_ptr(lse, "lse", torch.float32), _dev_ptr(dout, "dout", torch.bfloat16), T, H, Dd,
+        block, window, float(scale), _dev_ptr(dq, "dq", torch.float32),
+        _dev_ptr(dk, "dk", torch.float32), _dev_ptr(dv, "dv", torch.float32),
+        _dev_ptr(dg, "dg", torch.float32), _dev_ptr(workspace, "workspace", optional=True),
+        ws_bytes, _stream(q.device)))
+
+
+def _backward_args(q, g, k, v, ck, cv, dout, dq, dk, dv, dg, scale, workspace, block):
+    """Shape, dtype and device checks shared by the backward entry points; returns
+    (T, H, D, scale, workspace, ws_bytes) with the workspace allocated if None."""
+    import torch
     if q.dim() != 3:
         raise ValueError("q must be [T, H, D]")
     T, H, Dd = q.shape
@@ -377,11 +449,4 @@ def hca_attn_backward(q, g, k, v, ck, cv, dout, dq, dk, dv, dg, *, scale: float 
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().hca_attn_backward(
-        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(g, "g", torch.bfloat16),
-        _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
-        _dev_ptr(ck, "ck", torch.bfloat16, True), _dev_ptr(cv, "cv", torch.bfloat16, True),
-        _dev_ptr(dout, "dout", torch.bfloat16), T, H, Dd, block, window, float(scale),
-        _dev_ptr(dq, "dq", torch.float32), _dev_ptr(dk, "dk", torch.float32),
-        _dev_ptr(dv, "dv", torch.float32), _dev_ptr(dg, "dg", torch.float32),
-        _dev_ptr(workspace, "workspace", optional=True), ws_bytes, _stream(q.device)))
+    return T, H, Dd, scale, workspace, ws_bytes

@@ -152,7 +152,8 @@ static hca_status_t prefill_impl(const void* q, const void* g, const void* k, co
                                  int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D,
                                  int block, int window, float scale, const void* vha_up,
                                  const void* vha_down, int vha_rank, void* out,
-                                 hca_dtype_t out_dtype, void* stream, const char* what) {
+                                 hca_dtype_t out_dtype, float* lse, void* stream,
+                                 const char* what) {
   TRY(check_shape(D, block, window));
   if (H < 1 || H > 64) return fail(HCA_ERR_UNSUPPORTED, "H = %d (need 1 <= H <= 64)", H);
   if (vha_rank != 0) {
@@ -194,6 +195,7 @@ static hca_status_t prefill_impl(const void* q, const void* g, const void* k, co
     TRY(check_ptr(vha_up, "vha_up"));
     TRY(check_ptr(vha_down, "vha_down"));
   }
+  if (lse != nullptr) TRY(check_ptr(lse, "lse"));
   hca::PrefillProblem p;
   p.q = static_cast<const uint16_t*>(q);
   p.g = static_cast<const uint16_t*>(g);
@@ -213,6 +215,7 @@ static hca_status_t prefill_impl(const void* q, const void* g, const void* k, co
   p.vha_up = static_cast<const uint16_t*>(vha_up);
   p.vha_down = static_cast<const uint16_t*>(vha_down);
   p.vha_rank = vha_rank;
+  p.lse = lse;
   return hip_status(hca::launch_prefill(p, static_cast<hipStream_t>(stream)), what);
 }
 
@@ -222,8 +225,19 @@ hca_status_t hca_attn_prefill(const void* q, const void* g, const void* k, const
                               int window, float scale, void* out, hca_dtype_t out_dtype,
                               void* stream) {
   return prefill_impl(q, g, k, v, ck, cv, Tq, q_start, Tkv, kv_start, Nc, H, D, block, window,
-                      scale, nullptr, nullptr, 0, out, out_dtype, stream,
+                      scale, nullptr, nullptr, 0, out, out_dtype, nullptr, stream,
                       "hca_attn_prefill launch");
+}
+
+hca_status_t hca_attn_prefill_lse(const void* q, const void* g, const void* k, const void* v,
+                                  const void* ck, const void* cv, int64_t Tq, int64_t q_start,
+                                  int64_t Tkv, int64_t kv_start, int64_t Nc, int H, int D,
+                                  int block, int window, float scale, void* out,
+                                  hca_dtype_t out_dtype, float* lse, void* stream) {
+  if (lse == nullptr && Tq > 0) return fail(HCA_ERR_INVALID_ARG, "lse is NULL");
+  return prefill_impl(q, g, k, v, ck, cv, Tq, q_start, Tkv, kv_start, Nc, H, D, block, window,
+                      scale, nullptr, nullptr, 0, out, out_dtype, lse, stream,
+                      "hca_attn_prefill_lse launch");
 }
 
 hca_status_t hca_attn_prefill_vha(const void* q, const void* g, const void* k, const void* v,
@@ -234,7 +248,7 @@ hca_status_t hca_attn_prefill_vha(const void* q, const void* g, const void* k, c
                                   hca_dtype_t out_dtype, void* stream) {
   if (vha_rank == 0) return fail(HCA_ERR_UNSUPPORTED, "VHA rank 0 (use hca_attn_prefill)");
   return prefill_impl(q, g, k, v, ck, cv, Tq, q_start, Tkv, kv_start, Nc, H, D, block, window,
-                      scale, vha_up, vha_down, vha_rank, out, out_dtype, stream,
+                      scale, vha_up, vha_down, vha_rank, out, out_dtype, nullptr, stream,
                       "hca_attn_prefill_vha launch");
 }
 
@@ -394,11 +408,12 @@ size_t hca_backward_workspace_size(int64_t T, int H, int D) {
   return hca::backward_workspace_bytes(T, H);
 }
 
-hca_status_t hca_attn_backward(const void* q, const void* g, const void* k, const void* v,
-                               const void* ck, const void* cv, const void* dout, int64_t T, int H,
-                               int D, int block, int window, float scale, void* dq, void* dk,
-                               void* dv, void* dg, void* workspace, size_t ws_bytes,
-                               void* stream) {
+static hca_status_t backward_impl(const void* q, const void* g, const void* k, const void* v,
+                                  const void* ck, const void* cv, const void* out,
+                                  hca_dtype_t out_dtype, const float* lse, const void* dout,
+                                  int64_t T, int H, int D, int block, int window, float scale,
+                                  void* dq, void* dk, void* dv, void* dg, void* workspace,
+                                  size_t ws_bytes, void* stream, bool saved, const char* what) {
   TRY(check_shape(D, block, window));
   if (T < 0) return fail(HCA_ERR_INVALID_ARG, "T = %lld < 0", (long long)T);
   if (H < 1 || H > 64) return fail(HCA_ERR_UNSUPPORTED, "H = %d (need 1 <= H <= 64)", H);
@@ -406,12 +421,18 @@ hca_status_t hca_attn_backward(const void* q, const void* g, const void* k, cons
     return fail(HCA_ERR_UNSUPPORTED, "T * H = %lld query rows (at most 2^31 - 1)",
                 (long long)(T * H));
   TRY(check_scale(scale));
+  if (saved && out_dtype != HCA_BF16 && out_dtype != HCA_F32)
+    return fail(HCA_ERR_INVALID_ARG, "unknown out_dtype %d", (int)out_dtype);
   if (T == 0) return ok();
   TRY(check_ptr(q, "q"));
   TRY(check_ptr(g, "g"));
   TRY(check_ptr(k, "k"));
   TRY(check_ptr(v, "v"));
   TRY(check_ptr(dout, "dout"));
+  if (saved) {
+    TRY(check_ptr(out, "out"));
+    TRY(check_ptr(lse, "lse"));
+  }
   TRY(check_ptr(dq, "dq"));
   TRY(check_ptr(dk, "dk"));
   TRY(check_ptr(dv, "dv"));
@@ -439,8 +460,33 @@ hca_status_t hca_attn_backward(const void* q, const void* g, const void* k, cons
   p.T = T;
   p.H = H;
   p.scale = scale;
-  return hip_status(hca::launch_backward(p, workspace, static_cast<hipStream_t>(stream)),
-                    "hca_attn_backward launch");
+  if (saved) {
+    p.out = out;
+    p.lse = lse;
+    p.out_f32 = out_dtype == HCA_F32;
+  }
+  return hip_status(hca::launch_backward(p, workspace, static_cast<hipStream_t>(stream)), what);
+}
+
+hca_status_t hca_attn_backward(const void* q, const void* g, const void* k, const void* v,
+                               const void* ck, const void* cv, const void* dout, int64_t T, int H,
+                               int D, int block, int window, float scale, void* dq, void* dk,
+                               void* dv, void* dg, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  return backward_impl(q, g, k, v, ck, cv, nullptr, HCA_BF16, nullptr, dout, T, H, D, block,
+                       window, scale, dq, dk, dv, dg, workspace, ws_bytes, stream, false,
+                       "hca_attn_backward launch");
+}
+
+hca_status_t hca_attn_backward_saved(const void* q, const void* g, const void* k, const void* v,
+                                     const void* ck, const void* cv, const void* out,
+                                     hca_dtype_t out_dtype, const float* lse, const void* dout,
+                                     int64_t T, int H, int D, int block, int window, float scale,
+                                     void* dq, void* dk, void* dv, void* dg, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  return backward_impl(q, g, k, v, ck, cv, out, out_dtype, lse, dout, T, H, D, block, window,
+                       scale, dq, dk, dv, dg, workspace, ws_bytes, stream, true,
+                       "hca_attn_backward_saved launch");
 }
 
 }  // extern "C"

@@ -68,6 +68,9 @@ struct BwArgs {
   float *dq, *dg, *dk, *dv;
   float *lse, *dt, *dck, *dcv;  // workspace: row statistics, entry gradients
   uint16_t* da;                 // workspace: dA rows, bf16 [T * H, 512]
+  const void* out;              // saved state: the forward's gated output (bf16 or f32)
+  const float* lse_in;          //   and its row log-sum-exp (natural log)
+  int out_f32;
   int64_t T;
   int H, Nc, n_rb;              // n_rb: blocks of kTile flat rows
   int n_ent_tasks, n_chunks;    // entry tasks = entry groups x chunks of kChunkRb row blocks
@@ -1277,6 +1280,10 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 }
 
 // ----------------------------------------------------------------- rows pass
+// kSaved: the forward's output o and row log-sum-exp are given, so there is no
+// pass A: Dt = <dO, o> (= <dA, a>), dg = dO o (1 - sigmoid(g)) and lse come
+// from the saved state in the loop that forms dA.
+template <bool kSaved>
 __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   // stage s (0, 1): the K rows of a 32-key tile at lds + 2 s kStage, its V rows after them
   __shared__ __attribute__((aligned(256))) uint8_t lds[4 * kStage];
@@ -1300,18 +1307,39 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   // dA = dout * sigmoid(g) depends on the inputs alone: rounded to bf16 and
   // stored first (the key kernel reads it too), then read back as the B
   // operand of dP^T = V dA^T.  Lane (row l16, g4) handles dims 16 db + 4 g4.
+  // With the saved state the same loop forms dg and the lane's part of <dO, o>.
   const __amdgpu_buffer_rsrc_t rda = make_rsrc(a.da + r0 * kD, nr * 1024);
+  float dsum = 0.0f;
 #pragma unroll 4
   for (int db = 0; db < 32; ++db) {
     const int d0 = 16 * db + 4 * g4;
     const uint2 g2 = *reinterpret_cast<const uint2*>(a.g + ro + d0);
     const uint2 o2 = *reinterpret_cast<const uint2*>(a.dout + ro + d0);
-    const u32x2 w2 = {
-        pack_bf16x2(bf16_bits_to_f32(o2.x & 0xFFFFu) * sigmoid(bf16_bits_to_f32(g2.x & 0xFFFFu)),
-                    bf16_bits_to_f32(o2.x >> 16) * sigmoid(bf16_bits_to_f32(g2.x >> 16))),
-        pack_bf16x2(bf16_bits_to_f32(o2.y & 0xFFFFu) * sigmoid(bf16_bits_to_f32(g2.y & 0xFFFFu)),
-                    bf16_bits_to_f32(o2.y >> 16) * sigmoid(bf16_bits_to_f32(g2.y >> 16)))};
+    const float dov[4] = {bf16_bits_to_f32(o2.x & 0xFFFFu), bf16_bits_to_f32(o2.x >> 16),
+                          bf16_bits_to_f32(o2.y & 0xFFFFu), bf16_bits_to_f32(o2.y >> 16)};
+    const float sg[4] = {sigmoid(bf16_bits_to_f32(g2.x & 0xFFFFu)), sigmoid(bf16_bits_to_f32(g2.x >> 16)),
+                         sigmoid(bf16_bits_to_f32(g2.y & 0xFFFFu)), sigmoid(bf16_bits_to_f32(g2.y >> 16))};
+    const u32x2 w2 = {pack_bf16x2(dov[0] * sg[0], dov[1] * sg[1]),
+                      pack_bf16x2(dov[2] * sg[2], dov[3] * sg[3])};
     __builtin_amdgcn_raw_buffer_store_b64(w2, rda, l16 * 1024 + 2 * d0, 0, 0);
+    if constexpr (kSaved) {
+      float ov[4];
+      if (a.out_f32) {
+        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + ro + d0);
+        ov[0] = f.x; ov[1] = f.y; ov[2] = f.z; ov[3] = f.w;
+      } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.out) + ro + d0);
+        ov[0] = bf16_bits_to_f32(u.x & 0xFFFFu); ov[1] = bf16_bits_to_f32(u.x >> 16);
+        ov[2] = bf16_bits_to_f32(u.y & 0xFFFFu); ov[3] = bf16_bits_to_f32(u.y >> 16);
+      }
+      float dgv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum += dov[e] * ov[e];
+        dgv[e] = dov[e] * ov[e] * (1.0f - sg[e]);
+      }
+      if (valid) *reinterpret_cast<float4*>(a.dg + ro + d0) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
+    }
   }
   wait_vm<0>();  // the stores have reached L2 (the loads below bypass L1)
   bf16x8 daf[16], qf[16];
@@ -1381,6 +1409,15 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   // V as fragments and transposed.  Keys 16h + 4 g4 + r of a tile are in
   // sc[h][r] (h = 0, 1).
   f32x4 o[32];
+  float lse, dt;  // row statistics: log-sum-exp in base-2 score units, Dt = <dA, a>
+  if constexpr (kSaved) {
+    dt = xsum32(xsum16(dsum));
+    lse = a.lse_in[rmy] * 1.4426950408889634f;
+    if (valid && g4 == 0) {  // the key kernel reads them from the workspace
+      a.lse[rmy] = lse;
+      a.dt[rmy] = dt;
+    }
+  } else {
   float m = -INFINITY, mseen = -INFINITY, l = 0.0f, lb = 0.0f, ldp = 0.0f;
   bool fixed_m = false;
   for (int pass = 0;; ++pass) {
@@ -1445,8 +1482,8 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   // ---- row statistics and dg
   const float lrow = xsum32(xsum16(l));
   const float inv_b = 1.0f / xsum32(xsum16(lb));
-  const float lse = m + __builtin_amdgcn_logf(lrow);  // base 2: p_j = 2^(x_j - lse)
-  const float dt = xsum32(xsum16(ldp)) / lrow;
+  lse = m + __builtin_amdgcn_logf(lrow);  // base 2: p_j = 2^(x_j - lse)
+  dt = xsum32(xsum16(ldp)) / lrow;
   if (valid && g4 == 0) {
     a.lse[rmy] = lse;
     a.dt[rmy] = dt;
@@ -1468,6 +1505,7 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
     }
     if (valid) *reinterpret_cast<float4*>(a.dg + ro + d0) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
   }
+  }  // recompute (no saved state)
 
   // ---- pass B: dq.  K is read as fragments and transposed, V as fragments.
 #pragma unroll
@@ -1720,6 +1758,7 @@ hipError_t launch_backward(const BackwardProblem& p, void* ws, hipStream_t strea
   BwArgs a;
   a.q = p.q; a.g = p.g; a.k = p.k; a.v = p.v; a.ck = p.ck; a.cv = p.cv; a.dout = p.dout;
   a.dq = p.dq; a.dg = p.dg; a.dk = p.dk; a.dv = p.dv;
+  a.out = p.out; a.lse_in = p.lse; a.out_f32 = p.out_f32 ? 1 : 0;
   a.T = p.T;
   a.H = p.H;
   a.Nc = (int)(p.T / kBlock);
@@ -1745,8 +1784,11 @@ hipError_t launch_backward(const BackwardProblem& p, void* ws, hipStream_t strea
     hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, a.dck, (int64_t)a.Nc * kD);
     hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, a.dcv, (int64_t)a.Nc * kD);
   }
-  hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((rows + kRowsPerWg - 1) / kRowsPerWg)), dim3(256),
-                     0, stream, a);
+  const dim3 rows_grid((unsigned)((rows + kRowsPerWg - 1) / kRowsPerWg));
+  if (p.out != nullptr)
+    hipLaunchKernelGGL(rows_kernel<true>, rows_grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(rows_kernel<false>, rows_grid, dim3(256), 0, stream, a);
   const int64_t raw_tasks = (p.T + kKeysPerWg - 1) / kKeysPerWg;
   hipLaunchKernelGGL(keys_kernel, dim3((unsigned)(a.n_ent_tasks + raw_tasks)), dim3(256), 0, stream,
                      a);

@@ -33,6 +33,8 @@ struct PrefillProblem {
   const uint16_t* vha_up = nullptr;
   const uint16_t* vha_down = nullptr;
   int vha_rank = 0;
+  // Optional [Tq, H] fp32: each row's log-sum-exp ln sum_j exp(scale <q, k_j>).
+  float* lse = nullptr;
 };
 hipError_t launch_prefill(const PrefillProblem& p, hipStream_t stream);
 
@@ -85,6 +87,12 @@ struct BackwardProblem {
   int64_t T;
   int H;
   float scale;
+  // Optional saved state of the forward: its gated output [T, H, 512] (bf16, or
+  // f32 if out_f32) and row log-sum-exp [T, H] (natural log).  Given, the row
+  // statistics come from them instead of a recomputed forward.
+  const void* out = nullptr;
+  const float* lse = nullptr;
+  bool out_f32 = false;
 };
 size_t backward_workspace_bytes(int64_t T, int H);
 hipError_t launch_backward(const BackwardProblem& p, void* ws, hipStream_t stream);

@@ -99,6 +99,9 @@ struct Args {
   const uint16_t* vha_up;
   const uint16_t* vha_down;
   int vha_rank;
+  // Optional [Tq * H]: each row's log-sum-exp of its scores (natural log), the
+  // statistic a training pass keeps for the backward.
+  float* lse;
 };
 
 // Row -> query index (row / H), a shift when H is a power of two.
@@ -879,7 +882,7 @@ __device__ __forceinline__ void vha_query(const Args& a, WaveState& st, const It
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool kF32, bool kVha>
+template <bool kF32, bool kVha, bool kLse>
 __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
   // Separate arrays per stage: the compiler then knows a copy into one stage
   // cannot alias reads of another and inserts no wait between them.
@@ -1058,6 +1061,11 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
     {
       const float l_tot = st.l + __shfl_xor(st.l, 32);
       if (lane < 32) sL[wave * 32 + lane] = l_tot;
+      // log-sum-exp of row 32 wave + lane: the weights are 2^(x - m), x the
+      // scores in base-2 units, so ln sum = (m + log2 l) ln 2
+      if (kLse && lane < 32 && it.row0 + wave * 32 + lane <= it.last)
+        a.lse[it.row0 + wave * 32 + lane] =
+            (st.m + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
     }
     {
       int ln = lane;
@@ -1134,6 +1142,7 @@ hipError_t launch_prefill(const PrefillProblem& p, hipStream_t stream) {
   a.vha_up = p.vha_up;
   a.vha_down = p.vha_down;
   a.vha_rank = p.vha_rank;
+  a.lse = p.lse;
   a.n_items = (a.rows + kRowsPerItem - 1) / kRowsPerItem;
   if (a.n_items == 0) return hipSuccess;
   int dev = 0;
@@ -1157,14 +1166,20 @@ hipError_t launch_prefill(const PrefillProblem& p, hipStream_t stream) {
   const bool vha = p.vha_rank > 0;
   if (vha && p.H != 64) return hipErrorInvalidValue;
   const dim3 grid(8 * per_xcd), block(256);
-  if (a.out_f32 && vha)
-    hipLaunchKernelGGL((prefill_kernel<true, true>), grid, block, 0, stream, a);
+  // The row log-sum-exp is written by its own variants (not with the mix).
+  if (a.lse != nullptr && vha) return hipErrorInvalidValue;
+  if (a.lse != nullptr && a.out_f32)
+    hipLaunchKernelGGL((prefill_kernel<true, false, true>), grid, block, 0, stream, a);
+  else if (a.lse != nullptr)
+    hipLaunchKernelGGL((prefill_kernel<false, false, true>), grid, block, 0, stream, a);
+  else if (a.out_f32 && vha)
+    hipLaunchKernelGGL((prefill_kernel<true, true, false>), grid, block, 0, stream, a);
   else if (a.out_f32)
-    hipLaunchKernelGGL((prefill_kernel<true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<true, false, false>), grid, block, 0, stream, a);
   else if (vha)
-    hipLaunchKernelGGL((prefill_kernel<false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<false, true, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<false, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<false, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -106,7 +106,21 @@ int main() {
                            bneed, nullptr), HCA_ERR_INVALID_ARG);
   EXPECT(hca_attn_backward(nullptr, P, P, P, P, P, P, 0, 64, 512, 128, 128, sc, nullptr, P, P, P,
                            nullptr, 0, nullptr), HCA_OK);
-  if (g_launches < 11) ++failures;
+  // saved-state training pair: prefill with the row log-sum-exp, backward from it
+  float* L = reinterpret_cast<float*>(0x30000);
+  EXPECT(hca_attn_prefill_lse(P, P, P, P, P, P, 256, 0, 256, 0, 2, 64, 512, 128, 128, sc, P,
+                              HCA_BF16, L, nullptr), HCA_OK);
+  EXPECT(hca_attn_prefill_lse(P, P, P, P, P, P, 256, 0, 256, 0, 2, 64, 512, 128, 128, sc, P,
+                              HCA_BF16, nullptr, nullptr), HCA_ERR_INVALID_ARG);
+  EXPECT(hca_attn_prefill_lse(P, P, P, P, P, P, 0, 0, 0, 0, 0, 64, 512, 128, 128, sc, nullptr,
+                              HCA_BF16, nullptr, nullptr), HCA_OK);
+  EXPECT(hca_attn_backward_saved(P, P, P, P, P, P, P, HCA_F32, L, P, 1000, 64, 512, 128, 128, sc,
+                                 P, P, P, P, P, bneed, nullptr), HCA_OK);
+  EXPECT(hca_attn_backward_saved(P, P, P, P, P, P, nullptr, HCA_BF16, L, P, 1000, 64, 512, 128,
+                                 128, sc, P, P, P, P, P, bneed, nullptr), HCA_ERR_INVALID_ARG);
+  EXPECT(hca_attn_backward_saved(P, P, P, P, P, P, P, HCA_BF16, L, P, 1000, 64, 512, 128, 128, sc,
+                                 P, P, P, P, P, 16, nullptr), HCA_ERR_WORKSPACE);
+  if (g_launches < 13) ++failures;
   if (hca_version() < 100) ++failures;
   std::printf("api sanitizer run: %d failures, %d stub launches\n", failures, g_launches);
   return failures == 0 ? 0 : 1;

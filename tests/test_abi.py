@@ -91,6 +91,29 @@ def test_prefill_noop_and_optional_entries(L):
     assert b"out" in L.hca_last_error()
 
 
+def prefill_lse(L, **kw):
+    a = dict(q=P, g=P, k=P, v=P, ck=P, cv=P, Tq=256, q_start=0, Tkv=256, kv_start=0, Nc=2, H=64,
+             D=512, block=128, window=128, scale=512 ** -0.5, out=P, dtype=0, lse=P, stream=None)
+    a.update(kw)
+    return L.hca_attn_prefill_lse(a["q"], a["g"], a["k"], a["v"], a["ck"], a["cv"], a["Tq"],
+                                  a["q_start"], a["Tkv"], a["kv_start"], a["Nc"], a["H"], a["D"],
+                                  a["block"], a["window"], a["scale"], a["out"], a["dtype"],
+                                  a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=0), INVALID), (dict(lse=P + 2), INVALID), (dict(H=65), UNSUPPORTED),
+    (dict(dtype=3), INVALID), (dict(Nc=1), INVALID), (dict(q=0), INVALID),
+])
+def test_prefill_lse_rejects(L, kw, status):
+    assert prefill_lse(L, **kw) == status
+    assert L.hca_last_error()
+
+
+def test_prefill_lse_noop(L):
+    assert prefill_lse(L, Tq=0, q=0, out=0, lse=0) == OK
+
+
 def prefill_vha(L, **kw):
     a = dict(q=P, g=P, k=P, v=P, ck=P, cv=P, Tq=256, q_start=0, Tkv=256, kv_start=0, Nc=2, H=64,
              D=512, block=128, window=128, scale=512 ** -0.5, up=P, down=P, rank=8, out=P,
@@ -235,6 +258,31 @@ def test_backward_noop_and_optional_entries(L):
     # below one block there are no entries: ck, cv may be NULL (rejected later for
     # the missing workspace, so nothing is launched)
     assert backward(L, T=100, ck=0, cv=0, ws=None, ws_bytes=0) == WORKSPACE
+
+
+def backward_saved(L, **kw):
+    a = dict(q=P, g=P, k=P, v=P, ck=P, cv=P, out=P, dtype=0, lse=P, dout=P, T=1000, H=64, D=512,
+             block=128, window=128, scale=512 ** -0.5, dq=P, dk=P, dv=P, dg=P, ws=P,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.hca_attn_backward_saved(a["q"], a["g"], a["k"], a["v"], a["ck"], a["cv"], a["out"],
+                                     a["dtype"], a["lse"], a["dout"], a["T"], a["H"], a["D"],
+                                     a["block"], a["window"], a["scale"], a["dq"], a["dk"],
+                                     a["dv"], a["dg"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=0), INVALID), (dict(out=MIS), INVALID), (dict(lse=0), INVALID),
+    (dict(lse=P + 2), INVALID), (dict(dtype=2), INVALID), (dict(H=65), UNSUPPORTED),
+    (dict(T=-1), INVALID), (dict(ck=0), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(ws_bytes=1000), WORKSPACE),
+])
+def test_backward_saved_rejects(L, kw, status):
+    assert backward_saved(L, **kw) == status
+
+
+def test_backward_saved_noop(L):
+    assert backward_saved(L, T=0, q=0, out=0, lse=0, ws=None, ws_bytes=0) == OK
 
 
 def test_backward_workspace_size(L):
