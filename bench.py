@@ -220,10 +220,11 @@ def backward_pairs(T: int, H: int) -> int:
     return H * visible_keys(0, T)
 
 
-def w_backward(torch, hca, synth, T, H=64):
+def w_backward(torch, hca, synth, T, H=64, saved=False):
     """Backward pass of a whole-sequence prefill (T tokens, 64 heads): fp32 dq, dk,
     dv, dg.  Algorithmic FLOPs: 5 products of 2 * 512 per (query row, visible key)
-    pair (scores, dP, dV, dK, dQ), 2.5 times the forward's."""
+    pair (scores, dP, dV, dK, dQ), 2.5 times the forward's.  saved: from the
+    forward's output and row log-sum-exp (hca_attn_prefill_lse, run once before)."""
     dev = torch.device("cuda:0")
     gen = _gen(synth, torch, 7)
     q, g, do = gen(synth.Q, (T, H, D)), gen(synth.G, (T, H, D)), gen(12, (T, H, D))
@@ -236,11 +237,21 @@ def w_backward(torch, hca, synth, T, H=64):
     dq, dg = torch.empty((T, H, D), **f32), torch.empty((T, H, D), **f32)
     dk, dv = torch.empty((T, D), **f32), torch.empty((T, D), **f32)
     ws = torch.empty(hca.backward_workspace_size(T, H), dtype=torch.uint8, device=dev)
+    if saved:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, H), **f32)
+        hca.hca_attn_prefill_lse(q, g, k, v, ck, cv, out, lse)
 
-    def call():
-        hca.hca_attn_backward(q, g, k, v, ck, cv, do, dq, dk, dv, dg, workspace=ws)
+        def call():
+            hca.hca_attn_backward_saved(q, g, k, v, ck, cv, out, lse, do, dq, dk, dv, dg,
+                                        workspace=ws)
+    else:
+        def call():
+            hca.hca_attn_backward(q, g, k, v, ck, cv, do, dq, dk, dv, dg, workspace=ws)
 
     nbytes = 3 * T * H * D * 2 + 2 * T * H * D * 4 + 2 * T * D * (2 + 4) + 2 * Nc * D * 2
+    if saved:
+        nbytes += T * H * (D * 2 + 4)
     return dict(call=call, kernels=[("zero_kernel", 2), ("rows_kernel", 1), ("keys_kernel", 1),
                                     ("pool_kernel", 1)],
                 src=["backward.hip"], flops=10.0 * D * backward_pairs(T, H), bytes=nbytes)
@@ -268,6 +279,12 @@ def workload_table(torch, hca, synth):
          lambda: w_backward(torch, hca, synth, 8192)),
         ("backward_128k", "HCA backward (dq, dk, dv, dg in fp32): T=131072, 64 heads, dim 512",
          lambda: w_backward(torch, hca, synth, 131072)),
+        ("backward_saved_8k", "HCA backward from the forward's saved output and row "
+         "log-sum-exp: T=8192, 64 heads, dim 512",
+         lambda: w_backward(torch, hca, synth, 8192, saved=True)),
+        ("backward_saved_128k", "HCA backward from the forward's saved output and row "
+         "log-sum-exp: T=131072, 64 heads, dim 512",
+         lambda: w_backward(torch, hca, synth, 131072, saved=True)),
     ]
 
 
@@ -371,7 +388,7 @@ def counters_workload(torch, hca, synth, reps: int):
     dev = torch.device("cuda:0")
     built = []
     for name, what, build in workload_table(torch, hca, synth):
-        if name == "backward_128k":
+        if name in ("backward_128k", "backward_saved_128k"):
             continue
         built.append((name, build()))
         if name == "prefill_8k":

@@ -123,8 +123,10 @@ __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 1
 // one half of the ring are in flight while the other half's MFMAs issue, and a
 // group is refilled only after the MFMA reading it has issued and the reads in
 // between have been waited for.  Accumulators in AGPRs.  tr_rows: a ring of 16
-// groups in v192 .. v255; tr_keys: 8 groups in v224 .. v255 (the key kernel
-// keeps its K and V fragments in VGPRs).
+// groups in v192 .. v255.  tr_keys2: both products of the key kernel in one
+// block, o += (the stage's second tile)^T p then w += (its first tile)^T r,
+// through 8 groups in v224 .. v255 (the key kernel keeps its K and V fragments
+// in VGPRs), so the second product's reads overlap the first one's MFMAs.
 __device__ __forceinline__ void tr_rows(f32x4 (&o)[32], const uint32_t (&ta)[8], const bf16x8& p) {
   asm volatile(
       "ds_read_b64_tr_b16 v[192:193], %[t0] offset:0\n\t"
@@ -242,8 +244,115 @@ __device__ __forceinline__ void tr_rows(f32x4 (&o)[32], const uint32_t (&ta)[8],
         [p] "v"(p)
       : "memory", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
 }
-__device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8], const bf16x8& p) {
+__device__ __forceinline__ void tr_keys2(f32x4 (&o)[32], f32x4 (&w)[32], const uint32_t (&ta)[8], const bf16x8& p, const bf16x8& r) {
   asm volatile(
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:36864\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:55296\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:36864\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:55296\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:36864\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:55296\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:36864\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:55296\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:36864\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:55296\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:36864\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:55296\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:36864\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:55296\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:36864\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:55296\n\t"
+      "s_waitcnt lgkmcnt(8)\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o0], v[224:227], %[p], %[o0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o1], v[228:231], %[p], %[o1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o2], v[232:235], %[p], %[o2]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o3], v[236:239], %[p], %[o3]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:37120\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:55552\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:37120\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:55552\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:37120\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:55552\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:37120\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:55552\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o4], v[240:243], %[p], %[o4]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o5], v[244:247], %[p], %[o5]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o6], v[248:251], %[p], %[o6]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o7], v[252:255], %[p], %[o7]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:37120\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:55552\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:37120\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:55552\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:37120\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:55552\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:37120\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:55552\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o8], v[224:227], %[p], %[o8]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o9], v[228:231], %[p], %[o9]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o10], v[232:235], %[p], %[o10]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o11], v[236:239], %[p], %[o11]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:37376\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:55808\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:37376\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:55808\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:37376\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:55808\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:37376\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:55808\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o12], v[240:243], %[p], %[o12]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o13], v[244:247], %[p], %[o13]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o14], v[248:251], %[p], %[o14]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o15], v[252:255], %[p], %[o15]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:37376\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:55808\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:37376\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:55808\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:37376\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:55808\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:37376\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:55808\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o16], v[224:227], %[p], %[o16]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o17], v[228:231], %[p], %[o17]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o18], v[232:235], %[p], %[o18]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o19], v[236:239], %[p], %[o19]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[224:225], %[t0] offset:37632\n\t"
+      "ds_read_b64_tr_b16 v[226:227], %[t0] offset:56064\n\t"
+      "ds_read_b64_tr_b16 v[228:229], %[t1] offset:37632\n\t"
+      "ds_read_b64_tr_b16 v[230:231], %[t1] offset:56064\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[t2] offset:37632\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[t2] offset:56064\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[t3] offset:37632\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[t3] offset:56064\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o20], v[240:243], %[p], %[o20]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o21], v[244:247], %[p], %[o21]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o22], v[248:251], %[p], %[o22]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o23], v[252:255], %[p], %[o23]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[t4] offset:37632\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[t4] offset:56064\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[t5] offset:37632\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[t5] offset:56064\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[t6] offset:37632\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[t6] offset:56064\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[t7] offset:37632\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[t7] offset:56064\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o24], v[224:227], %[p], %[o24]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o25], v[228:231], %[p], %[o25]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o26], v[232:235], %[p], %[o26]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o27], v[236:239], %[p], %[o27]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
       "ds_read_b64_tr_b16 v[224:225], %[t0] offset:0\n\t"
       "ds_read_b64_tr_b16 v[226:227], %[t0] offset:18432\n\t"
       "ds_read_b64_tr_b16 v[228:229], %[t1] offset:0\n\t"
@@ -252,6 +361,12 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
       "ds_read_b64_tr_b16 v[234:235], %[t2] offset:18432\n\t"
       "ds_read_b64_tr_b16 v[236:237], %[t3] offset:0\n\t"
       "ds_read_b64_tr_b16 v[238:239], %[t3] offset:18432\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o28], v[240:243], %[p], %[o28]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o29], v[244:247], %[p], %[o29]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o30], v[248:251], %[p], %[o30]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[o31], v[252:255], %[p], %[o31]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 7\n\t"
       "ds_read_b64_tr_b16 v[240:241], %[t4] offset:0\n\t"
       "ds_read_b64_tr_b16 v[242:243], %[t4] offset:18432\n\t"
       "ds_read_b64_tr_b16 v[244:245], %[t5] offset:0\n\t"
@@ -260,11 +375,10 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
       "ds_read_b64_tr_b16 v[250:251], %[t6] offset:18432\n\t"
       "ds_read_b64_tr_b16 v[252:253], %[t7] offset:0\n\t"
       "ds_read_b64_tr_b16 v[254:255], %[t7] offset:18432\n\t"
-      "s_waitcnt lgkmcnt(8)\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o0], v[224:227], %[p], %[o0]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o1], v[228:231], %[p], %[o1]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o2], v[232:235], %[p], %[o2]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o3], v[236:239], %[p], %[o3]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w0], v[224:227], %[r], %[w0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w1], v[228:231], %[r], %[w1]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w2], v[232:235], %[r], %[w2]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w3], v[236:239], %[r], %[w3]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b64_tr_b16 v[224:225], %[t0] offset:256\n\t"
@@ -275,10 +389,10 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
       "ds_read_b64_tr_b16 v[234:235], %[t2] offset:18688\n\t"
       "ds_read_b64_tr_b16 v[236:237], %[t3] offset:256\n\t"
       "ds_read_b64_tr_b16 v[238:239], %[t3] offset:18688\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o4], v[240:243], %[p], %[o4]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o5], v[244:247], %[p], %[o5]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o6], v[248:251], %[p], %[o6]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o7], v[252:255], %[p], %[o7]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w4], v[240:243], %[r], %[w4]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w5], v[244:247], %[r], %[w5]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w6], v[248:251], %[r], %[w6]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w7], v[252:255], %[r], %[w7]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b64_tr_b16 v[240:241], %[t4] offset:256\n\t"
@@ -289,10 +403,10 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
       "ds_read_b64_tr_b16 v[250:251], %[t6] offset:18688\n\t"
       "ds_read_b64_tr_b16 v[252:253], %[t7] offset:256\n\t"
       "ds_read_b64_tr_b16 v[254:255], %[t7] offset:18688\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o8], v[224:227], %[p], %[o8]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o9], v[228:231], %[p], %[o9]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o10], v[232:235], %[p], %[o10]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o11], v[236:239], %[p], %[o11]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w8], v[224:227], %[r], %[w8]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w9], v[228:231], %[r], %[w9]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w10], v[232:235], %[r], %[w10]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w11], v[236:239], %[r], %[w11]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b64_tr_b16 v[224:225], %[t0] offset:512\n\t"
@@ -303,10 +417,10 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
       "ds_read_b64_tr_b16 v[234:235], %[t2] offset:18944\n\t"
       "ds_read_b64_tr_b16 v[236:237], %[t3] offset:512\n\t"
       "ds_read_b64_tr_b16 v[238:239], %[t3] offset:18944\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o12], v[240:243], %[p], %[o12]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o13], v[244:247], %[p], %[o13]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o14], v[248:251], %[p], %[o14]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o15], v[252:255], %[p], %[o15]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w12], v[240:243], %[r], %[w12]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w13], v[244:247], %[r], %[w13]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w14], v[248:251], %[r], %[w14]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w15], v[252:255], %[r], %[w15]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b64_tr_b16 v[240:241], %[t4] offset:512\n\t"
@@ -317,10 +431,10 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
       "ds_read_b64_tr_b16 v[250:251], %[t6] offset:18944\n\t"
       "ds_read_b64_tr_b16 v[252:253], %[t7] offset:512\n\t"
       "ds_read_b64_tr_b16 v[254:255], %[t7] offset:18944\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o16], v[224:227], %[p], %[o16]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o17], v[228:231], %[p], %[o17]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o18], v[232:235], %[p], %[o18]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o19], v[236:239], %[p], %[o19]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w16], v[224:227], %[r], %[w16]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w17], v[228:231], %[r], %[w17]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w18], v[232:235], %[r], %[w18]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w19], v[236:239], %[r], %[w19]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b64_tr_b16 v[224:225], %[t0] offset:768\n\t"
@@ -331,10 +445,10 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
       "ds_read_b64_tr_b16 v[234:235], %[t2] offset:19200\n\t"
       "ds_read_b64_tr_b16 v[236:237], %[t3] offset:768\n\t"
       "ds_read_b64_tr_b16 v[238:239], %[t3] offset:19200\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o20], v[240:243], %[p], %[o20]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o21], v[244:247], %[p], %[o21]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o22], v[248:251], %[p], %[o22]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o23], v[252:255], %[p], %[o23]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w20], v[240:243], %[r], %[w20]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w21], v[244:247], %[r], %[w21]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w22], v[248:251], %[r], %[w22]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w23], v[252:255], %[r], %[w23]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
       "s_nop 7\n\t"
       "ds_read_b64_tr_b16 v[240:241], %[t4] offset:768\n\t"
@@ -345,15 +459,15 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
       "ds_read_b64_tr_b16 v[250:251], %[t6] offset:19200\n\t"
       "ds_read_b64_tr_b16 v[252:253], %[t7] offset:768\n\t"
       "ds_read_b64_tr_b16 v[254:255], %[t7] offset:19200\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o24], v[224:227], %[p], %[o24]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o25], v[228:231], %[p], %[o25]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o26], v[232:235], %[p], %[o26]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o27], v[236:239], %[p], %[o27]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w24], v[224:227], %[r], %[w24]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w25], v[228:231], %[r], %[w25]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w26], v[232:235], %[r], %[w26]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w27], v[236:239], %[r], %[w27]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o28], v[240:243], %[p], %[o28]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o29], v[244:247], %[p], %[o29]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o30], v[248:251], %[p], %[o30]\n\t"
-      "v_mfma_f32_16x16x32_bf16 %[o31], v[252:255], %[p], %[o31]"
+      "v_mfma_f32_16x16x32_bf16 %[w28], v[240:243], %[r], %[w28]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w29], v[244:247], %[r], %[w29]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w30], v[248:251], %[r], %[w30]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[w31], v[252:255], %[r], %[w31]"
       : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]),
         [o4] "+a"(o[4]), [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]),
         [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]), [o11] "+a"(o[11]),
@@ -361,10 +475,18 @@ __device__ __forceinline__ void tr_keys(f32x4 (&o)[32], const uint32_t (&ta)[8],
         [o16] "+a"(o[16]), [o17] "+a"(o[17]), [o18] "+a"(o[18]), [o19] "+a"(o[19]),
         [o20] "+a"(o[20]), [o21] "+a"(o[21]), [o22] "+a"(o[22]), [o23] "+a"(o[23]),
         [o24] "+a"(o[24]), [o25] "+a"(o[25]), [o26] "+a"(o[26]), [o27] "+a"(o[27]),
-        [o28] "+a"(o[28]), [o29] "+a"(o[29]), [o30] "+a"(o[30]), [o31] "+a"(o[31])
+        [o28] "+a"(o[28]), [o29] "+a"(o[29]), [o30] "+a"(o[30]), [o31] "+a"(o[31]),
+        [w0] "+a"(w[0]), [w1] "+a"(w[1]), [w2] "+a"(w[2]), [w3] "+a"(w[3]),
+        [w4] "+a"(w[4]), [w5] "+a"(w[5]), [w6] "+a"(w[6]), [w7] "+a"(w[7]),
+        [w8] "+a"(w[8]), [w9] "+a"(w[9]), [w10] "+a"(w[10]), [w11] "+a"(w[11]),
+        [w12] "+a"(w[12]), [w13] "+a"(w[13]), [w14] "+a"(w[14]), [w15] "+a"(w[15]),
+        [w16] "+a"(w[16]), [w17] "+a"(w[17]), [w18] "+a"(w[18]), [w19] "+a"(w[19]),
+        [w20] "+a"(w[20]), [w21] "+a"(w[21]), [w22] "+a"(w[22]), [w23] "+a"(w[23]),
+        [w24] "+a"(w[24]), [w25] "+a"(w[25]), [w26] "+a"(w[26]), [w27] "+a"(w[27]),
+        [w28] "+a"(w[28]), [w29] "+a"(w[29]), [w30] "+a"(w[30]), [w31] "+a"(w[31])
       : [t0] "v"(ta[0]), [t1] "v"(ta[1]), [t2] "v"(ta[2]), [t3] "v"(ta[3]),
         [t4] "v"(ta[4]), [t5] "v"(ta[5]), [t6] "v"(ta[6]), [t7] "v"(ta[7]),
-        [p] "v"(p)
+        [p] "v"(p), [r] "v"(r)
       : "memory", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
 }
 
@@ -1600,6 +1722,12 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
   const int key = wfirst + l16;  // this lane's key (column l16 of S)
   const int key_t0 = ent ? kBlock * key + kBlock - 1 : key;  // its first query
   const bool key_ok = l16 < wkeys;
+  // The flat rows (t, h) that see the key, row = t H + h: row_lo <= row < row_hi
+  // (a raw key is seen by queries key .. key + 127, an entry by all from key_t0),
+  // so the per-row test needs no division by H.
+  const int64_t row_lo = key_ok ? (int64_t)key_t0 * a.H : nrows;
+  int64_t row_hi = ent ? nrows : ((int64_t)key + kWindow) * a.H;
+  row_hi = row_hi < nrows ? row_hi : nrows;
 
   f32x4 dk[32], dv[32];
 #pragma unroll
@@ -1672,12 +1800,15 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
       chains_keys(sc[0], sc[1], dp[0], dp[1], ad, kf, vf, lds_addr(sp + 2 * kStage + 16 * g4), stt);
     }
     bf16x8 pb, dsb;
+    // the block's rows r0 + off (off 0 .. 31) that see this lane's key: lo <= off < hi
+    const int64_t lo64 = row_lo - r0, hi64 = row_hi - r0;
+    const int lo = lo64 < 0 ? 0 : (lo64 > kTile ? kTile : (int)lo64);
+    const int hi = hi64 < 0 ? 0 : (hi64 > kTile ? kTile : (int)hi64);
 #pragma unroll
     for (int i8 = 0; i8 < 8; ++i8) {
       const int h = i8 >> 2, r = i8 & 3;
-      const int64_t row = r0 + 16 * h + 4 * g4 + r;
-      const int t = row < nrows ? (int)(row / a.H) : -1;
-      const bool v = key_ok && t >= key_t0 && (ent || t - (kWindow - 1) <= key);
+      const int off = 16 * h + 4 * g4 + r;
+      const bool v = off >= lo && off < hi;
       const float p = v ? __builtin_amdgcn_exp2f(sc[h][r] * a.c - stt[h][r]) : 0.0f;
       pb[i8] = (__bf16)p;
       dsb[i8] = (__bf16)(p * (dp[h][r] - stt[2 + h][r]));
@@ -1685,11 +1816,8 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
     // dV^T += dA^T P, dK^T += Q^T dS (transposing reads of the row tiles)
     uint32_t ta[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) ta[b] = lds_addr(sp + kStage) + tb[b];
-    tr_keys(dv, ta, pb);
-#pragma unroll
     for (int b = 0; b < 8; ++b) ta[b] = lds_addr(sp) + tb[b];
-    tr_keys(dk, ta, dsb);
+    tr_keys2(dv, dk, ta, pb, dsb);
   }
   mfma_drain();
   // lane (key l16, g4) holds dims 16 db + 4 g4 .. +3 of key l16
