@@ -1426,50 +1426,113 @@ __global__ void __launch_bounds__(256, 1) rows_kernel(BwArgs a) {
   const int lo_my = t_my - (kWindow - 1) > 0 ? t_my - (kWindow - 1) : 0;
   const int64_t ro = rmy * kD;
 
-  // dA = dout * sigmoid(g) depends on the inputs alone: rounded to bf16 and
-  // stored first (the key kernel reads it too), then read back as the B
-  // operand of dP^T = V dA^T.  Lane (row l16, g4) handles dims 16 db + 4 g4.
-  // With the saved state the same loop forms dg and the lane's part of <dO, o>.
+  // dA = dout * sigmoid(g) depends on the inputs alone (rounded to bf16; the
+  // key kernel reads it from the workspace too).  With the saved state lane
+  // (row l16, g4) forms dims 32 ss + 8 g4 .. +7, exactly its B operand fragment
+  // ss of dP^T = V dA^T, so dA stays in registers and nothing waits for its
+  // stores; the same loop forms dg and the lane's part of <dO, o>.
   const __amdgpu_buffer_rsrc_t rda = make_rsrc(a.da + r0 * kD, nr * 1024);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + r0 * kD, nr * 1024);
+  bf16x8 daf[16], qf[16];
   float dsum = 0.0f;
+  if constexpr (kSaved) {
+#pragma unroll
+  for (int ss = 0; ss < 16; ++ss)
+    qf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, l16 * 1024 + 64 * ss + 16 * g4, 0, 0));
+  // Four batches of four fragments; the loads of batch b+1 are issued before
+  // batch b is formed and stored (the stores could alias later loads, so the
+  // compiler would not move those loads above them).
+  uint4 gb[2][4], ob[2][4], xb[2][4][2];
+  auto load_batch = [&](int b, int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * (4 * b + i) + 8 * g4;
+      gb[slot][i] = *reinterpret_cast<const uint4*>(a.g + ro + d0);
+      ob[slot][i] = *reinterpret_cast<const uint4*>(a.dout + ro + d0);
+      if constexpr (kSaved) {
+        if (a.out_f32) {
+          xb[slot][i][0] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.out) + ro + d0);
+          xb[slot][i][1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.out) + ro + d0 + 4);
+        } else {
+          xb[slot][i][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.out) + ro + d0);
+        }
+      }
+    }
+  };
+  auto form_batch = [&](int b, int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ss = 4 * b + i, d0 = 32 * ss + 8 * g4;
+      const uint32_t gw[4] = {gb[slot][i].x, gb[slot][i].y, gb[slot][i].z, gb[slot][i].w};
+      const uint32_t ow[4] = {ob[slot][i].x, ob[slot][i].y, ob[slot][i].z, ob[slot][i].w};
+      float dov[8], sg[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dov[2 * e] = bf16_bits_to_f32(ow[e] & 0xFFFFu);
+        dov[2 * e + 1] = bf16_bits_to_f32(ow[e] >> 16);
+        sg[2 * e] = sigmoid(bf16_bits_to_f32(gw[e] & 0xFFFFu));
+        sg[2 * e + 1] = sigmoid(bf16_bits_to_f32(gw[e] >> 16));
+      }
+      const u32x4 w4 = {pack_bf16x2(dov[0] * sg[0], dov[1] * sg[1]), pack_bf16x2(dov[2] * sg[2], dov[3] * sg[3]),
+                        pack_bf16x2(dov[4] * sg[4], dov[5] * sg[5]), pack_bf16x2(dov[6] * sg[6], dov[7] * sg[7])};
+      daf[ss] = __builtin_bit_cast(bf16x8, w4);
+      __builtin_amdgcn_raw_buffer_store_b128(w4, rda, l16 * 1024 + 2 * d0, 0, 0);
+      if constexpr (kSaved) {
+        float ov[8];
+        if (a.out_f32) {
+          const uint32_t xw[8] = {xb[slot][i][0].x, xb[slot][i][0].y, xb[slot][i][0].z, xb[slot][i][0].w,
+                                  xb[slot][i][1].x, xb[slot][i][1].y, xb[slot][i][1].z, xb[slot][i][1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ov[e] = __uint_as_float(xw[e]);
+        } else {
+          const uint32_t uw[4] = {xb[slot][i][0].x, xb[slot][i][0].y, xb[slot][i][0].z, xb[slot][i][0].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ov[2 * e] = bf16_bits_to_f32(uw[e] & 0xFFFFu);
+            ov[2 * e + 1] = bf16_bits_to_f32(uw[e] >> 16);
+          }
+        }
+        float dgv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dsum += dov[e] * ov[e];
+          dgv[e] = dov[e] * ov[e] * (1.0f - sg[e]);
+        }
+        if (valid) {
+          *reinterpret_cast<float4*>(a.dg + ro + d0) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
+          *reinterpret_cast<float4*>(a.dg + ro + d0 + 4) = make_float4(dgv[4], dgv[5], dgv[6], dgv[7]);
+        }
+      }
+    }
+  };
+  load_batch(0, 0);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (b + 1 < 4) load_batch(b + 1, (b + 1) & 1);
+    form_batch(b, b & 1);
+  }
+  } else {
+  // Without the saved state dA is stored, then read back into the operand
+  // registers with the Q fragments (forming it in registers here leaves pass A
+  // short of registers).
 #pragma unroll 4
   for (int db = 0; db < 32; ++db) {
     const int d0 = 16 * db + 4 * g4;
     const uint2 g2 = *reinterpret_cast<const uint2*>(a.g + ro + d0);
     const uint2 o2 = *reinterpret_cast<const uint2*>(a.dout + ro + d0);
-    const float dov[4] = {bf16_bits_to_f32(o2.x & 0xFFFFu), bf16_bits_to_f32(o2.x >> 16),
-                          bf16_bits_to_f32(o2.y & 0xFFFFu), bf16_bits_to_f32(o2.y >> 16)};
-    const float sg[4] = {sigmoid(bf16_bits_to_f32(g2.x & 0xFFFFu)), sigmoid(bf16_bits_to_f32(g2.x >> 16)),
-                         sigmoid(bf16_bits_to_f32(g2.y & 0xFFFFu)), sigmoid(bf16_bits_to_f32(g2.y >> 16))};
-    const u32x2 w2 = {pack_bf16x2(dov[0] * sg[0], dov[1] * sg[1]),
-                      pack_bf16x2(dov[2] * sg[2], dov[3] * sg[3])};
+    const u32x2 w2 = {
+        pack_bf16x2(bf16_bits_to_f32(o2.x & 0xFFFFu) * sigmoid(bf16_bits_to_f32(g2.x & 0xFFFFu)),
+                    bf16_bits_to_f32(o2.x >> 16) * sigmoid(bf16_bits_to_f32(g2.x >> 16))),
+        pack_bf16x2(bf16_bits_to_f32(o2.y & 0xFFFFu) * sigmoid(bf16_bits_to_f32(g2.y & 0xFFFFu)),
+                    bf16_bits_to_f32(o2.y >> 16) * sigmoid(bf16_bits_to_f32(g2.y >> 16)))};
     __builtin_amdgcn_raw_buffer_store_b64(w2, rda, l16 * 1024 + 2 * d0, 0, 0);
-    if constexpr (kSaved) {
-      float ov[4];
-      if (a.out_f32) {
-        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + ro + d0);
-        ov[0] = f.x; ov[1] = f.y; ov[2] = f.z; ov[3] = f.w;
-      } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.out) + ro + d0);
-        ov[0] = bf16_bits_to_f32(u.x & 0xFFFFu); ov[1] = bf16_bits_to_f32(u.x >> 16);
-        ov[2] = bf16_bits_to_f32(u.y & 0xFFFFu); ov[3] = bf16_bits_to_f32(u.y >> 16);
-      }
-      float dgv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dsum += dov[e] * ov[e];
-        dgv[e] = dov[e] * ov[e] * (1.0f - sg[e]);
-      }
-      if (valid) *reinterpret_cast<float4*>(a.dg + ro + d0) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
-    }
   }
   wait_vm<0>();  // the stores have reached L2 (the loads below bypass L1)
-  bf16x8 daf[16], qf[16];
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + r0 * kD, nr * 1024);
 #pragma unroll
   for (int ss = 0; ss < 16; ++ss) {
     daf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rda, l16 * 1024 + 64 * ss + 16 * g4, 0, 1));
     qf[ss] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, l16 * 1024 + 64 * ss + 16 * g4, 0, 0));
+  }
   }
 
   // visible range of key kk (0 .. 31) of tile j for this lane's row: lo_v <= kk < hi_v
