@@ -625,9 +625,12 @@ __device__ __forceinline__ void step(const Args& a, WaveState& st, bf16x8 (&qf)[
 // registers.  The 16 logit pieces are read before any result is written back,
 // so the reads are not ordered behind the writes.
 //   out = O / l * sigmoid(G) = O / (l + l * 2^(-G log2 e))
-template <bool kF32>
+// issue(j) runs at the start of output piece j: copies whose issue is spread
+// over the gating, so that they leave the memory path room as they go.
+template <bool kF32, typename F>
 __device__ __forceinline__ void gate_rb(const Args& a, const WaveState& st, const Item& it, int rb,
-                                        uint8_t* region, const float* sL, int lane, int wave) {
+                                        uint8_t* region, const float* sL, int lane, int wave,
+                                        F&& issue) {
   asm volatile("" : "+v"(lane));
   constexpr float kLog2e = 1.4426950408889634f;
   const int l32 = lane & 31, g = lane >> 5;
@@ -639,6 +642,7 @@ __device__ __forceinline__ void gate_rb(const Args& a, const WaveState& st, cons
     gw[j] = *reinterpret_cast<const uint2*>(row + ((j ^ (l32 & 15)) << 4));
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
+    issue(j);
     const int bb = j >> 2, q = j & 3;
     const float gv[4] = {bf16_bits_to_f32(gw[j].x & 0xFFFFu), bf16_bits_to_f32(gw[j].x >> 16),
                          bf16_bits_to_f32(gw[j].y & 0xFFFFu), bf16_bits_to_f32(gw[j].y >> 16)};
@@ -1076,25 +1080,30 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(Args a) {
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): row sums written, Q read
     barrier_no_fence();                  // everyone's
-    {
+    // The gate logits of row blocks 0, 1 into the K stages (each wave its own
+    // region): with the plain epilogue one row per output piece of block 2.
+    const __amdgpu_buffer_rsrc_t g0 = block_rsrc(a.g, it, 0), g1 = block_rsrc(a.g, it, 1);
+    auto copy_g01 = [&](int jj) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      const __amdgpu_buffer_rsrc_t g0 = block_rsrc(a.g, it, 0), g1 = block_rsrc(a.g, it, 1);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) dma_rows(g0, jj, 256 * wave, sK0 + greg, ln);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) dma_rows(g1, jj, 256 * wave, sK1 + greg, ln);
-    }
+      if (jj < 8)
+        dma_rows(g0, jj, 256 * wave, sK0 + greg, ln);
+      else
+        dma_rows(g1, jj - 8, 256 * wave, sK1 + greg, ln);
+    };
     if constexpr (!kVha) {
-      gate_rb<kF32>(a, st, it, 2, sV0 + greg, sL, lane, wave);
+      auto none = [](int) {};
+      gate_rb<kF32>(a, st, it, 2, sV0 + greg, sL, lane, wave, copy_g01);
       if (!kF32) store_rb(a, it, 2, sV0 + greg, lane, wave);
-      gate_rb<kF32>(a, st, it, 3, sV1 + greg, sL, lane, wave);
+      gate_rb<kF32>(a, st, it, 3, sV1 + greg, sL, lane, wave, none);
       if (!kF32) store_rb(a, it, 3, sV1 + greg, lane, wave);
-      gate_rb<kF32>(a, st, it, 0, sK0 + greg, sL, lane, wave);
+      gate_rb<kF32>(a, st, it, 0, sK0 + greg, sL, lane, wave, none);
       if (!kF32) store_rb(a, it, 0, sK0 + greg, lane, wave);
-      gate_rb<kF32>(a, st, it, 1, sK1 + greg, sL, lane, wave);
+      gate_rb<kF32>(a, st, it, 1, sK1 + greg, sL, lane, wave, none);
       if (!kF32) store_rb(a, it, 1, sK1 + greg, lane, wave);
     } else {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) copy_g01(jj);
       // The item's second query (row blocks 2, 3) first: its logits are in.
       gate_rb_vha(st, 2, sV0 + greg, sL, lane);
       VhaFrags vf;
