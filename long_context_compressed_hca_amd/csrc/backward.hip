@@ -1746,13 +1746,19 @@ __global__ void __launch_bounds__(256, 1) keys_kernel(BwArgs a) {
   const int64_t nrows = a.T * a.H;
 
   // Task -> 64 keys and the row blocks rb0 .. rb1 of queries that can see
-  // them (the entry tasks first: they are the long ones).
+  // them (the entry tasks first: they are the long ones).  The entry tasks of
+  // one row chunk (every entry group's) are consecutive among the workgroups
+  // of one XCD (blockIdx % 8), so they run together and read the chunk's Q and
+  // dA rows, in the same order, through that XCD's L2: the rows come from HBM
+  // about once rather than once per entry group.
   const int task = blockIdx.x;
   const bool ent = task < a.n_ent_tasks;
   int first, nkeys;
   int64_t rb0, rb1;
   if (ent) {
-    const int grp = task / a.n_chunks, ch = task % a.n_chunks;
+    const int n_grp = a.n_ent_tasks / a.n_chunks;  // n_chunks is a multiple of 8
+    const int k = task >> 3;
+    const int grp = k % n_grp, ch = 8 * (k / n_grp) + (task & 7);
     first = kKeysPerWg * grp;
     nkeys = a.Nc - first < kKeysPerWg ? a.Nc - first : kKeysPerWg;
     const int64_t t0 = (int64_t)kBlock * first + kBlock - 1;  // first query seeing entry `first`
@@ -1966,7 +1972,7 @@ hipError_t launch_backward(const BackwardProblem& p, void* ws, hipStream_t strea
   w += up((size_t)a.Nc * kD * 4);
   a.dcv = reinterpret_cast<float*>(w);
   a.n_rb = (int)((rows + kTile - 1) / kTile);
-  a.n_chunks = (a.n_rb + kChunkRb - 1) / kChunkRb;
+  a.n_chunks = ((a.n_rb + kChunkRb - 1) / kChunkRb + 7) / 8 * 8;  // chunks past the rows are empty
   a.n_ent_tasks = ((a.Nc + kKeysPerWg - 1) / kKeysPerWg) * a.n_chunks;
   a.scale = p.scale;
   a.c = p.scale * 1.4426950408889634f;
