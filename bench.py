@@ -381,30 +381,37 @@ def cpu_baseline(args, torch, tensors):
 
 # ----------------------------------------------------------------- profiling
 def counters_workload(torch, hca, synth, reps: int):
-    """Every workload's inputs first, then `reps` launches of each in table order
-    (the 128K prefill and its VHA variant after prefill_8k; backward at 8K only),
-    then a plain copy of COPY_BYTES, for rocprofv3 runs (--pmc passes with reps = 1,
-    the kernel trace with more).  --write-profiles assumes this dispatch order."""
+    """Each workload in table order (the 128K prefill and its VHA variant right
+    after prefill_8k): its inputs are built, it is launched `reps` times, and it
+    is freed before the next is built (so the 128K backward fits); then a plain
+    copy of COPY_BYTES.  For rocprofv3 runs (--pmc passes with reps = 1, the
+    kernel trace with more); --write-profiles finds each workload's launches by
+    their kernel names, in this order."""
     dev = torch.device("cuda:0")
-    built = []
-    for name, what, build in workload_table(torch, hca, synth):
-        if name in ("backward_128k", "backward_saved_128k"):
-            continue
-        built.append((name, build()))
-        if name == "prefill_8k":
-            pf = w_prefill(torch, hca, synth, 131072, 64)
-            built.append(("prefill_128k", pf))
-            built.append(("prefill_vha_128k", w_prefill_vha(torch, hca, synth, pf)))
-    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
     order = []
-    for name, w in built:
+
+    def run(name, w):
+        torch.cuda.synchronize()
         print(f"counters: {name}", flush=True)
         for _ in range(reps):
             w["call"]()
             torch.cuda.synchronize()
         order.append({"name": name, "kernels": w["kernels"], "src": w["src"], "reps": reps})
+
+    for name, what, build in workload_table(torch, hca, synth):
+        w = build()
+        run(name, w)
+        del w
+        if name == "prefill_8k":
+            pf = w_prefill(torch, hca, synth, 131072, 64)
+            run("prefill_128k", pf)
+            vha = w_prefill_vha(torch, hca, synth, pf)
+            run("prefill_vha_128k", vha)
+            del pf, vha
+        torch.cuda.empty_cache()
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"order": order}), flush=True)
@@ -443,28 +450,23 @@ def _traced(run_dir):
 
 
 def _match(dispatches, order):
-    """Assign dispatches to workloads: the last dispatches of the run are each
-    workload's kernels, `reps` times, in table order, then the copy.  Returns
-    {name: [[dispatches of launch 1], ...]}."""
+    """Assign dispatches to workloads: in the run's order, each workload's
+    launches are the first run of its kernels, `reps` times over, after the
+    previous workload's (the dispatches of building its inputs come before it);
+    the run's last dispatch is the copy.  Returns {name: [[dispatches of launch
+    1], ...]}."""
     names = [d["name"] for d in dispatches]
-    need = sum(w["reps"] * sum(n for _, n in w["kernels"]) for w in order)
-    start = len(names) - need - 1
-    if start < 0:
-        raise SystemExit("fewer dispatches than the counters workload launches")
-    out, i = {}, start
+    out, i = {}, 0
     for w in order:
-        launches = []
-        for _ in range(w["reps"]):
-            got = []
-            for pat, n in w["kernels"]:
-                for _ in range(n):
-                    if pat not in names[i]:
-                        raise SystemExit(f"dispatch {i} is {names[i]!r}, expected {pat!r}")
-                    got.append(dispatches[i])
-                    i += 1
-            launches.append(got)
-        out[w["name"]] = launches
-    out["copy"] = [[dispatches[i]]]
+        seq = [pat for _ in range(w["reps"]) for pat, n in w["kernels"] for _ in range(n)]
+        while i + len(seq) <= len(names) and not all(p in names[i + k] for k, p in enumerate(seq)):
+            i += 1
+        if i + len(seq) > len(names):
+            raise SystemExit(f"the launches of {w['name']} are not in the trace")
+        per = len(seq) // w["reps"]
+        out[w["name"]] = [dispatches[i + r * per:i + (r + 1) * per] for r in range(w["reps"])]
+        i += len(seq)
+    out["copy"] = [[dispatches[-1]]]
     return out
 
 

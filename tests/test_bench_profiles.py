@@ -1,0 +1,39 @@
+"""The profile summariser's assignment of traced dispatches to workloads (CPU)."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _d(names):
+    return [{"name": n, "ns": i} for i, n in enumerate(names)]
+
+
+def test_match_skips_input_building_dispatches():
+    order = [{"name": "a", "kernels": [("prefill_kernel", 1)], "reps": 2},
+             {"name": "b", "kernels": [("zero_kernel", 2), ("rows_kernel", 1)], "reps": 2}]
+    names = ["normal_kernel", "compress_kernel", "prefill_kernel<0>", "prefill_kernel<0>",
+             "normal_kernel", "prefill_kernel<lse>",  # building b: not b's kernels
+             "zero_kernel", "zero_kernel", "rows_kernel", "zero_kernel", "zero_kernel",
+             "rows_kernel", "fill", "copy"]
+    m = bench._match(_d(names), order)
+    assert [[d["ns"] for d in l] for l in m["a"]] == [[2], [3]]
+    assert [[d["ns"] for d in l] for l in m["b"]] == [[6, 7, 8], [9, 10, 11]]
+    assert m["copy"][0][0]["name"] == "copy"
+
+
+def test_match_needs_the_whole_run_of_launches():
+    # a lone match of the first kernel (a build step) is skipped for the full run
+    order = [{"name": "b", "kernels": [("zero_kernel", 1), ("rows_kernel", 1)], "reps": 1}]
+    m = bench._match(_d(["zero_kernel", "x", "zero_kernel", "rows_kernel", "copy"]), order)
+    assert [d["ns"] for d in m["b"][0]] == [2, 3]
+
+
+def test_match_reports_missing_launches():
+    order = [{"name": "a", "kernels": [("gate_kernel", 1)], "reps": 1}]
+    with pytest.raises(SystemExit):
+        bench._match(_d(["prefill_kernel", "copy"]), order)
