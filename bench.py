@@ -390,13 +390,16 @@ def counters_workload(torch, hca, synth, reps: int):
     dev = torch.device("cuda:0")
     order = []
 
+    warm = 1 if reps > 1 else 0  # the trace's launches follow one untimed launch
+
     def run(name, w):
         torch.cuda.synchronize()
         print(f"counters: {name}", flush=True)
-        for _ in range(reps):
+        for _ in range(warm + reps):
             w["call"]()
             torch.cuda.synchronize()
-        order.append({"name": name, "kernels": w["kernels"], "src": w["src"], "reps": reps})
+        order.append({"name": name, "kernels": w["kernels"], "src": w["src"], "reps": reps,
+                      "warm": warm})
 
     for name, what, build in workload_table(torch, hca, synth):
         w = build()
@@ -451,20 +454,23 @@ def _traced(run_dir):
 
 def _match(dispatches, order):
     """Assign dispatches to workloads: in the run's order, each workload's
-    launches are the first run of its kernels, `reps` times over, after the
-    previous workload's (the dispatches of building its inputs come before it);
+    launches are the first run of its kernels, `warm` + `reps` times over, after
+    the previous workload's (the dispatches of building its inputs come before
+    it), of which the first `warm` are left out;
     the run's last dispatch is the copy.  Returns {name: [[dispatches of launch
     1], ...]}."""
     names = [d["name"] for d in dispatches]
     out, i = {}, 0
     for w in order:
-        seq = [pat for _ in range(w["reps"]) for pat, n in w["kernels"] for _ in range(n)]
+        n_l = w.get("warm", 0) + w["reps"]  # warm-up launches first, then the counted ones
+        seq = [pat for _ in range(n_l) for pat, n in w["kernels"] for _ in range(n)]
         while i + len(seq) <= len(names) and not all(p in names[i + k] for k, p in enumerate(seq)):
             i += 1
         if i + len(seq) > len(names):
             raise SystemExit(f"the launches of {w['name']} are not in the trace")
-        per = len(seq) // w["reps"]
-        out[w["name"]] = [dispatches[i + r * per:i + (r + 1) * per] for r in range(w["reps"])]
+        per = len(seq) // n_l
+        out[w["name"]] = [dispatches[i + r * per:i + (r + 1) * per]
+                          for r in range(w.get("warm", 0), n_l)]
         i += len(seq)
     out["copy"] = [[dispatches[-1]]]
     return out

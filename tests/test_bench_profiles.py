@@ -37,3 +37,9 @@ def test_match_reports_missing_launches():
     order = [{"name": "a", "kernels": [("gate_kernel", 1)], "reps": 1}]
     with pytest.raises(SystemExit):
         bench._match(_d(["prefill_kernel", "copy"]), order)
+
+
+def test_match_leaves_out_warm_up_launches():
+    order = [{"name": "a", "kernels": [("gate_kernel", 1)], "reps": 2, "warm": 1}]
+    m = bench._match(_d(["x", "gate_kernel", "gate_kernel", "gate_kernel", "copy"]), order)
+    assert [[d["ns"] for d in l] for l in m["a"]] == [[2], [3]]
