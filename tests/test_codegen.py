@@ -1,14 +1,15 @@
-"""Generated-code checks for the prefill kernel's inline-asm MFMAs (CPU only).
+"""Generated-code checks for the kernels' inline-asm MFMAs (CPU only).
 
-The score MFMAs of the prefill kernel, and the two products of its head-mix
-epilogue, are inline asm, so the compiler inserts no wait states around them.  The hardware needs 2 wait
-states between a VALU write of an MFMA operand and the MFMA, and some more
-between the MFMA and a VALU read of its result.  The kernel source supplies the
-second (s_nop after the last MFMA of a chain) and arranges for the first (the
-operands come from LDS reads; the chain's first MFMA carries its own s_nop).
-This test compiles the kernel for gfx950 and checks both in the assembly, so a
-compiler change that moves a register copy in front of one of these MFMAs is
-caught on the CPU.
+The score MFMAs of the prefill kernel and the two products of its head-mix
+epilogue, the decode kernels' products, the backward kernels' chains and the
+gate GEMM's MFMAs are inline asm, so the compiler inserts no wait states
+around them.  The hardware needs 2 wait states between a VALU write of an
+MFMA operand and the MFMA, and some more between the MFMA and a VALU read of
+its result.  The kernel sources supply the second (s_nop after the last MFMA
+of a chain) and arrange for the first (the operands come from LDS or memory
+reads, or the MFMA carries its own s_nop).  These tests compile each kernel
+source for gfx950 and check both in the assembly, so a compiler change that
+moves a register copy in front of one of these MFMAs is caught on the CPU.
 """
 import os
 import re
@@ -40,14 +41,16 @@ def _wait_states(line):
     return int(line.split()[1]) + 1 if line.startswith("s_nop") else 1
 
 
-@pytest.fixture(scope="module")
-def prefill_asm(tmp_path_factory):
+SOURCES = ["prefill.hip", "decode.hip", "decode_sk.hip", "backward.hip", "gate.hip"]
+
+
+def _compile(src, tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "prefill.s"
+    out = tmp_path_factory.mktemp("asm") / (src + ".s")
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
            "-Xclang", "-packed-fp32-ops", "-S", "--cuda-device-only",
-           os.path.join(CSRC, "prefill.hip"), "-o", str(out)]
+           "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     lines = []
     for raw in out.read_text().splitlines():
@@ -55,6 +58,16 @@ def prefill_asm(tmp_path_factory):
         if t and not t.startswith(".") and not t.endswith(":"):
             lines.append(t)
     return lines
+
+
+@pytest.fixture(scope="module")
+def prefill_asm(tmp_path_factory):
+    return _compile("prefill.hip", tmp_path_factory)
+
+
+@pytest.fixture(scope="module", params=SOURCES)
+def kernel_asm(request, tmp_path_factory):
+    return _compile(request.param, tmp_path_factory)
 
 
 def _vgpr_mfmas(lines):
@@ -84,10 +97,12 @@ def test_no_valu_write_of_an_operand_just_before_an_asm_mfma(prefill_asm):
     assert not bad, bad[:5]
 
 
-def test_no_valu_write_of_any_operand_just_before_an_mfma(prefill_asm):
+def test_no_valu_write_of_any_operand_just_before_an_mfma(kernel_asm):
     # every MFMA, also those accumulating into AGPRs (the head-mix product of the
-    # epilogue is inline asm of that kind): no VALU write, v_accvgpr_write
-    # included, of a source operand within 2 wait states
+    # prefill epilogue, the decode and backward products are inline asm of that
+    # kind): no VALU write, v_accvgpr_write included, of a source operand
+    # within 2 wait states
+    prefill_asm = kernel_asm
     bad = []
     for i, l in enumerate(prefill_asm):
         if not l.startswith("v_mfma"):
@@ -106,9 +121,10 @@ def test_no_valu_write_of_any_operand_just_before_an_mfma(prefill_asm):
     assert not bad, bad[:5]
 
 
-def test_chain_results_wait_before_valu_reads(prefill_asm):
+def test_chain_results_wait_before_valu_reads(kernel_asm):
     # after an MFMA writing VGPRs, the first instruction that reads them must be
     # at least 18 wait states later (another MFMA of the same chain excepted)
+    prefill_asm = kernel_asm
     bad = []
     for i, l in _vgpr_mfmas(prefill_asm):
         dst = _regs(_operands(l)[0])
