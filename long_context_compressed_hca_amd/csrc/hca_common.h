@@ -29,9 +29,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return u >> 16;
 }
 
-// Two floats -> packed bfloat16 pair (lo in bits 0..15), nearest even.
+// Two floats -> packed bfloat16 pair (lo in bits 0..15), nearest even: one
+// v_cvt_pk_bf16_f32 (the same rounding as f32_to_bf16_bits for every
+// non-NaN input; a NaN stays a NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // ---------------------------------------------------------------- LDS DMA
