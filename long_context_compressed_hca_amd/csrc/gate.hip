@@ -11,8 +11,9 @@
 // (latent [T, R] row major, W_g [N, R] like a linear layer's weight):
 //   * a workgroup computes a 256 (n) x 256 (t) tile of G^T, four waves of
 //     128 x 128, each 4 x 4 MFMA 32x32x16 blocks with the accumulators in
-//     AGPRs; computing G^T puts four consecutive n of one t in each lane, so
-//     the epilogue stores 8 contiguous bytes per lane;
+//     AGPRs; computing G^T puts four consecutive n of one t in each lane, and
+//     the epilogue turns the wave's block into rows of G through LDS so that
+//     it stores whole 128-byte lines;
 //   * K advances 32 at a time through four LDS stages (32 KiB each), filled by
 //     DMA three steps ahead; 64-byte rows are stored with their 16-byte chunks
 //     permuted (chunk c of row i at c ^ ((i >> 2) & 3)), so the fragment reads
@@ -35,6 +36,8 @@ constexpr int kRowB = kBK * 2;              // 64 bytes per row per stage
 constexpr int kOpBytes = 256 * kRowB;       // one operand of one stage: 16 KiB
 constexpr int kStageB = 2 * kOpBytes;       // W_g then latent
 constexpr int kStages = 4;
+constexpr int kEpiRow = 256 + 16;           // LDS row of the epilogue's transpose
+constexpr int kLdsBytes = kStages * kStageB > 4 * 128 * kEpiRow ? kStages * kStageB : 4 * 128 * kEpiRow;
 
 struct GateArgs {
   const uint16_t* lat;  // [T, R]
@@ -73,7 +76,7 @@ __device__ __forceinline__ void mfma32(f32x16& acc, const bf16x8& a, const bf16x
 }
 
 __global__ void __launch_bounds__(256, 1) gate_kernel(GateArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
   // blockIdx -> (t tile, n tile): consecutive workgroups of one XCD (blockIdx
   // % 8) fill a group of 4 t tiles x 8 n tiles.
@@ -185,24 +188,37 @@ __global__ void __launch_bounds__(256, 1) gate_kernel(GateArgs a) {
   }
 
   asm volatile("s_nop 15\n\ts_nop 15");  // wait states before VALU reads of the accumulators
-  // Epilogue: D[n][t] block (bi, bj): lane (t = lane % 32, half h), register r
-  // -> n = 8 (r / 4) + 4 h + r % 4.  Four consecutive n of one t: 8 bytes of a
-  // row of G, range checked against the last row.
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + t0 * a.N, (int)t_rows * a.N * 2);
+  // Epilogue through LDS.  D[n][t] block (bi, bj): lane (t = lane % 32, half
+  // h), register r -> n = 8 (r / 4) + 4 h + r % 4, so each lane holds 8-byte
+  // pieces of 32 rows of G; stored as they are, every instruction writes 16
+  // bytes of each of 32 rows, which stores at about half the rate of whole
+  // lines.  So each wave writes its 128 x 128 block into its own LDS region
+  // (rows t of 256 bytes, 16 bytes of padding so a piece write of 16 rows
+  // hits distinct banks) and stores it as whole rows, 4 rows of 256 bytes
+  // per instruction.  The stages are free: every wave's last LDS reads were
+  // waited for before the loop's last barrier.
+  uint8_t* region = lds + wave * 128 * kEpiRow;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-      const int t = 128 * wb + 32 * bj + fi;
+      const f32x16& c = acc[bi][bj];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int n = n0 + 128 * wa + 32 * bi + 8 * qq + 4 * fh;
-        const f32x16& c = acc[bi][bj];
         typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
         const u32x2 v = {pack_bf16x2(c[4 * qq], c[4 * qq + 1]), pack_bf16x2(c[4 * qq + 2], c[4 * qq + 3])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, rg, (t * a.N + n) * 2, 0, 0);
+        *reinterpret_cast<u32x2*>(region + (32 * bj + fi) * kEpiRow + (32 * bi + 8 * qq + 4 * fh) * 2) = v;
       }
     }
+  // Rows past the last one are range checked.
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.g + t0 * a.N, (int)t_rows * a.N * 2);
+  const int c16 = lane & 15;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int row = 4 * k + (lane >> 4);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region + row * kEpiRow + 16 * c16);
+    store16_buf(rg, ((128 * wb + row) * a.N + n0 + 128 * wa + 8 * c16) * 2, v);
+  }
 }
 
 }  // namespace
