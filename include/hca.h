@@ -244,7 +244,7 @@ hca_status_t hca_attn_decode_multi(const void* q, const void* g, const void* ck,
  *   latent  device, bf16 [T, R]
  *   w_g     device, bf16 [N, R]    (out x in, like a linear layer's weight)
  *   g       device, bf16 [T, N]    (overwritten)
- * R a multiple of 32 from 32 to 16384, N a multiple of 2048 up to 65536 (H * 512 with
+ * R a multiple of 64 from 64 to 16384, N a multiple of 2048 up to 65536 (H * 512 with
  * H a multiple of 4), else HCA_ERR_UNSUPPORTED.  T = 0 is a no-op.
  */
 hca_status_t hca_gate_logits(const void* latent, const void* w_g, int64_t T, int R, int N,

@@ -364,8 +364,8 @@ hca_status_t hca_attn_decode_noalloc(const void* q, const void* g, const void* c
 hca_status_t hca_gate_logits(const void* latent, const void* w_g, int64_t T, int R, int N,
                              void* g, void* stream) {
   if (T < 0) return fail(HCA_ERR_INVALID_ARG, "T = %lld < 0", (long long)T);
-  if (R < 32 || R > 16384 || R % 32 != 0)
-    return fail(HCA_ERR_UNSUPPORTED, "R = %d (need a multiple of 32, 32 .. 16384)", R);
+  if (R < 64 || R > 16384 || R % 64 != 0)
+    return fail(HCA_ERR_UNSUPPORTED, "R = %d (need a multiple of 64, 64 .. 16384)", R);
   if (N < 2048 || N > 65536 || N % 2048 != 0)
     return fail(HCA_ERR_UNSUPPORTED, "N = %d (need a multiple of 2048, at most 65536)", N);
   if (T > ((int64_t)1 << 40)) return fail(HCA_ERR_UNSUPPORTED, "T beyond 2^40");

@@ -14,12 +14,16 @@
 //     AGPRs; computing G^T puts four consecutive n of one t in each lane, and
 //     the epilogue turns the wave's block into rows of G through LDS so that
 //     it stores whole 128-byte lines;
-//   * K advances 32 at a time through four LDS stages (32 KiB each), filled by
-//     DMA three steps ahead; 64-byte rows are stored with their 16-byte chunks
-//     permuted (chunk c of row i at c ^ ((i >> 2) & 3)), so the fragment reads
-//     of 8 lanes hit 8 different bank groups; the permutation is applied on
-//     the global side of the copy (each lane fetches the chunk that belongs at
-//     its LDS position);
+//   * K advances 64 at a time.  Each operand's 256 x 64 slice of a step (32
+//     KiB: 128-byte row pieces, whole cache lines) is copied into LDS by DMA,
+//     W_g two steps ahead through three buffers, the latent one step ahead
+//     through two (five buffers, 160 KiB).  A copy instruction fetches 8 rows
+//     x 128 bytes: whole lines, which the copy path moves faster than the
+//     half-line pieces of a 32-wide step (the steps are bound by the copies
+//     more than by the MFMAs).  The 16-byte chunks of
+//     a row are permuted (chunk c of row i at c ^ ((i >> 1) & 7)), applied on
+//     the global side of the copy, so the fragment reads of 16 lanes hit 16
+//     different bank groups;
 //   * tiles are dealt in groups of 4 (t) x 8 (n) per XCD, so the 32
 //     workgroups of a group read their latent and W_g slices from that XCD's
 //     L2 (12 slices instead of 64 per step).
@@ -31,13 +35,13 @@
 namespace hca {
 namespace {
 
-constexpr int kBT = 256, kBN = 256, kBK = 32;
-constexpr int kRowB = kBK * 2;              // 64 bytes per row per stage
-constexpr int kOpBytes = 256 * kRowB;       // one operand of one stage: 16 KiB
-constexpr int kStageB = 2 * kOpBytes;       // W_g then latent
-constexpr int kStages = 4;
+constexpr int kBT = 256, kBN = 256, kBK = 64;
+constexpr int kRowB = kBK * 2;              // 128 bytes per row per step
+constexpr int kOpBytes = 256 * kRowB;       // one operand's slice of a step: 32 KiB
+constexpr int kWBufs = 3, kLBufs = 2;       // W_g buffers, then latent buffers
+constexpr int kLdsBytes = (kWBufs + kLBufs) * kOpBytes;
 constexpr int kEpiRow = 256 + 16;           // LDS row of the epilogue's transpose
-constexpr int kLdsBytes = kStages * kStageB > 4 * 128 * kEpiRow ? kStages * kStageB : 4 * 128 * kEpiRow;
+static_assert(4 * 128 * kEpiRow <= kLdsBytes, "the epilogue fits the buffers");
 
 struct GateArgs {
   const uint16_t* lat;  // [T, R]
@@ -48,22 +52,18 @@ struct GateArgs {
   int n_tiles_t, n_tiles_n;
 };
 
-// Position of 16-byte chunk c of row i inside its 64-byte LDS row.
-__device__ __forceinline__ int chunk_pos(int i, int c) { return c ^ ((i >> 2) & 3); }
+// Position of 16-byte chunk c of row i inside its 128-byte LDS row.
+__device__ __forceinline__ int chunk_pos(int i, int c) { return c ^ ((i >> 1) & 7); }
 
-// DMA of one operand's 256 x 32 slice (columns k0 .. k0+31) into an LDS
-// stage: wave `wave` copies rows 64 wave .. 64 wave + 63, 16 rows (1 KiB) per
-// instruction; lane L writes LDS row r0 + L / 4, position L % 4, and fetches
-// the chunk stored there.
-__device__ __forceinline__ void dma_slice(__amdgpu_buffer_rsrc_t src, int ld_bytes, int k0,
-                                          uint8_t* dst, int wave, int lane) {
-  const int rr = lane >> 2, pos = lane & 3;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = 64 * wave + 16 * u + rr;
-    const int c = pos ^ ((row >> 2) & 3);
-    dma16_buf(src, row * ld_bytes + 2 * k0 + 16 * c, (lds_void*)(dst + (64 * wave + 16 * u) * kRowB));
-  }
+// DMA of one operand's 256 x 64 slice (columns k0 .. k0+63) into an LDS
+// buffer: wave `wave` copies rows 64 wave .. 64 wave + 63, 8 rows (1 KiB) per
+// instruction u (0..7); lane L writes LDS row r0 + L / 8, position L % 8, and
+// fetches the chunk stored there.
+__device__ __forceinline__ void dma_rows8(__amdgpu_buffer_rsrc_t src, int ld_bytes, int k0,
+                                          uint8_t* dst, int wave, int lane, int u) {
+  const int row = 64 * wave + 8 * u + (lane >> 3), pos = lane & 7;
+  const int c = pos ^ ((row >> 1) & 7);
+  dma16_buf(src, row * ld_bytes + 2 * k0 + 16 * c, (lds_void*)(dst + (64 * wave + 8 * u) * kRowB));
 }
 
 // MFMA with the accumulator pinned to AGPRs (inline asm: the builtin lets the
@@ -105,20 +105,26 @@ __global__ void __launch_bounds__(256, 1) gate_kernel(GateArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   const int nk = a.R / kBK;
-  // Prologue: steps 0, 1, 2.
+  uint8_t* const wbuf = lds;                       // W_g of step s: buffer s % 3
+  uint8_t* const lbuf = lds + kWBufs * kOpBytes;   // latent of step s: buffer s % 2
+  auto w_dst = [&](int s) { return wbuf + (s % kWBufs) * kOpBytes; };
+  auto l_dst = [&](int s) { return lbuf + (s % kLBufs) * kOpBytes; };
+  // Prologue: W_g of steps 0 and 1, the latent of step 0.
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (s < nk) {
-      dma_slice(rw, ld, s * kBK, lds + s * kStageB, wave, lane);
-      dma_slice(rl, ld, s * kBK, lds + s * kStageB + kOpBytes, wave, lane);
-    }
+  for (int u = 0; u < 8; ++u) dma_rows8(rw, ld, 0, w_dst(0), wave, lane, u);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) dma_rows8(rl, ld, 0, l_dst(0), wave, lane, u);
+  if (nk > 1) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dma_rows8(rw, ld, kBK, w_dst(1), wave, lane, u);
   }
   // Fragment offsets: lane (i = lane % 32, k half = lane / 32) of 32-row block
-  // bi reads row 32 bi + i, logical chunk 2 kk + lane / 32.
+  // bi reads row 32 bi + i, logical chunk 2 kk + lane / 32 (kk = 0..3: the
+  // four 16-wide k slices of a step).
   const int fi = lane & 31, fh = lane >> 5;
   auto read_frags = [&](int s, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
-    const uint8_t* sw = lds + (s % kStages) * kStageB;
-    const uint8_t* sl = sw + kOpBytes;
+    const uint8_t* sw = w_dst(s);
+    const uint8_t* sl = l_dst(s);
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
       const int r = 128 * wa + 32 * bi + fi;
@@ -130,61 +136,52 @@ __global__ void __launch_bounds__(256, 1) gate_kernel(GateArgs a) {
       bfr[bj] = *reinterpret_cast<const bf16x8*>(sl + r * kRowB + 16 * chunk_pos(r, 2 * kk + fh));
     }
   };
-  // This wave's copies of step s have landed: the copies of the steps after
-  // it that are already issued (up to s + 2, 8 each) may still be in flight.
-  // (s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at "no wait")
-  auto wait_step = [&](int s) {
-    if (s + 2 < nk)
-      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
-    else if (s + 1 < nk)
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  };
-  // One DMA instruction of step t's copies (u = 0..7: W_g rows, then latent rows).
-  auto dma_one = [&](int t, int u) {
-    uint8_t* st = lds + (t % kStages) * kStageB + (u < 4 ? 0 : kOpBytes);
-    const int uu = u & 3, rr = lane >> 2, pos = lane & 3;
-    const int row = 64 * wave + 16 * uu + rr;
-    const int c = pos ^ ((row >> 2) & 3);
-    dma16_buf(u < 4 ? rw : rl, row * ld + 2 * t * kBK + 16 * c, (lds_void*)(st + (64 * wave + 16 * uu) * kRowB));
-  };
+  // s_waitcnt vmcnt(8) / vmcnt(0), expcnt and lgkmcnt left at "no wait".
+  auto wait_vm8 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F78); };
+  auto wait_vm0 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  // Step s runs in two halves of 16 MFMAs (k = 0..15, then 16..31):
-  //   first half   MFMAs on the k 0..15 fragments (read during the previous
-  //                step), while this step's k 16..31 fragments are read and
-  //                step s+3's 8 copies issue, one after every other MFMA (an
-  //                issuing copy stalls the wave; spread out, the MFMAs already
-  //                issued keep the pipe busy);
-  //   sync         this wave's copies of step s+1 have landed and its reads of
-  //                step s are done; barrier: every wave's, so step s+1 may be
-  //                read and step s's stage may be refilled by step s+4;
-  //   second half  MFMAs on the k 16..31 fragments, while step s+1's k 0..15
-  //                fragments are read.
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
-  wait_step(0);
+  // Step s runs four k slices of 16 MFMAs each, the fragments of slice kk+1
+  // read during slice kk:
+  //   slice 0   issues the latent copies of step s+1, one after every other
+  //             MFMA (an issuing copy stalls the wave; spread out, the MFMAs
+  //             already issued keep the pipe busy);
+  //   slice 1   issues the W_g copies of step s+2 the same way;
+  //   sync      after slice 2: this wave's copies of step s+1 have landed
+  //             (only the W_g copies of step s+2 may still be in flight) and
+  //             its reads of step s are done (slice 3's fragments were read
+  //             during slice 2); barrier: every wave's, so step s+1 may be
+  //             read and the buffers of step s refilled (latent by step s+2,
+  //             W_g by step s+3);
+  //   slice 3   while step s+1's slice-0 fragments are read.
+  bf16x8 af[2][4], bf[2][4];
+  if (nk > 1) wait_vm8(); else wait_vm0();
   barrier_no_fence();
-  read_frags(0, 0, a0, b0);
+  read_frags(0, 0, af[0], bf[0]);
   for (int s = 0; s < nk; ++s) {
-    const bool copy = s + 3 < nk;
+    const bool copy_l = s + 1 < nk, copy_w = s + 2 < nk;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      mfma32(acc[m >> 2][m & 3], a0[m >> 2], b0[m & 3]);
-      if (m == 1) {
-        // after the first MFMAs (which wait for the k 0..15 reads): a wait
-        // placed by the compiler for those would otherwise cover these too
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(s, 1, a1, b1);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1;
+      if (kk == 3) {
+        if (copy_w) wait_vm8(); else wait_vm0();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's reads are done
+        barrier_no_fence();
+        if (s + 1 < nk) read_frags(s + 1, 0, af[0], bf[0]);
       }
-      if ((m & 1) && copy) dma_one(s + 3, m >> 1);
-    }
-    if (s + 1 < nk) wait_step(s + 1);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's reads are done
-    barrier_no_fence();
-    if (s + 1 < nk) read_frags(s + 1, 0, a0, b0);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) mfma32(acc[m >> 2][m & 3], a1[m >> 2], b1[m & 3]);
+      for (int m = 0; m < 16; ++m) {
+        mfma32(acc[m >> 2][m & 3], af[cur][m >> 2], bf[cur][m & 3]);
+        if (m == 1 && kk < 3) {
+          // after the first MFMAs (which wait for this slice's reads): a wait
+          // placed by the compiler for those would otherwise cover these too
+          __builtin_amdgcn_sched_barrier(0);
+          read_frags(s, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kk == 0 && (m & 1) && copy_l) dma_rows8(rl, ld, (s + 1) * kBK, l_dst(s + 1), wave, lane, m >> 1);
+        if (kk == 1 && (m & 1) && copy_w) dma_rows8(rw, ld, (s + 2) * kBK, w_dst(s + 2), wave, lane, m >> 1);
+      }
+    }
   }
 
   asm volatile("s_nop 15\n\ts_nop 15");  // wait states before VALU reads of the accumulators

@@ -73,7 +73,7 @@ hipError_t launch_decode_sk(const DecodeProblem& p, const uint16_t* nk, const ui
                             void* ws, hipStream_t stream);
 
 // Gate logits of the low-rank gate: g [T, N] = bf16(latent [T, R] * w [N, R]^T);
-// R a multiple of 32, N a multiple of 2048.
+// R a multiple of 64, N a multiple of 2048.
 hipError_t launch_gate(const uint16_t* latent, const uint16_t* w, uint16_t* g, int64_t T, int R,
                        int N, hipStream_t stream);
 

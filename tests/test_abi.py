@@ -321,3 +321,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(hca, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         hca.lib()
+
+
+def gate(L, **kw):
+    a = dict(latent=P, w=P, T=256, R=1024, N=32768, g=P, stream=None)
+    a.update(kw)
+    return L.hca_gate_logits(a["latent"], a["w"], a["T"], a["R"], a["N"], a["g"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=32), UNSUPPORTED), (dict(R=96), UNSUPPORTED), (dict(R=0), UNSUPPORTED),
+    (dict(R=16384 + 64), UNSUPPORTED), (dict(N=1024), UNSUPPORTED), (dict(N=3072), UNSUPPORTED),
+    (dict(N=65536 + 2048), UNSUPPORTED), (dict(T=-1), INVALID), (dict(latent=0), INVALID),
+    (dict(w=0), INVALID), (dict(g=0), INVALID),
+])
+def test_gate_logits_rejects(L, kw, status):
+    assert gate(L, **kw) == status
+
+
+def test_gate_logits_noop(L):
+    assert gate(L, T=0, latent=0, w=0, g=0) == OK
