@@ -44,25 +44,31 @@ def test_logits_against_oracle(T, N):
 
 
 def test_logits_large_sampled_rows():
-    # 4096 queries x 64 heads x 512: every row of 4 tiles and sampled rows elsewhere
-    T, R, N = 4096, 1024, 32768
+    # 4133 queries x 64 heads x 512 (17 t tiles, the last one ragged; several
+    # tiles per workgroup): the first, boundary and last rows and sampled rows
+    T, R, N = 4133, 1024, 32768
     lat, w = _inputs(7, T, R, N)
     g = torch.empty((T, N), dtype=torch.bfloat16, device=dev())
     hca.hca_gate_logits(lat, w, g)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(250, 262), np.arange(T - 8, T),
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(250, 262), np.arange(4090, 4100), np.arange(T - 8, T),
                                      np.random.default_rng(7).integers(0, T, 64)]))
     idx = torch.as_tensor(rows, device=dev())
     want = oracle.gate_logits(host(lat.index_select(0, idx)), host(w))
     _check_logits(host(g.index_select(0, idx)), want)
 
 
-def test_logits_exact_when_partial_sums_are_exact():
-    # integer latent, weights multiples of 1/8: every fp32 partial sum and the
-    # result are exact, so the GPU equals the exact value rounded to bf16 (here
-    # the value itself), bit for bit
-    T, R, N = 300, 64, 2048
-    rng = np.random.default_rng(3)
+@pytest.mark.parametrize("T,R,N", [
+    (300, 64, 2048),      # one tile per workgroup, one K step per tile
+    (2085, 64, 16384),    # two tiles per workgroup with one K step each, ragged last t tile
+    (4096, 128, 16384),   # several tiles per workgroup, two K steps each
+    (1100, 192, 32768),   # three K steps per tile (the W_g buffers wrap mid-tile)
+])
+def test_logits_exact_when_partial_sums_are_exact(T, R, N):
+    # integer latent, weights multiples of 1/8: every fp32 partial sum is exact
+    # (multiples of 1/8 below 2^21), so the GPU's result is the exact value
+    # rounded to nearest-even bf16, bit for bit, whatever the order of the sums
+    rng = np.random.default_rng(3 + R + T)
     lat_f = rng.integers(-2, 3, size=(T, R)).astype(np.float32)
     w_f = (rng.integers(-4, 5, size=(N, R)) / 8).astype(np.float32)
     lat_b, w_b = synth.f32_to_bf16_bits(lat_f), synth.f32_to_bf16_bits(w_f)
@@ -71,7 +77,7 @@ def test_logits_exact_when_partial_sums_are_exact():
     hca.hca_gate_logits(to_dev(lat_b), to_dev(w_b), g)
     torch.cuda.synchronize()
     want = oracle.gate_logits(lat_b, w_b)
-    assert np.all(np.abs(want) < 32)
+    assert np.all(np.abs(want) < 2.0 ** 21)
     np.testing.assert_array_equal(host(g), synth.f32_to_bf16_bits(want.astype(np.float32)))
 
 
