@@ -214,8 +214,13 @@ __device__ __forceinline__ void pv_mfma(f32x4& acc, i16x4 v, i16x4 p) {
   asm("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
 
-template <int NHB, bool MT>
-__global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
+// CW: four more waves (waves 4 .. 7) that only copy the V tiles, so the four
+// compute waves issue only their K loads.  A wave issues its vector-memory
+// instructions at a limited rate, so the step, whose copies and loads took
+// about as long to issue as its arithmetic, gets shorter.  It needs the
+// compute waves to fit two per SIMD (one head block, one token).
+template <int NHB, bool MT, bool CW = false>
+__global__ void __launch_bounds__(CW ? 512 : 256, 1) decode_kernel(Args a) {
   // Six V stages (V(j) in stage j % 6), two buffers each of weights (P^T of
   // every head block) and of partial scores (every wave's, for every head
   // block), the row sums and the repeat flags.  Separate arrays, so the
@@ -251,26 +256,28 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     const int lane16 = lane * 16;
     load_k<MT>(kk, 0, wave, l16, g4, kr[0]);
     load_k<MT>(kk, 1, wave, l16, g4, kr[1]);
-    copy_rows<MT>(kk, 0, kk.ev, kk.wv, kk.nv, sV0, kVRow, wave, lane16);
+    if (!CW) copy_rows<MT>(kk, 0, kk.ev, kk.wv, kk.nv, sV0, kVRow, wave, lane16);
     load_k<MT>(kk, 2, wave, l16, g4, kr[2]);
-    copy_rows<MT>(kk, 1, kk.ev, kk.wv, kk.nv, sV1, kVRow, wave, lane16);
+    if (!CW) copy_rows<MT>(kk, 1, kk.ev, kk.wv, kk.nv, sV1, kVRow, wave, lane16);
     load_k<MT>(kk, 3, wave, l16, g4, kr[3]);
-    copy_rows<MT>(kk, 2, kk.ev, kk.wv, kk.nv, sV2, kVRow, wave, lane16);
+    if (!CW) copy_rows<MT>(kk, 2, kk.ev, kk.wv, kk.nv, sV2, kVRow, wave, lane16);
     load_k<MT>(kk, 4, wave, l16, g4, kr[4]);
-    copy_rows<MT>(kk, 3, kk.ev, kk.wv, kk.nv, sV3, kVRow, wave, lane16);
+    if (!CW) copy_rows<MT>(kk, 3, kk.ev, kk.wv, kk.nv, sV3, kVRow, wave, lane16);
     load_k<MT>(kk, 5, wave, l16, g4, kr[5]);
-    copy_rows<MT>(kk, 4, kk.ev, kk.wv, kk.nv, sV4, kVRow, wave, lane16);
+    if (!CW) copy_rows<MT>(kk, 4, kk.ev, kk.wv, kk.nv, sV4, kVRow, wave, lane16);
   };
   const int64_t t_raw = a.pos[b];
   const int64_t head0 = (int64_t)b * a.H + hg * 16 * NHB;
   // Gate logits of this lane's outputs: head 16hb + l16, dims 128w + 16db + 4g4 .. +3.
   const int64_t rowo = (head0 + l16) * kD + 128 * wave + 4 * g4;
   uint2 gw[NHB][8];
+  if (!CW || wave < 4) {
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
+    for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      gw[hb][db] = *reinterpret_cast<const uint2*>(a.g + rowo + (int64_t)16 * hb * kD + 16 * db);
+      for (int db = 0; db < 8; ++db)
+        gw[hb][db] = *reinterpret_cast<const uint2*>(a.g + rowo + (int64_t)16 * hb * kD + 16 * db);
+  }
   // Q^T fragments (B operand of the partial scores): head 16hb + l16, dims
   // 128w + 32ss + 8g4 .. +7; loaded at the start of each pass (a value loaded
   // before the pass loop and used in it would make the compiler wait for every
@@ -300,6 +307,40 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
   ks.nk = MT ? a.nk + (int64_t)b * a.M * kD : nullptr;
   ks.nv = MT ? a.nv + (int64_t)b * a.M * kD : nullptr;
   const int n = ks.n_tiles;  // >= 1: the new token itself is always a key
+  if constexpr (CW) {
+    if (wave >= 4) {
+      // Copy waves: V(j) into stage j % 6, rows 4 (wave - 4) .. +3, five tiles
+      // ahead, meeting every barrier of the compute waves' passes (two before
+      // the steps, one per step, two after).
+      const int cw = wave - 4, lane16 = lane * 16;
+      auto stage = [&](int j) -> uint8_t* {
+        switch (j % 6) {
+          case 0: return sV0;
+          case 1: return sV1;
+          case 2: return sV2;
+          case 3: return sV3;
+          case 4: return sV4;
+          default: return sV5;
+        }
+      };
+      for (int pass = 0;; ++pass) {
+        for (int j = 0; j < 5; ++j) copy_rows<MT>(ks, j, ks.ev, ks.wv, ks.nv, stage(j), kVRow, cw, lane16);
+        barrier_no_fence();  // the compute waves' partial scores of tiles 0, 1
+        __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): V(0) is in (V(1) .. V(4) may be in flight)
+        barrier_no_fence();
+        for (int s = 0; s < n; ++s) {
+          copy_rows<MT>(ks, s + 5, ks.ev, ks.wv, ks.nv, stage(s + 5), kVRow, cw, lane16);
+          __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): V(s+1) is in
+          barrier_no_fence();
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        const bool redo = (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0;
+        if (pass == 1 || !redo) return;
+        __syncthreads();
+      }
+    }
+  }
   // MT: the keys visible to the rows of head block `wave` (owner waves), whose
   // token j sits at position t + j: entries below ncj, ring rows from rlo on,
   // new rows up to j.
@@ -410,14 +451,15 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
     if (owner) weights(s + 1, sp, sPn);  // tile s+1
     scores(kc, sQn);  // tile s+2
     load_k<MT>(ks, s + 6, w, l16, g4, kn);
-    copy_rows<MT>(ks, s + 5, ks.ev, ks.wv, ks.nv, sVd, kVRow, w, lane16);
+    if (!CW) copy_rows<MT>(ks, s + 5, ks.ev, ks.wv, ks.nv, sVd, kVRow, w, lane16);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
       for (int db = 0; db < 8; ++db) pv_mfma(o[hb][db], vf[db], pf[hb]);  // tile s
     // V(s+1) is in for this wave (the loads and copies of steps s-3 .. s may
-    // be in flight), the LDS writes done; then for every wave.
-    wait_4_steps();
+    // be in flight; with copy waves, they wait for it), the LDS writes done;
+    // then for every wave.
+    if (!CW) wait_4_steps();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     barrier_no_fence();
   };
@@ -447,7 +489,7 @@ __global__ void __launch_bounds__(256, 1) decode_kernel(Args a) {
       read_partials(sQ0, sp);
       weights(0, sp, sP0);
     }
-    wait_4_steps();  // V(0) in
+    if (!CW) wait_4_steps();  // V(0) in
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier_no_fence();
     // Whole groups of six steps, then the rest (nested, so the compiler sees
@@ -554,7 +596,7 @@ hipError_t launch_decode(const DecodeProblem& p, hipStream_t stream) {
   switch (nhb) {
     case 4: hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<1, false, true>), grid, dim3(512), 0, stream, a); break;
   }
   return hipGetLastError();
 }
