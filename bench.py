@@ -145,6 +145,23 @@ def w_prefill(torch, hca, synth, T, H, q_start=0, out_f32=False, seed=3):
                 tensors=(q, g, k_all, v_all, ck, cv, out))
 
 
+def w_compress(torch, hca, synth, T=131072, seed=5):
+    """Block compression of T rows of K and V into T/128 entries each (the first
+    kernel of the prefill step)."""
+    dev = torch.device("cuda:0")
+    gen = _gen(synth, torch, seed)
+    k, v = gen(synth.K, (T, D)), gen(synth.V, (T, D))
+    ck = torch.empty((T // BLOCK, D), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+
+    def call():
+        hca.hca_compress(k, v, ck, cv)
+
+    nbytes = 2 * T * D * 2 + 2 * (T // BLOCK) * D * 2
+    return dict(call=call, kernels=[("compress_kernel", 1)], src=["compress.hip"],
+                flops=0.0, bytes=nbytes)
+
+
 def w_prefill_vha(torch, hca, synth, base, rank=16):
     """The 128K prefill launch with the VHA head mix fused (rank 16, factors N(0,1)/8)."""
     dev = torch.device("cuda:0")
@@ -260,6 +277,8 @@ def w_backward(torch, hca, synth, T, H=64, saved=False):
 # name -> (builder, description); the step's own workload is "prefill_128k"
 def workload_table(torch, hca, synth):
     return [
+        ("compress_128k", "block compression of K and V at T=131072 (1024 entries each), "
+         "bf16", lambda: w_compress(torch, hca, synth)),
         ("prefill_2k_h8_f32", "HCA prefill, batch 1, T=2048, 8 query heads, 1 KV head, dim "
          "512, block 128, window 128; fp32 output",
          lambda: w_prefill(torch, hca, synth, 2048, 8, out_f32=True)),
@@ -674,7 +693,7 @@ def main():
         for name, what, build in workload_table(torch, hca, synth):
             w = build()
             log(f"{name}")
-            n = {"decode": 240, "decode_multi": 240}.get(name, max(3, args.steps))
+            n = {"decode": 240, "decode_multi": 240, "compress_128k": 50}.get(name, max(3, args.steps))
             wl[name] = run_workload(torch, name, what, w, n, counters,
                                     back_to_back=name.startswith("decode"))
             if name.startswith("decode"):
