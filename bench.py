@@ -12,13 +12,16 @@ Also reported (each launch timed with HIP events on the stream it runs on):
   roofline      the 128K prefill kernel's rate against the 2.5 PFLOP/s dense bf16
                 MFMA peak, with HBM bytes and counter-derived MFMA FLOPs from
                 rocprofv3 counters taken on the current kernel source;
-  workloads     every other measured configuration: prefill at 2K tokens x 8
-                heads (fp32 out), at 8K x 64, the last 64K queries of a 1M-token
+  workloads     every other measured configuration: block compression at 128K,
+                prefill at 2K tokens x 8 heads (fp32 out), at 8K x 64, the last 64K queries of a 1M-token
                 sequence, prefill with the VHA head mix, batched and multi-token
                 decode, the low-rank gate GEMM and the backward pass; each with
                 its bound (MFMA or HBM: whichever roofline time is longer), the
                 achieved rate and its fraction of that peak;
   cpu_baseline  the fp64 oracle timed on a bounded sample of the 128K workload.
+  parity        the GPU output of the bench step on that sample's rows against the
+                oracle's (rel-L2, max-abs, worst row) and the compressed entries
+                compared bit for bit.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -372,11 +375,14 @@ def run_workload(torch, name, what, w, n, counters, back_to_back=False):
 
 
 # ----------------------------------------------------------------- cpu baseline
-def cpu_baseline(args, torch, tensors):
+def cpu_baseline(args, torch, tensors, hca):
     """The oracle, as it stands, on a bounded sample of query positions of the same
-    128K workload (every head), timed on this host's cores."""
+    128K workload (every head), timed on this host's cores.  The rows it computes
+    are then compared with the GPU's output of the bench step (re-run once, since
+    the VHA workload writes the same output tensor), and the entries it compresses
+    with the GPU's: the parity of the measured configuration."""
     import oracle
-    q, g, k, v = tensors[:4]
+    q, g, k, v, ck_d, cv_d, out = tensors
     T, H = q.shape[0], q.shape[1]
     rng = np.random.default_rng(2024)
     pos = np.sort(rng.choice(T, size=args.cpu_positions, replace=False)).astype(np.int64)
@@ -387,15 +393,33 @@ def cpu_baseline(args, torch, tensors):
     threads = oracle.threads()
     t0 = time.perf_counter()
     ck, cv = oracle.compress(kh), oracle.compress(vh)
-    oracle.attn(qh, gh, pos, kh, vh, 0, ck, cv, nthreads=threads)
+    ref = oracle.attn(qh, gh, pos, kh, vh, 0, ck, cv, nthreads=threads)
     dt = time.perf_counter() - t0
     t = pos
     keys = int(((t + 1) // BLOCK).sum() + np.minimum(t + 1, WINDOW).sum())
     flops = 4.0 * D * H * keys
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"{len(pos)} seeded query positions (all {H} heads) of the 128K-token "
-                      f"workload, plus compressing its full K and V; fp64 C oracle"}
+    rec = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle", "seconds": round(dt, 2),
+           "sample": f"{len(pos)} seeded query positions (all {H} heads) of the 128K-token "
+                     f"workload, plus compressing its full K and V; fp64 C oracle"}
+    # parity of the same rows: the GPU's bf16 output of the bench step
+    hca.hca_compress(k, v, ck_d, cv_d)
+    hca.hca_attn_prefill(q, g, k, v, ck_d, cv_d, out)
+    torch.cuda.synchronize()
+    got = out.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    diff = got - ref
+    row_err = np.linalg.norm(diff, axis=2) / np.maximum(np.linalg.norm(ref, axis=2), 1e-300)
+    parity = {"reference": "fp64 C oracle, the rows of the cpu_baseline sample",
+              "rows": int(ref.shape[0] * ref.shape[1]),
+              "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref)),
+              "max_abs": float(np.abs(diff).max()),
+              "worst_row_rel_l2": float(row_err.max()),
+              "tolerance": {"rel_l2": 1e-2, "max_abs": 3e-2},
+              "compress_bit_exact": bool(np.array_equal(host(ck_d), ck)
+                                         and np.array_equal(host(cv_d), cv))}
+    parity["pass"] = bool(parity["rel_l2"] <= 1e-2 and parity["max_abs"] <= 3e-2
+                          and parity["compress_bit_exact"])
+    return rec, parity
 
 
 # ----------------------------------------------------------------- profiling
@@ -711,7 +735,7 @@ def main():
         tensors = pf["tensors"]
     if not args.no_cpu_baseline:
         log("cpu baseline")
-        rec["cpu_baseline"] = cpu_baseline(args, torch, tensors)
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, torch, tensors, hca)
     print(json.dumps(rec), flush=True)
 
 
