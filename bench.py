@@ -26,6 +26,8 @@ Also reported (each launch timed with HIP events on the stream it runs on):
 python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Profiling modes (their outputs are summarised under profiles/):
+  --copy-rate OUT_MD      per-CU rate of the copy path (LDS DMA and VGPR loads of
+                          1 KiB rows) at 1, 32 and 256 workgroups, table to OUT_MD;
   --counters-workload [--reps N]
                           N launches of every workload plus a 1 GiB copy, for a
                           rocprofv3 kernel trace and --pmc passes;
@@ -625,6 +627,61 @@ def write_profiles(kt_dir, fetch_dir, write_dir, mfma_dir, out_dir, kt_order, pm
     print(json.dumps(rec, indent=1))
 
 
+# ----------------------------------------------------------------- copy path
+def copy_rate(out_md):
+    """Per-CU rate of the copy path: one workgroup per CU moves 512 KiB (or 64
+    KiB) of 1 KiB rows by LDS DMA or by 16-byte loads into VGPRs, 16 rows in
+    flight per wave, with 4 or 8 waves, for 1, 32 and 256 workgroups, from HBM
+    (the MALL flushed by a 1 GiB write first) or warm (a second pass over the
+    same data: from L2 where the workgroups' data fit in it, 4 MiB per XCD,
+    else from the MALL).  Bytes per shader clock (s_memtime) per workgroup,
+    the median over workgroups; the clock from s_memtime against
+    s_memrealtime (100 MHz)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_compressed_hca_amd", "libhca_probe.so"))
+    lib.hca_probe_copy_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    src = torch.ones(256 * (512 << 10) // 4, dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for warm in (False, True):
+        for grid, per_wg in ((1, 512 << 10), (32, 512 << 10), (256, 512 << 10),
+                             (256, 64 << 10)):
+            for waves in (4, 8):
+                for dma in (1, 0):
+                    clk = torch.zeros(3 * grid, dtype=torch.int64, device=dev)
+                    flush.zero_()
+                    torch.cuda.synchronize()
+                    rc = lib.hca_probe_copy_rate(src.data_ptr(), grid, waves, per_wg,
+                                                 2 if warm else 1, dma, clk.data_ptr(), stream)
+                    if rc != 0:
+                        raise SystemExit(f"copy probe launch failed: {rc}")
+                    torch.cuda.synchronize()
+                    c = clk.view(grid, 3).cpu().numpy()
+                    bpc = per_wg / c[:, 0].astype(np.float64)
+                    mhz = c[:, 0].astype(np.float64) / (c[:, 1].astype(np.float64) / 100.0)
+                    rows.append({"source": "warm" if warm else "HBM", "workgroups": grid,
+                                 "kib_per_wg": per_wg >> 10, "waves": waves, "path": "LDS DMA" if dma else "VGPR loads",
+                                 "bytes_per_clk_per_cu": round(float(np.median(bpc)), 2),
+                                 "min": round(float(bpc.min()), 2),
+                                 "sclk_mhz": round(float(np.median(mhz)), 1)})
+                    print(json.dumps(rows[-1]), flush=True)
+    lines = ["| source | workgroups | KiB each | waves | path | B/clk per CU (median) | min | "
+             "sclk MHz |", "|---|---:|---:|---:|---|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| {r['source']} | {r['workgroups']} | {r['kib_per_wg']} | {r['waves']} | "
+                     f"{r['path']} | "
+                     f"{r['bytes_per_clk_per_cu']} | {r['min']} | {r['sclk_mhz']} |")
+    with open(out_md, "w") as f:
+        f.write("# Per-CU copy path: 1 KiB rows, one workgroup per CU, 16 rows in flight "
+                "per wave\n\nCommand (R = the repository):\n\n    python3 $R/bench.py "
+                "--copy-rate $R/gpurun_out/copy_rate.md\n\n" + "\n".join(lines) + "\n")
+
+
 # ----------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -636,6 +693,7 @@ def main():
     ap.add_argument("--only-step", action="store_true", help="skip the other workloads")
     ap.add_argument("--counters-workload", action="store_true")
     ap.add_argument("--reps", type=int, default=1, help="launches per workload (profiling)")
+    ap.add_argument("--copy-rate", metavar="OUT_MD", help="per-CU copy-path probe, table to OUT_MD")
     ap.add_argument("--write-profiles", nargs=8,
                     metavar=("KT", "FETCH", "WRITE", "MFMA", "OUT", "KT_ORDER", "PMC_ORDER",
                              "BENCH_JSON"))
@@ -655,6 +713,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     hca.lib()  # fail loudly if the HIP library is missing
+    if args.copy_rate:
+        copy_rate(args.copy_rate)
+        return
     if args.counters_workload:
         counters_workload(torch, hca, synth, args.reps)
         return

@@ -9,6 +9,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhca.so")
+# Measurement support for bench.py --copy-rate (not part of the attention path).
+PROBE_LIB = os.path.join(PKG, "libhca_probe.so")
+PROBE_SRC = "copy_probe.hip"
 SOURCES = ["api.cpp", "compress.hip", "prefill.hip", "decode.hip", "decode_sk.hip", "gate.hip",
            "backward.hip"]
 HEADERS = ["hca_common.h", "hca_kernels.h"]
@@ -38,6 +41,10 @@ def build(verbose: bool = False) -> str:
             cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                                  stderr=subprocess.PIPE, text=True)))
+    probe_tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", os.path.join(CSRC, PROBE_SRC), "-o", probe_tmp]
+    procs.append((PROBE_SRC, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                   stderr=subprocess.PIPE, text=True)))
     failed = []
     for src, cmd, p in procs:
         try:
@@ -61,6 +68,7 @@ def build(verbose: bool = False) -> str:
     if link.returncode != 0:
         raise RuntimeError(f"link failed:\n{_quiet(link.stderr)}")
     os.replace(tmp, LIB)
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 
