@@ -43,3 +43,15 @@ def test_match_leaves_out_warm_up_launches():
     order = [{"name": "a", "kernels": [("gate_kernel", 1)], "reps": 2, "warm": 1}]
     m = bench._match(_d(["x", "gate_kernel", "gate_kernel", "gate_kernel", "copy"]), order)
     assert [[d["ns"] for d in l] for l in m["a"]] == [[2], [3]]
+
+
+def test_copy_probe_library_exports_its_entry_point():
+    """The copy-path probe behind bench.py --copy-rate is built and loadable (no
+    GPU call here)."""
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "long_context_compressed_hca_amd", "libhca_probe.so")
+    assert os.path.exists(path), "build() makes libhca_probe.so"
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "hca_probe_copy_rate")
