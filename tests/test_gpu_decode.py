@@ -140,3 +140,24 @@ def test_batch_zero_is_noop():
     d = Decode(seed=15, positions=[5], H=16)
     hca.hca_attn_decode(d.q[:0], d.g[:0], d.ck[:0], d.cv[:0], d.wk[:0], d.wv[:0], d.pos[:0],
                         d.out[:0])
+
+
+def test_entry_cache_of_2_21_entries():
+    # 2^21 entries per sequence (a token past position 2^28): entry offsets no
+    # longer fit one 32-bit buffer descriptor, and the per-tile-descriptor
+    # kernel takes the batch.  The last entry's key is head 0's query times 4
+    # (exact in bf16), so at scale 1/sqrt(512) its score is about 90 while the
+    # others stay near N(0, 1): head 0's output is close to that entry's value
+    # times the gate, and an entry read from a wrapped offset would show.  The
+    # score also rises far above the first tile's maximum, so the exact-maximum
+    # second pass runs.
+    nc = 1 << 21
+    pos = (nc << 7) + 5
+    d = Decode(seed=30, positions=[pos], H=64, nc_cap=nc, out_dtype="f32")
+    d.ck[0, nc - 1] = d.q[0, 0] * 4
+    torch.cuda.synchronize()
+    got = host_f64(d.run())
+    print(compare(got, d.oracle(), "decode with 2^21 entries"))
+    g0 = host_f64(d.g[0, 0])
+    want = host_f64(d.cv[0, nc - 1]) / (1.0 + np.exp(-g0))
+    assert np.abs(got[0, 0] - want).max() <= 3e-2
