@@ -670,6 +670,18 @@ def copy_rate(out_md):
                                  "min": round(float(bpc.min()), 2),
                                  "sclk_mhz": round(float(np.median(mhz)), 1)})
                     print(json.dumps(rows[-1]), flush=True)
+    lib.hca_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    mfma = []
+    for chains in (1, 4):
+        clk = torch.zeros(8, dtype=torch.int64, device=dev)
+        n = 4096
+        if lib.hca_probe_mfma_rate(n, chains, clk.data_ptr(), stream) != 0:
+            raise SystemExit("mfma probe launch failed")
+        torch.cuda.synchronize()
+        cyc = clk.view(4, 2)[:, 0].cpu().numpy().astype(np.float64) / n
+        mfma.append({"chains": chains, "cycles_per_mfma_32x32x16_bf16": round(float(cyc.mean()), 2)})
+        print(json.dumps(mfma[-1]), flush=True)
     lines = ["| source | workgroups | KiB each | waves | path | B/clk per CU (median) | min | "
              "sclk MHz |", "|---|---:|---:|---:|---|---:|---:|---:|"]
     for r in rows:
@@ -679,7 +691,11 @@ def copy_rate(out_md):
     with open(out_md, "w") as f:
         f.write("# Per-CU copy path: 1 KiB rows, one workgroup per CU, 16 rows in flight "
                 "per wave\n\nCommand (R = the repository):\n\n    python3 $R/bench.py "
-                "--copy-rate $R/gpurun_out/copy_rate.md\n\n" + "\n".join(lines) + "\n")
+                "--copy-rate $R/gpurun_out/copy_rate.md\n\n" + "\n".join(lines) + "\n\n"
+                "MFMA issue (one wave per SIMD, 4096 v_mfma_f32_32x32x16_bf16 each, "
+                "s_memtime cycles per MFMA): "
+                + ", ".join(f"{m['chains']} accumulator chain(s): {m['cycles_per_mfma_32x32x16_bf16']}"
+                            for m in mfma) + "\n")
 
 
 # ----------------------------------------------------------------- main

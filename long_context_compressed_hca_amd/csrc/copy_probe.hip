@@ -1,5 +1,6 @@
 // copy_probe.hip - measurement support, not part of the attention path: the
-// rate at which one CU moves 1 KiB key rows from memory, by LDS DMA (the way
+// MFMA issue rate of one SIMD, and the rate at which one CU moves 1 KiB key
+// rows from memory, by LDS DMA (the way
 // the prefill, decode and gate kernels stage their tiles) or by 16-byte loads
 // into VGPRs.  Built into its own library (libhca_probe.so) for bench.py's
 // --copy-rate mode.
@@ -63,8 +64,53 @@ __global__ void __launch_bounds__(512) copy_probe_kernel(const uint8_t* src, int
   if (!kDma) atomicXor(reinterpret_cast<unsigned*>(&clk[3 * blockIdx.x + 2]), sum);
 }
 
+// MFMA issue rate: each wave runs `n` v_mfma_f32_32x32x16_bf16 in `chains`
+// independent accumulator chains (1 or 4), timed with s_memtime; clk[2 i] =
+// cycles of wave i, clk[2 i + 1] = a word of its result (so the chain is kept).
+template <int kChains>
+__global__ void __launch_bounds__(256) mfma_probe_kernel(int n, unsigned long long* clk) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.001f * (float)(lane + e));
+    b[e] = (__bf16)(0.002f * (float)(lane - e));
+  }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+  __syncthreads();
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  for (int i = 0; i < n; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc[u % kChains] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u % kChains], 0, 0, 0);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) r += acc[c][0];
+  asm volatile("" : "+v"(r));
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  const int w = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (lane == 0) {
+    clk[2 * w] = c1 - c0;
+    clk[2 * w + 1] = (unsigned long long)__float_as_uint(r);
+  }
+}
+
 }  // namespace
 }  // namespace hca
+
+// One workgroup of 4 waves (one per SIMD); n a multiple of 4; clk holds 8
+// words.  Returns a hipError_t.
+extern "C" int hca_probe_mfma_rate(int n, int chains, unsigned long long* clk, void* stream) {
+  if (n < 4 || (n & 3) != 0 || (chains != 1 && chains != 4)) return (int)hipErrorInvalidValue;
+  if (chains == 1)
+    hipLaunchKernelGGL(hca::mfma_probe_kernel<1>, dim3(1), dim3(256), 0, (hipStream_t)stream, n, clk);
+  else
+    hipLaunchKernelGGL(hca::mfma_probe_kernel<4>, dim3(1), dim3(256), 0, (hipStream_t)stream, n, clk);
+  return (int)hipGetLastError();
+}
 
 // grid workgroups of waves * 64 threads; src must hold grid * bytes_per_wg
 // bytes; clk must hold 3 * grid zeroed words.  Returns a hipError_t.
