@@ -147,7 +147,37 @@ def w_prefill(torch, hca, synth, T, H, q_start=0, out_f32=False, seed=3):
     return dict(call=call, step=step, kernels=[("prefill_kernel", 1)],
                 src=["prefill.hip"], flops=prefill_flops(T, H, q_start),
                 bytes=prefill_bytes(T, H, q_start, 4 if out_f32 else 2),
-                tensors=(q, g, k_all, v_all, ck, cv, out))
+                tensors=(q, g, k_all, v_all, ck, cv, out), q_start=q_start)
+
+
+def parity_sample(torch, w, n_pos, seed):
+    """Host copies of what the oracle needs for n_pos seeded query positions of a
+    prefill workload (all heads), with the GPU's output of those rows from its last
+    timed launch.  No arithmetic: the cpu_baseline leg runs the oracle on them."""
+    q, g, k_all, v_all, ck, cv, out = w["tensors"]
+    T, q_start = q.shape[0], w["q_start"]
+    rng = np.random.default_rng(seed)
+    i = np.sort(rng.choice(T, size=min(n_pos, T), replace=False)).astype(np.int64)
+    t = q_start + i
+    lo = int(max(0, t.min() - (WINDOW - 1)))
+    host = lambda x: x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    idx = torch.as_tensor(i, device=q.device)
+    return {"t": t, "q": host(q.index_select(0, idx)), "g": host(g.index_select(0, idx)),
+            "k": host(k_all[lo:int(t.max()) + 1]), "v": host(v_all[lo:int(t.max()) + 1]),
+            "kv_start": lo, "ck": host(ck), "cv": host(cv),
+            "got": out.index_select(0, idx).float().cpu().numpy().astype(np.float64)}
+
+
+def parity_figures(got, ref, tol=(1e-2, 3e-2)):
+    """rel-L2, max-abs and the worst row's rel-L2 of got against ref ([..., D])."""
+    diff = got - ref
+    row_err = (np.linalg.norm(diff.reshape(-1, diff.shape[-1]), axis=1)
+               / np.maximum(np.linalg.norm(ref.reshape(-1, ref.shape[-1]), axis=1), 1e-300))
+    rel = float(np.linalg.norm(diff) / np.linalg.norm(ref))
+    mx = float(np.abs(diff).max())
+    return {"rows": int(row_err.size), "rel_l2": rel, "max_abs": mx,
+            "worst_row_rel_l2": float(row_err.max()),
+            "pass": bool(rel <= tol[0] and mx <= tol[1])}
 
 
 def w_compress(torch, hca, synth, T=131072, seed=5):
@@ -277,6 +307,12 @@ def w_backward(torch, hca, synth, T, H=64, saved=False):
     return dict(call=call, kernels=[("zero_kernel", 2), ("rows_kernel", 1), ("keys_kernel", 1),
                                     ("pool_kernel", 1)],
                 src=["backward.hip"], flops=10.0 * D * backward_pairs(T, H), bytes=nbytes)
+
+
+# Prefill workloads whose sampled rows the cpu_baseline leg checks against the
+# oracle: name -> (query positions, seed).
+PARITY_SAMPLES = {"prefill_2k_h8_f32": (2048, 11), "prefill_8k": (256, 12),
+                  "prefill_1m_chunk": (32, 13)}
 
 
 # name -> (builder, description); the step's own workload is "prefill_128k"
@@ -422,6 +458,19 @@ def cpu_baseline(args, torch, tensors, hca):
     parity["pass"] = bool(parity["rel_l2"] <= 1e-2 and parity["max_abs"] <= 3e-2
                           and parity["compress_bit_exact"])
     return rec, parity
+
+
+def cpu_parity(samples):
+    """The oracle on the sampled rows of the other prefill workloads (configs of 2K x
+    8 heads, 8K x 64 and the 1M-token chunk), compared with the GPU's rows."""
+    import oracle
+    out = {}
+    for name, sm in samples.items():
+        ref = oracle.attn(sm["q"], sm["g"], sm["t"], sm["k"], sm["v"], sm["kv_start"],
+                          sm["ck"], sm["cv"], nthreads=oracle.threads())
+        out[name] = parity_figures(sm["got"], ref)
+        out[name]["positions"] = int(len(sm["t"]))
+    return out
 
 
 # ----------------------------------------------------------------- profiling
@@ -791,12 +840,15 @@ def main():
         tensors = pf["tensors"]
         del pf, vha
         log(f"step: {ms_step:.3f} ms, prefill launch {launch_ms:.3f} ms")
+        samples = {}
         for name, what, build in workload_table(torch, hca, synth):
             w = build()
             log(f"{name}")
             n = {"decode": 240, "decode_multi": 240, "compress_128k": 50}.get(name, max(3, args.steps))
             wl[name] = run_workload(torch, name, what, w, n, counters,
                                     back_to_back=name.startswith("decode"))
+            if name in PARITY_SAMPLES and not args.no_cpu_baseline:
+                samples[name] = parity_sample(torch, w, *PARITY_SAMPLES[name])
             if name.startswith("decode"):
                 wl[name]["us_per_call"] = round(wl[name]["ms"] * 1e3, 2)
                 wl[name]["us_per_call_alone"] = round(
@@ -813,6 +865,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline")
         rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, torch, tensors, hca)
+        if not args.only_step:
+            rec["parity"].update(cpu_parity(samples))
     print(json.dumps(rec), flush=True)
 
 

@@ -55,3 +55,19 @@ def test_copy_probe_library_exports_its_entry_point():
     assert os.path.exists(path), "build() makes libhca_probe.so"
     lib = ctypes.CDLL(path)
     assert hasattr(lib, "hca_probe_copy_rate")
+
+
+def test_parity_figures_flag_a_planted_error():
+    """The bench line's parity figures: exact rows pass, one row off by 5e-2 fails
+    on max-abs and is named as the worst row."""
+    import numpy as np
+    import bench
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((4, 8, 512))
+    ok = bench.parity_figures(ref.copy(), ref)
+    assert ok["pass"] and ok["rel_l2"] == 0.0 and ok["rows"] == 32
+    bad = ref.copy()
+    bad[2, 3, 7] += 5e-2
+    f = bench.parity_figures(bad, ref)
+    assert not f["pass"] and abs(f["max_abs"] - 5e-2) < 1e-12
+    assert f["worst_row_rel_l2"] > 1e-3
