@@ -249,7 +249,16 @@ def w_decode(torch, hca, synth, M=1, reps=6):
     flops = 4 * D * H * B * sum((pos + j + 1) // BLOCK + min(pos + j + 1, WINDOW)
                                 for j in range(M))
     return dict(call=call, kernels=[("decode", 1)], src=["decode.hip", "decode_sk.hip"],
-                flops=float(flops), bytes=nbytes)
+                flops=float(flops), bytes=nbytes, sets=sets, pos=posd, M=M)
+
+
+def decode_parity_sample(torch, w):
+    """Host copies of the first input set of a one-token decode workload and the
+    GPU's output for it from the timed calls (no arithmetic)."""
+    s = w["sets"][0]
+    host = lambda x: x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return {k: host(s[k]) for k in ("q", "g", "ck", "cv", "wk", "wv")} | {
+        "pos": w["pos"].cpu().numpy(), "got": s["out"].float().cpu().numpy().astype(np.float64)}
 
 
 def w_gate(torch, hca, synth, T=131072, R=1024, H=64):
@@ -462,10 +471,17 @@ def cpu_baseline(args, torch, tensors, hca):
 
 def cpu_parity(samples):
     """The oracle on the sampled rows of the other prefill workloads (configs of 2K x
-    8 heads, 8K x 64 and the 1M-token chunk), compared with the GPU's rows."""
+    8 heads, 8K x 64 and the 1M-token chunk) and on every output of the batched
+    decode's first input set, compared with the GPU's."""
     import oracle
     out = {}
     for name, sm in samples.items():
+        if name == "decode":
+            ref = oracle.decode(sm["q"], sm["g"], sm["ck"], sm["cv"], sm["wk"], sm["wv"],
+                                sm["pos"], nthreads=oracle.threads())
+            out[name] = parity_figures(sm["got"], ref)
+            out[name]["sequences"] = int(len(sm["pos"]))
+            continue
         ref = oracle.attn(sm["q"], sm["g"], sm["t"], sm["k"], sm["v"], sm["kv_start"],
                           sm["ck"], sm["cv"], nthreads=oracle.threads())
         out[name] = parity_figures(sm["got"], ref)
@@ -849,6 +865,8 @@ def main():
                                     back_to_back=name.startswith("decode"))
             if name in PARITY_SAMPLES and not args.no_cpu_baseline:
                 samples[name] = parity_sample(torch, w, *PARITY_SAMPLES[name])
+            if name == "decode" and not args.no_cpu_baseline:
+                samples[name] = decode_parity_sample(torch, w)
             if name.startswith("decode"):
                 wl[name]["us_per_call"] = round(wl[name]["ms"] * 1e3, 2)
                 wl[name]["us_per_call_alone"] = round(
